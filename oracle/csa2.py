@@ -100,8 +100,9 @@ def quantize_fp4(y, chunk=8192):
     division done in float32 (6 is the largest E2M1 magnitude); a zero scale
     gives all-zero codes; otherwise each |y| becomes the nearest point of
     {0, .5, 1, 1.5, 2, 3, 4, 6} * scale, an exact tie keeping the even code;
-    the sign is kept except on zero.  (Distances are exact in float64: the
-    grid points have at most 7 significant bits and |y| at most 24.)
+    the sign is kept except on zero; values beyond 6 * scale take the top of
+    the grid.  (After that clip the distances are exact in float64: the grid
+    points have at most 7 significant bits and |y| at most 24.)
 
     Returns codes uint8 [E, 256] (channel 2j in the low nibble of byte j,
     channel 2j+1 in the high nibble) and scales uint8 [E, 32].
@@ -118,7 +119,10 @@ def quantize_fp4(y, chunk=8192):
         s_code = e4m3_rne_sat((amax / np.float32(6.0)).astype(np.float64))
         s = e4m3_decode(s_code)
         grid = E2M1_MAGNITUDES[None, None, None, :] * s[:, :, None, None]
-        d = np.abs(np.abs(yg)[..., None] - grid)          # [e, G, 16, 8]
+        # beyond the top of the grid the nearest point is the top (6 * scale);
+        # clipping first keeps every distance exact in float64
+        a = np.minimum(np.abs(yg), 6.0 * s[:, :, None])
+        d = np.abs(a[..., None] - grid)                   # [e, G, 16, 8]
         ties = d == d.min(axis=3, keepdims=True)
         even_tie = ties & even
         mag = np.where(even_tie.any(axis=3), even_tie.argmax(axis=3), ties.argmax(axis=3))

@@ -74,6 +74,7 @@ def test_scale_edge_cases():
     y = np.zeros((4, 512))
     y[1, :16] = 2.0 ** -12                  # amax/6 below half the smallest subnormal scale
     y[2, :16] = np.linspace(-1e5, 1e5, 16)  # amax/6 above 448: scale saturates
+    y[2, 16:32] = np.linspace(-3e38, 3e38, 16)   # far beyond the grid
     y[3, :16] = -0.0
     codes, scales = O.quantize_fp4(y)
     assert (scales[0] == 0).all() and (codes[0] == 0).all()
@@ -81,6 +82,7 @@ def test_scale_edge_cases():
     assert scales[2, 0] == 0x7E
     nib = nibbles(codes)
     assert nib[2, 0] == 15 and nib[2, 15] == 7          # clipped to -+6 * 448
+    assert nib[2, 16] == 15 and nib[2, 31] == 7 and scales[2, 1] == 0x7E
     assert (codes[3] == 0).all()                         # no negative zero
 
 
