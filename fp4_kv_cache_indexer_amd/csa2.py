@@ -1,0 +1,280 @@
+"""Thin ctypes binding of libcsa2.so (include/csa2.h).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors are
+torch tensors on the GPU (torch supplies device memory and the current
+stream); outputs and workspaces the caller does not pass are allocated with
+torch.  Non-zero statuses raise ``Csa2Error`` with the library's message.
+The module refuses to work without the built library: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+_lib = None
+
+LATENT_DIM = 512
+IDX_HEADS = 32
+IDX_DIM = 128
+BLOCK_POS = 8
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"csa2 status {status}: {msg}")
+        self.status = status
+
+
+class IndexerArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_rows", ctypes.c_int32),
+        ("n_seq", ctypes.c_int64),
+        ("row_seq", ctypes.c_void_p),
+        ("n_valid", ctypes.c_void_p),
+        ("n_ent", ctypes.c_int64),
+        ("top_k", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("head_w", ctypes.c_void_p),
+        ("keys", ctypes.c_void_p),
+        ("block_keys", ctypes.c_void_p),
+        ("keep_blocks", ctypes.c_int32),
+        ("cand", ctypes.c_void_p),
+        ("n_cand", ctypes.c_int32),
+        ("out_idx", ctypes.c_void_p),
+        ("out_score", ctypes.c_void_p),
+        ("out_blocks", ctypes.c_void_p),
+    ]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_rows", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_seq", ctypes.c_int64),
+        ("row_seq", ctypes.c_void_p),
+        ("q_bf16", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("n_ent", ctypes.c_int64),
+        ("idx", ctypes.c_void_p),
+        ("top_k", ctypes.c_int32),
+        ("swa", ctypes.c_void_p),
+        ("swa_cap", ctypes.c_int32),
+        ("swa_start", ctypes.c_void_p),
+        ("swa_len", ctypes.c_void_p),
+        ("sm_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = (
+    "csa2_abi_version", "csa2_status_string", "csa2_last_error",
+    "csa2_kv_compress_quantize", "csa2_index_block_summary",
+    "csa2_indexer_topk_workspace", "csa2_indexer_topk",
+    "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
+)
+
+
+def lib():
+    """Load libcsa2.so (once) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.csa2_abi_version.restype = i32
+    L.csa2_abi_version.argtypes = []
+    L.csa2_status_string.restype = ctypes.c_char_p
+    L.csa2_status_string.argtypes = [i32]
+    L.csa2_last_error.restype = ctypes.c_char_p
+    L.csa2_last_error.argtypes = []
+    L.csa2_kv_compress_quantize.restype = i32
+    L.csa2_kv_compress_quantize.argtypes = [vp, vp, i64, i64, i32, i64, vp, vp, i64, vp]
+    L.csa2_index_block_summary.restype = i32
+    L.csa2_index_block_summary.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+    L.csa2_indexer_topk_workspace.restype = sz
+    L.csa2_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
+    L.csa2_indexer_topk.restype = i32
+    L.csa2_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), vp, sz, vp]
+    L.csa2_sparse_attn_workspace.restype = sz
+    L.csa2_sparse_attn_workspace.argtypes = [ctypes.POINTER(AttnArgs)]
+    L.csa2_sparse_attn_decode.restype = i32
+    L.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
+    _lib = L
+    return L
+
+
+def _check(st):
+    if st != 0:
+        L = lib()
+        raise Csa2Error(st, L.csa2_last_error().decode() or L.csa2_status_string(st).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def abi_version():
+    return lib().csa2_abi_version()
+
+
+def status_string(st):
+    return lib().csa2_status_string(st).decode()
+
+
+def last_error():
+    return lib().csa2_last_error().decode()
+
+
+def kv_compress_quantize(x, m, gate=None, codes=None, scales=None, n_tok=None,
+                         out_seq_stride=0, stream=None):
+    """x, gate: bf16 [S, T, 512].  Returns (codes uint8 [S, T//m, 256],
+    scales uint8 [S, T//m, 32]) unless caller-owned outputs (possibly with
+    ``out_seq_stride``) are given."""
+    _dev(x, "x"), _dev(gate, "gate")
+    S, T = x.shape[0], x.shape[1] if n_tok is None else n_tok
+    E = T // m
+    if codes is None:
+        codes = torch.empty((S, E, LATENT_DIM // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((S, E, LATENT_DIM // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().csa2_kv_compress_quantize(
+        _ptr(x), _ptr(gate), S, T, m, x.shape[1], _ptr(codes), _ptr(scales), out_seq_stride,
+        _stream(stream)))
+    return codes, scales
+
+
+def index_block_summary(keys, summ=None, blk_begin=0, blk_end=None, stream=None):
+    """keys uint8 [S, N, 128] -> summaries uint8 [S, ceil(N/8), 128]."""
+    _dev(keys, "keys")
+    S, N = keys.shape[0], keys.shape[1]
+    nb = (N + BLOCK_POS - 1) // BLOCK_POS
+    if summ is None:
+        summ = torch.empty((S, nb, IDX_DIM), dtype=torch.uint8, device=keys.device)
+    blk_end = nb if blk_end is None else blk_end
+    _check(lib().csa2_index_block_summary(_ptr(keys), S, N, blk_begin, blk_end, _ptr(summ),
+                                          _stream(stream)))
+    return summ
+
+
+def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
+                    out_idx, out_score, out_blocks):
+    a = IndexerArgs()
+    a.n_rows = q.shape[0]
+    a.n_seq = keys.shape[0]
+    a.row_seq = _ptr(row_seq)
+    a.n_valid = _ptr(n_valid)
+    a.n_ent = keys.shape[1]
+    a.top_k = top_k
+    a.q = _ptr(q)
+    a.head_w = _ptr(head_w)
+    a.keys = _ptr(keys)
+    a.block_keys = _ptr(block_keys)
+    a.keep_blocks = keep_blocks
+    a.cand = _ptr(cand)
+    a.n_cand = 0 if cand is None else cand.shape[1]
+    a.out_idx = _ptr(out_idx)
+    a.out_score = _ptr(out_score)
+    a.out_blocks = _ptr(out_blocks)
+    return a
+
+
+def indexer_topk_workspace(q, keys, top_k, block_keys=None, keep_blocks=2048, cand=None):
+    a = _indexer_struct(q, keys, top_k, None, None, None, block_keys, keep_blocks, cand,
+                        None, None, None)
+    return lib().csa2_indexer_topk_workspace(ctypes.byref(a))
+
+
+def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_keys=None,
+                 keep_blocks=2048, cand=None, out_idx=None, out_score=None, out_blocks=None,
+                 workspace=None, stream=None):
+    """q uint8 [R, 32, 128]; keys uint8 [S, N, 128].  Returns out_idx int32
+    [R, top_k] (ascending, -1 padded)."""
+    for t, nm in ((q, "q"), (keys, "keys"), (head_w, "head_w"), (row_seq, "row_seq"),
+                  (n_valid, "n_valid"), (block_keys, "block_keys"), (cand, "cand")):
+        _dev(t, nm)
+    R = q.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((R, top_k), dtype=torch.int32, device=q.device)
+    a = _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
+                        out_idx, out_score, out_blocks)
+    L = lib()
+    need = L.csa2_indexer_topk_workspace(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(L.csa2_indexer_topk(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out_idx
+
+
+def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse):
+    a = AttnArgs()
+    a.n_rows = q.shape[0]
+    a.n_heads = q.shape[1]
+    a.n_seq = q.shape[0] if codes is None else codes.shape[0]
+    if swa is not None and codes is not None and swa.shape[0] != codes.shape[0]:
+        raise ValueError("swa and codes must hold the same sequences")
+    if codes is None and swa is not None:
+        a.n_seq = swa.shape[0]
+    a.row_seq = _ptr(row_seq)
+    a.q_bf16 = _ptr(q)
+    a.codes = _ptr(codes)
+    a.scales = _ptr(scales)
+    a.n_ent = 0 if codes is None else codes.shape[1]
+    a.idx = _ptr(idx)
+    a.top_k = 0 if idx is None else idx.shape[1]
+    a.swa = _ptr(swa)
+    a.swa_cap = 0 if swa is None else swa.shape[1]
+    a.swa_start = _ptr(swa_start)
+    a.swa_len = _ptr(swa_len)
+    a.sm_scale = float(sm_scale)
+    a.out = _ptr(out)
+    a.lse = _ptr(lse)
+    return a
+
+
+def sparse_attn_workspace(q, idx, swa=None, swa_len=None, codes=None):
+    a = _attn_struct(q, codes, None, idx, swa, None, swa_len, None, 0.0, None, None)
+    return lib().csa2_sparse_attn_workspace(ctypes.byref(a))
+
+
+def sparse_attn_decode(q, codes, scales, idx, swa=None, swa_start=None, swa_len=None,
+                       row_seq=None, sm_scale=0.0, out=None, lse=None, workspace=None,
+                       stream=None):
+    """q bf16 [R, H, 512]; codes/scales [S, N, 256]/[S, N, 32]; idx int32
+    [R, k]; swa uint8 [S, cap, 512].  Returns (out float32 [R, H, 512],
+    lse float32 [R, H])."""
+    for t, nm in ((q, "q"), (codes, "codes"), (scales, "scales"), (idx, "idx"), (swa, "swa"),
+                  (swa_start, "swa_start"), (swa_len, "swa_len"), (row_seq, "row_seq")):
+        _dev(t, nm)
+    R, H = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((R, H, LATENT_DIM), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=q.device)
+    a = _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse)
+    L = lib()
+    need = L.csa2_sparse_attn_workspace(ctypes.byref(a))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(L.csa2_sparse_attn_decode(ctypes.byref(a), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(),
+                                     _stream(stream)))
+    return out, lse

@@ -1,0 +1,378 @@
+// C ABI of libcsa2.so: argument validation, workspace layout and launch
+// order.  Every check runs on the host before anything is enqueued; a
+// non-zero status means nothing was launched (see include/csa2.h).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "csa2.h"
+#include "csa2_dev.h"
+#include "csa2_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(CSA2_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- indexer workspace layout ---------------------------------------------
+
+struct IndexerPlan {
+  int mode;                 // 0 flat, 1 hierarchical, 2 candidate
+  int64_t R, N, NB;
+  int32_t keep;
+  size_t off_hist0, off_hist1, off_scores0, off_scores1, off_blocks, total;
+  int32_t items0, items1;   // scores row lengths of stage 0 / 1
+};
+
+int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p) {
+  if (!a) return fail(CSA2_EINVAL, "indexer: args is NULL");
+  if (a->n_rows < 0) return fail(CSA2_EINVAL, "indexer: n_rows < 0");
+  if (a->n_seq < 0) return fail(CSA2_EINVAL, "indexer: n_seq < 0");
+  if (a->n_ent < 0 || a->n_ent > 0x7FFFFFF0LL) return fail(CSA2_EINVAL, "indexer: n_ent out of range");
+  if (a->top_k < 1 || a->top_k > CSA2_MAX_TOPK)
+    return fail(CSA2_EUNSUPPORTED, "indexer: top_k %d outside [1, %d]", a->top_k, CSA2_MAX_TOPK);
+  if (a->block_keys && a->cand) return fail(CSA2_EINVAL, "indexer: block_keys and cand are exclusive");
+  if (a->n_rows > 0) {
+    if (!a->q || !a->keys || !a->out_idx) return fail(CSA2_EINVAL, "indexer: q, keys and out_idx are required");
+    if (!aligned(a->q, 16) || !aligned(a->keys, 16)) return fail(CSA2_EINVAL, "indexer: q/keys not 16-byte aligned");
+    if (!aligned(a->out_idx, 4) || (a->out_score && !aligned(a->out_score, 4)) ||
+        (a->head_w && !aligned(a->head_w, 4)))
+      return fail(CSA2_EINVAL, "indexer: out_idx/out_score/head_w not 4-byte aligned");
+  }
+  p->R = a->n_rows;
+  p->N = a->n_ent;
+  p->NB = (a->n_ent + CSA2_BLOCK_POS - 1) / CSA2_BLOCK_POS;
+  p->keep = 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+  const size_t hist = (size_t)p->R * csa2::kHistBins * 4;
+  if (a->block_keys) {
+    if (a->keep_blocks < 1 || a->keep_blocks > CSA2_MAX_TOPK)
+      return fail(CSA2_EUNSUPPORTED, "indexer: keep_blocks %d outside [1, %d]", a->keep_blocks, CSA2_MAX_TOPK);
+    if (!aligned(a->block_keys, 16)) return fail(CSA2_EINVAL, "indexer: block_keys not 16-byte aligned");
+    if (a->out_blocks && !aligned(a->out_blocks, 4)) return fail(CSA2_EINVAL, "indexer: out_blocks not aligned");
+    p->mode = 1;
+    p->keep = a->keep_blocks;
+    p->items0 = (int32_t)p->NB;
+    p->items1 = a->keep_blocks * CSA2_BLOCK_POS;
+    p->off_hist0 = take(hist);
+    p->off_hist1 = take(hist);
+    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
+    p->off_scores1 = take((size_t)p->R * p->items1 * 4);
+    p->off_blocks = take((size_t)p->R * p->keep * 4);
+  } else if (a->cand) {
+    if (a->n_cand < 1) return fail(CSA2_EINVAL, "indexer: n_cand < 1 with cand set");
+    if (!aligned(a->cand, 4)) return fail(CSA2_EINVAL, "indexer: cand not 4-byte aligned");
+    p->mode = 2;
+    p->items0 = a->n_cand;
+    p->items1 = 0;
+    p->off_hist0 = take(hist);
+    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
+    p->off_hist1 = p->off_scores1 = p->off_blocks = 0;
+  } else {
+    p->mode = 0;
+    p->items0 = (int32_t)p->N;
+    p->items1 = 0;
+    p->off_hist0 = take(hist);
+    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
+    p->off_hist1 = p->off_scores1 = p->off_blocks = 0;
+  }
+  p->total = off;
+  return CSA2_OK;
+}
+
+int32_t score_chunk(int64_t n_items, int64_t rows) {
+  // aim at ~2048 workgroups in total; multiples of 256 items (4 waves x 4 tiles x 16)
+  const int64_t per_row_wgs = rows >= 2048 ? 1 : 2048 / rows;
+  int64_t c = (n_items + per_row_wgs - 1) / per_row_wgs;
+  c = (c + 255) / 256 * 256;
+  if (c < 256) c = 256;
+  return (int32_t)c;
+}
+
+// ---- attention plan --------------------------------------------------------
+
+struct AttnPlan {
+  int32_t n_split, keys_per_split;
+  size_t off_o, off_ml, total;
+};
+
+int32_t check_attn(const csa2_attn_args* a, AttnPlan* p) {
+  if (!a) return fail(CSA2_EINVAL, "attn: args is NULL");
+  if (a->n_rows < 0) return fail(CSA2_EINVAL, "attn: n_rows < 0");
+  if (a->n_seq < 0) return fail(CSA2_EINVAL, "attn: n_seq < 0");
+  if (a->n_heads != 16 && a->n_heads != 32 && a->n_heads != 64 && a->n_heads != 128)
+    return fail(CSA2_EUNSUPPORTED, "attn: n_heads %d not in {16, 32, 64, 128}", a->n_heads);
+  if (a->top_k < 0 || a->top_k > CSA2_MAX_TOPK)
+    return fail(CSA2_EUNSUPPORTED, "attn: top_k %d outside [0, %d]", a->top_k, CSA2_MAX_TOPK);
+  if (a->n_ent < 0) return fail(CSA2_EINVAL, "attn: n_ent < 0");
+  const bool has_swa = a->swa_len != nullptr;
+  if (has_swa && (a->swa_cap < 1 || a->swa_cap > 65536))
+    return fail(CSA2_EINVAL, "attn: swa_cap %d outside [1, 65536] with swa_len set", a->swa_cap);
+  if (a->n_rows > 0) {
+    if (!a->q_bf16 || !a->out) return fail(CSA2_EINVAL, "attn: q_bf16 and out are required");
+    if (!aligned(a->q_bf16, 16) || !aligned(a->out, 16)) return fail(CSA2_EINVAL, "attn: q/out not 16-byte aligned");
+    if (a->top_k > 0 && (!a->idx || !a->codes || !a->scales))
+      return fail(CSA2_EINVAL, "attn: idx, codes and scales are required when top_k > 0");
+    if (a->top_k > 0 && (!aligned(a->codes, 16) || !aligned(a->scales, 16) || !aligned(a->idx, 4)))
+      return fail(CSA2_EINVAL, "attn: codes/scales/idx misaligned");
+    if (has_swa && (!a->swa || !aligned(a->swa, 16))) return fail(CSA2_EINVAL, "attn: swa missing or misaligned");
+    if (a->lse && !aligned(a->lse, 4)) return fail(CSA2_EINVAL, "attn: lse misaligned");
+  }
+  const int64_t nk = (int64_t)a->top_k + (has_swa ? a->swa_cap : 0);
+  const int64_t hg = (a->n_heads + 63) / 64;
+  const int64_t wgs = (int64_t)a->n_rows * hg;
+  int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
+  const int64_t max_split = (nk + 63) / 64;
+  if (ns > max_split) ns = max_split;
+  if (ns < 1) ns = 1;
+  int64_t kps = (nk + ns - 1) / ns;
+  kps = (kps + 31) / 32 * 32;
+  if (kps < 32) kps = 32;
+  ns = (nk + kps - 1) / kps;
+  if (ns < 1) ns = 1;
+  p->n_split = (int32_t)ns;
+  p->keys_per_split = (int32_t)kps;
+  size_t off = 0;
+  if (ns > 1) {
+    const size_t rh = (size_t)a->n_rows * a->n_heads;
+    p->off_o = off;
+    off = round_up(off + (size_t)ns * rh * CSA2_LATENT_DIM * 4, 256);
+    p->off_ml = off;
+    off = round_up(off + (size_t)ns * rh * 2 * 4, 256);
+  } else {
+    p->off_o = p->off_ml = 0;
+  }
+  p->total = off;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_status_string(int32_t st) {
+  switch (st) {
+    case CSA2_OK: return "ok";
+    case CSA2_EINVAL: return "invalid argument";
+    case CSA2_EUNSUPPORTED: return "unsupported configuration";
+    case CSA2_EWORKSPACE: return "workspace too small";
+    case CSA2_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int64_t n_seq,
+                                  int64_t n_tok, int32_t m, int64_t x_seq_stride,
+                                  uint8_t* codes, uint8_t* scales, int64_t out_seq_stride,
+                                  void* stream) {
+  g_err.clear();
+  if (m != 1 && m != 2 && m != 4) return fail(CSA2_EUNSUPPORTED, "kv_compress_quantize: m=%d not in {1,2,4}", m);
+  if (n_seq < 0 || n_tok < 0) return fail(CSA2_EINVAL, "kv_compress_quantize: negative size");
+  const int64_t n_ent = n_tok / m;
+  if (x_seq_stride == 0) x_seq_stride = n_tok;
+  if (out_seq_stride == 0) out_seq_stride = n_ent;
+  if (x_seq_stride < n_tok) return fail(CSA2_EINVAL, "kv_compress_quantize: x_seq_stride < n_tok");
+  if (out_seq_stride < n_ent) return fail(CSA2_EINVAL, "kv_compress_quantize: out_seq_stride < n_tok/m");
+  if (n_seq == 0 || n_ent == 0) return CSA2_OK;
+  if (!x_bf16 || !codes || !scales) return fail(CSA2_EINVAL, "kv_compress_quantize: NULL pointer");
+  if (!aligned(x_bf16, 16) || (gate_bf16 && !aligned(gate_bf16, 16)))
+    return fail(CSA2_EINVAL, "kv_compress_quantize: x/gate not 16-byte aligned");
+  if (!aligned(codes, 8)) return fail(CSA2_EINVAL, "kv_compress_quantize: codes not 8-byte aligned");
+  hipError_t e = csa2::launch_kv_compress_quantize(x_bf16, gate_bf16, n_seq, n_ent, m, x_seq_stride,
+                                                   codes, scales, out_seq_stride,
+                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "kv_compress_quantize launch");
+}
+
+int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_ent,
+                                 int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                 void* stream) {
+  g_err.clear();
+  if (n_seq < 0 || n_ent < 0) return fail(CSA2_EINVAL, "index_block_summary: negative size");
+  const int64_t nb = (n_ent + CSA2_BLOCK_POS - 1) / CSA2_BLOCK_POS;
+  if (blk_begin < 0 || blk_end < blk_begin || blk_end > nb)
+    return fail(CSA2_EINVAL, "index_block_summary: block range [%lld, %lld) outside [0, %lld)",
+                (long long)blk_begin, (long long)blk_end, (long long)nb);
+  if (n_seq == 0 || blk_end == blk_begin) return CSA2_OK;
+  if (!keys || !summ) return fail(CSA2_EINVAL, "index_block_summary: NULL pointer");
+  if (!aligned(keys, 4) || !aligned(summ, 4)) return fail(CSA2_EINVAL, "index_block_summary: misaligned");
+  hipError_t e = csa2::launch_block_summary(keys, n_seq, n_ent, blk_begin, blk_end, summ,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "index_block_summary launch");
+}
+
+size_t csa2_indexer_topk_workspace(const csa2_indexer_args* a) {
+  IndexerPlan p;
+  if (check_indexer(a, &p) != CSA2_OK) return 0;
+  return p.total;
+}
+
+int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  IndexerPlan p;
+  int32_t st = check_indexer(a, &p);
+  if (st != CSA2_OK) return st;
+  if (a->n_rows == 0) return CSA2_OK;
+  if (ws_bytes < p.total || (p.total && !ws))
+    return fail(CSA2_EWORKSPACE, "indexer: workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if (!aligned(ws, 256)) return fail(CSA2_EINVAL, "indexer: workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e;
+
+  csa2::ItemMap im0{};
+  im0.n_seq = a->n_seq;
+  im0.row_seq = a->row_seq;
+  im0.n_valid = a->n_valid;
+  im0.n_ent = a->n_ent;
+  im0.n_items = p.items0;
+
+  csa2::ScoreArgs sa{};
+  sa.n_rows = a->n_rows;
+  sa.n_seq = a->n_seq;
+  sa.q = a->q;
+  sa.w = a->head_w;
+
+  csa2::SelectArgs se{};
+  se.n_rows = a->n_rows;
+
+  uint32_t* hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist0);
+  float* scores0 = reinterpret_cast<float*>(w + p.off_scores0);
+  const size_t nhist = (size_t)p.R * csa2::kHistBins * (p.mode == 1 ? 2 : 1);
+  // one fill covers both histograms in hierarchical mode (they are adjacent)
+  if ((e = csa2::launch_fill_u32(hist0, p.mode == 1 ? (p.off_scores0 - p.off_hist0) / 4 : nhist, 0u, s)) != hipSuccess)
+    return hip_fail(e, "indexer fill");
+
+  if (p.mode == 0 || p.mode == 2) {
+    im0.mode = p.mode == 0 ? csa2::kItemsFlat : csa2::kItemsCand;
+    im0.list = a->cand;
+    im0.list_len = a->n_cand;
+    sa.im = im0;
+    sa.keys = a->keys;
+    sa.seq_rows = a->n_ent;
+    sa.scores = scores0;
+    sa.hist = hist0;
+    sa.chunk = score_chunk(p.items0, p.R);
+    if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer score");
+    se.im = im0;
+    se.k = a->top_k;
+    se.scores = scores0;
+    se.hist = hist0;
+    se.out_idx = a->out_idx;
+    se.out_score = a->out_score;
+    if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer select");
+    return CSA2_OK;
+  }
+
+  // hierarchical: coarse blocks -> kept blocks -> pool positions -> top-k
+  uint32_t* hist1 = reinterpret_cast<uint32_t*>(w + p.off_hist1);
+  float* scores1 = reinterpret_cast<float*>(w + p.off_scores1);
+  int32_t* blocks = a->out_blocks ? a->out_blocks : reinterpret_cast<int32_t*>(w + p.off_blocks);
+  im0.mode = csa2::kItemsBlocks;
+  sa.im = im0;
+  sa.keys = a->block_keys;
+  sa.seq_rows = p.NB;
+  sa.scores = scores0;
+  sa.hist = hist0;
+  sa.chunk = score_chunk(p.items0, p.R);
+  if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer coarse score");
+  se.im = im0;
+  se.k = p.keep;
+  se.scores = scores0;
+  se.hist = hist0;
+  se.out_idx = blocks;
+  se.out_score = nullptr;
+  if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer coarse select");
+
+  csa2::ItemMap im1{};
+  im1.n_seq = a->n_seq;
+  im1.row_seq = a->row_seq;
+  im1.mode = csa2::kItemsPool;
+  im1.n_items = p.items1;
+  im1.n_valid = a->n_valid;
+  im1.n_ent = a->n_ent;
+  im1.list = blocks;
+  im1.list_len = p.keep;
+  sa.im = im1;
+  sa.keys = a->keys;
+  sa.seq_rows = a->n_ent;
+  sa.scores = scores1;
+  sa.hist = hist1;
+  sa.chunk = score_chunk(p.items1, p.R);
+  if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer fine score");
+  se.im = im1;
+  se.k = a->top_k;
+  se.scores = scores1;
+  se.hist = hist1;
+  se.out_idx = a->out_idx;
+  se.out_score = a->out_score;
+  if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer fine select");
+  return CSA2_OK;
+}
+
+size_t csa2_sparse_attn_workspace(const csa2_attn_args* a) {
+  AttnPlan p;
+  if (check_attn(a, &p) != CSA2_OK) return 0;
+  return p.total;
+}
+
+int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  AttnPlan p;
+  int32_t st = check_attn(a, &p);
+  if (st != CSA2_OK) return st;
+  if (a->n_rows == 0) return CSA2_OK;
+  if (ws_bytes < p.total || (p.total && !ws))
+    return fail(CSA2_EWORKSPACE, "attn: workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if (p.total && !aligned(ws, 256)) return fail(CSA2_EINVAL, "attn: workspace not 256-byte aligned");
+  csa2::AttnArgs k{};
+  k.n_rows = a->n_rows;
+  k.n_heads = a->n_heads;
+  k.n_seq = a->n_seq;
+  k.row_seq = a->row_seq;
+  k.q = static_cast<const uint16_t*>(a->q_bf16);
+  k.codes = a->codes;
+  k.scales = a->scales;
+  k.n_ent = a->n_ent;
+  k.idx = a->idx;
+  k.top_k = a->top_k;
+  k.swa = a->swa_len ? a->swa : nullptr;
+  k.swa_cap = a->swa_len ? a->swa_cap : 0;
+  k.swa_start = a->swa_start;
+  k.swa_len = a->swa_len;
+  const float sm = a->sm_scale > 0.0f ? a->sm_scale : 0.044194173824159216f;   // 1/sqrt(512)
+  k.sm_scale_log2 = sm * 1.4426950408889634f;
+  k.out = a->out;
+  k.lse = a->lse;
+  k.n_split = p.n_split;
+  k.keys_per_split = p.keys_per_split;
+  k.part_o = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_o) : nullptr;
+  k.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ml) : nullptr;
+  hipError_t e = csa2::launch_sparse_attn(k, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "sparse_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Host-side launchers of the CSA2 kernels (internal to libcsa2.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+hipError_t launch_kv_compress_quantize(const void* x, const void* z, int64_t n_seq, int64_t n_ent,
+                                       int32_t m, int64_t x_seq_stride, uint8_t* codes,
+                                       uint8_t* scales, int64_t out_seq_stride, hipStream_t stream);
+
+hipError_t launch_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_ent,
+                                int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                hipStream_t stream);
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
+
+// Which items a row of the score/select kernels walks and how they map to
+// cache positions.
+enum ItemMode : int32_t {
+  kItemsFlat = 0,    // item i = entry i, rows walk [0, n_valid)
+  kItemsBlocks = 1,  // item i = block i, rows walk [0, ceil(n_valid/8))
+  kItemsPool = 2,    // item i = position blocks[i/8]*8 + i%8 (invalid -> NaN score)
+  kItemsCand = 3,    // item i = cand[i] (invalid -> NaN score)
+};
+
+struct ItemMap {
+  int32_t mode;
+  int64_t n_seq;            // rows whose sequence is outside [0, n_seq) see nothing
+  const int32_t* row_seq;   // [R] or null
+  int32_t n_items;          // item stride per row (scores row length)
+  const int32_t* n_valid;   // [R] or null
+  int64_t n_ent;            // default n_valid
+  const int32_t* list;      // kept blocks [R][list_len] or cand [R][list_len]
+  int32_t list_len;
+};
+
+struct ScoreArgs {
+  ItemMap im;
+  int32_t n_rows;
+  int64_t n_seq;
+  const int32_t* row_seq;
+  const uint8_t* keys;      // key rows (index keys, or block keys in kItemsBlocks mode)
+  int64_t seq_rows;         // key rows per sequence in `keys`
+  const uint8_t* q;         // [R][32][128]
+  const float* w;           // [R][32] or null
+  float* scores;            // [R][n_items]
+  uint32_t* hist;           // [R][kHistBins]
+  int32_t chunk;            // items per workgroup
+};
+
+struct SelectArgs {
+  ItemMap im;
+  int32_t n_rows;
+  int32_t k;
+  const float* scores;      // [R][n_items]
+  const uint32_t* hist;     // [R][kHistBins]
+  int32_t* out_idx;         // [R][k]
+  float* out_score;         // [R][k] or null
+};
+
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  int32_t n_rows, n_heads;
+  int64_t n_seq;
+  const int32_t* row_seq;
+  const uint16_t* q;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int64_t n_ent;
+  const int32_t* idx;
+  int32_t top_k;
+  const uint8_t* swa;
+  int32_t swa_cap;
+  const int32_t* swa_start;
+  const int32_t* swa_len;
+  float sm_scale_log2;      // sm_scale * log2(e)
+  float* out;
+  float* lse;
+  int32_t n_split;          // key splits per row
+  int32_t keys_per_split;   // multiple of the key chunk
+  float* part_o;            // [n_split][R][H][512] when n_split > 1
+  float* part_ml;           // [n_split][R][H][2]
+};
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace csa2

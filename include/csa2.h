@@ -1,0 +1,225 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path on MI355X (gfx950).
+ *
+ * CSA2 (Compressed Sparse Attention 2) keeps one 512-channel latent per
+ * global KV entry, shared by every query head and used as both key and value,
+ * stored as FP4 E2M1 with one FP8 E4M3 scale per 16 channels and no second
+ * level scale; a 32-head x 128-dim sparse indexer picks the top 512 entries
+ * (optionally coarse-to-fine through 8-position blocks) and attention runs
+ * over them jointly with a 128-token FP8 sliding window.  Sources (web pages):
+ *   [0539edu §3]  http://www.0539edu.com/news/5732216/ , section 3: the
+ *                 inference configuration (cache dtypes, scale granularity,
+ *                 window, indexer heads/dim/top-k, hierarchical blocks and
+ *                 candidate pool, layer groups and compression ratios).
+ *   [nxbn §4.2]   http://m.nxbn.cn/news/78290 , §4.2: the main key
+ *                 compressor pools m tokens with context-dependent weights.
+ *   [daiw]        https://daiw.net/manual/deepseek-v4-flash/million-token-cost ,
+ *                 "four factors" table: one 512-dim latent shared by all
+ *                 query heads; encoder m = 2, decoder m = 1.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scratch space is a caller-owned
+ *     device workspace whose size the matching *_workspace call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; results are ready after the stream is
+ *     synchronised.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     non-zero status nothing was enqueued and csa2_last_error() (per calling
+ *     thread) describes the problem.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - Pointers must be 16-byte aligned except where noted.
+ *   - No C++ exception crosses this boundary.  Calls are re-entrant; two
+ *     calls that share a workspace must be ordered on one stream.
+ *
+ * Layouts (row-major, innermost last; S = sequences, N = entries per
+ * sequence, R = query rows, H = attention heads):
+ *   FP4 codes   uint8 [S][N][256]  byte j holds channel 2j in its low nibble
+ *                                  and channel 2j+1 in its high nibble
+ *   FP4 scales  uint8 [S][N][32]   E4M3FN scale of channels 16g..16g+15
+ *   index keys  uint8 [S][N][128]  E4M3FN, one 128-dim key per entry shared
+ *                                  by the 32 indexer heads
+ *   block keys  uint8 [S][ceil(N/8)][128] E4M3FN block summaries
+ *   SWA tokens  uint8 [S][cap][512] E4M3FN ring buffer
+ * E4M3 is the OCP "FN" variant (max 448, no inf); values rounded into it use
+ * round-to-nearest-even, saturate at +-448 and never produce -0.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+/* Status codes. */
+#define CSA2_OK 0
+#define CSA2_EINVAL 1        /* null/misaligned pointer, bad size or shape      */
+#define CSA2_EUNSUPPORTED 2  /* valid request outside what the kernels support  */
+#define CSA2_EWORKSPACE 3    /* workspace smaller than *_workspace reported     */
+#define CSA2_EHIP 4          /* the HIP runtime refused a launch                */
+
+/* Fixed dimensions of the method [0539edu §3; daiw]. */
+#define CSA2_LATENT_DIM 512
+#define CSA2_SCALE_GROUP 16
+#define CSA2_IDX_HEADS 32
+#define CSA2_IDX_DIM 128
+#define CSA2_BLOCK_POS 8
+#define CSA2_MAX_TOPK 2048
+
+/* Version of this ABI (CSA2_ABI_VERSION of the built library). */
+int32_t csa2_abi_version(void);
+
+/* Static text for a status code. */
+const char* csa2_status_string(int32_t status);
+
+/* Detail of the last non-zero status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+const char* csa2_last_error(void);
+
+/*
+ * Cache write [0539edu §3 (fp4_e2m1, e4m3_per_16_channel, compression_ratio);
+ * nxbn §4.2 (context-weighted pooling)].
+ *
+ * For every sequence s and group g of m consecutive tokens, per channel c:
+ *   y_c = sum_j softmax_j(gate[s][g*m+j][c]) * x[s][g*m+j][c]   (m > 1)
+ *   y_c = x[s][g][c]                                            (m = 1)
+ * with equal weights (the mean) when gate is NULL; pooling runs in float32.
+ * Then per 16-channel group: scale = E4M3(amax / 6) (float32 division),
+ * each value rounded to the nearest of {0,.5,1,1.5,2,3,4,6} * scale with ties
+ * to the even code, sign kept except on zero; a zero scale gives zero codes.
+ *
+ *   x_bf16, gate_bf16 : bf16 [n_seq][x_seq_stride tokens][512]; gate may be NULL
+ *   n_tok             : tokens per sequence to consume; a trailing group of
+ *                       fewer than m tokens is not emitted (n_tok/m entries)
+ *   m                 : 1, 2 or 4
+ *   x_seq_stride      : tokens between consecutive sequences in x/gate
+ *                       (0 = n_tok)
+ *   codes, scales     : entry e of sequence s goes to
+ *                       codes + (s*out_seq_stride + e)*256 and
+ *                       scales + (s*out_seq_stride + e)*32
+ *   out_seq_stride    : entries between consecutive sequences in the output
+ *                       (0 = n_tok/m); lets a decode step append in place.
+ * codes/scales need only 8-byte alignment.
+ */
+int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int64_t n_seq,
+                                  int64_t n_tok, int32_t m, int64_t x_seq_stride,
+                                  uint8_t* codes, uint8_t* scales, int64_t out_seq_stride,
+                                  void* stream);
+
+/*
+ * Block summaries of the index keys for the hierarchical indexer
+ * [0539edu §3, positions_per_block = 8]: block b of sequence s gets the mean
+ * of the decoded keys of its members [8b, min(8b+8, n_ent)) (exact float32
+ * sum divided by the member count in float32), rounded to E4M3.
+ * Only blocks [blk_begin, blk_end) are written, so a decode step can refresh
+ * the one block its new entry falls in.
+ *   keys : uint8 [n_seq][n_ent][128];  summ : uint8 [n_seq][ceil(n_ent/8)][128]
+ */
+int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_ent,
+                                 int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                 void* stream);
+
+/*
+ * Indexer + top-k [0539edu §3, csa2.indexer and its hierarchical block].
+ *
+ * Row r scores entries of sequence row_seq[r] (r if NULL) that are visible to
+ * it, t < n_valid[r] (n_ent if NULL):
+ *   I_t = sum_{h<32} head_w[r][h] * max(0, sum_{i<128} q[r][h][i] * key[t][i])
+ * (E4M3 x E4M3 products, float32 accumulation), and keeps the top_k entries
+ * ordered by score descending then index ascending.  out_idx[r] receives the
+ * kept indices in ascending order, padded with -1 when fewer than top_k are
+ * visible; out_score (optional) the matching float32 scores (0 for padding).
+ *
+ * Modes (exactly one):
+ *   flat          block_keys == NULL and cand == NULL.
+ *   hierarchical  block_keys != NULL: score the ceil(n_valid/8) blocks,
+ *                 keep the top min(keep_blocks, #blocks) (ties to the lower
+ *                 block id), expand each to its positions below n_valid and
+ *                 select among those.
+ *   candidate     cand != NULL: select among cand[r][0..n_cand) (distinct
+ *                 entry ids; -1 and ids >= n_valid are skipped), e.g. a pool
+ *                 kept from an earlier layer.
+ * Supported: 1 <= top_k <= 2048, 1 <= keep_blocks <= 2048.
+ */
+typedef struct {
+  int32_t n_rows;           /* R >= 1                                           */
+  int64_t n_seq;            /* S, sequences in keys (rows whose row_seq is
+                               outside [0, S) see no entry)                     */
+  const int32_t* row_seq;   /* [R] sequence of each row, or NULL (identity)     */
+  const int32_t* n_valid;   /* [R] visible entries per row (clamped to
+                               [0, n_ent]), or NULL (n_ent)                     */
+  int64_t n_ent;            /* N, entries per sequence in keys                  */
+  int32_t top_k;            /* k                                                */
+  const uint8_t* q;         /* [R][32][128] E4M3 indexer queries                */
+  const float* head_w;      /* [R][32] head weights, or NULL (all 1)            */
+  const uint8_t* keys;      /* [S][N][128] E4M3 index keys                      */
+  const uint8_t* block_keys;/* [S][ceil(N/8)][128] summaries, or NULL           */
+  int32_t keep_blocks;      /* blocks kept by the coarse stage (e.g. 2048)      */
+  const int32_t* cand;      /* [R][n_cand] candidate entry ids, or NULL         */
+  int32_t n_cand;           /* candidates per row when cand != NULL             */
+  int32_t* out_idx;         /* [R][k] kept entry ids, ascending, -1 padded      */
+  float* out_score;         /* [R][k] their scores, or NULL                     */
+  int32_t* out_blocks;      /* [R][keep_blocks] kept blocks (hierarchical mode,
+                               ascending, -1 padded), or NULL                   */
+} csa2_indexer_args;
+
+/* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error). */
+size_t csa2_indexer_topk_workspace(const csa2_indexer_args* args);
+
+int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Joint sparse + sliding-window attention for one decode step per row
+ * [daiw "four factors" (one 512-dim latent shared by all heads);
+ *  0539edu §3 (top_k, swa_window_size, fp8 SWA)].
+ *
+ * Keys = values = the latent: for row r the key set is the dequantised FP4
+ * entries idx[r][0..top_k) of sequence row_seq[r] (entries < 0 skipped)
+ * followed by the SWA tokens in slots (swa_start[r] + j) mod swa_cap,
+ * j < swa_len[r].  For every head h:
+ *   s_t = sm_scale * q[r][h] . K_t,   out[r][h] = sum_t softmax(s)_t K_t,
+ *   lse[r][h] = log(sum_t exp(s_t))   (natural log)
+ * one softmax over all keys, float32 accumulation.  With no key the output
+ * is 0 and lse = -inf.
+ *   q_bf16 : bf16 [R][H][512];  out : float32 [R][H][512];  lse : [R][H] or NULL
+ *   H in {16, 32, 64, 128};  sm_scale <= 0 selects 1/sqrt(512).
+ *   swa may be NULL when every swa_len is 0 (swa_len NULL = no window).
+ */
+typedef struct {
+  int32_t n_rows;           /* R                                                */
+  int32_t n_heads;          /* H                                                */
+  int64_t n_seq;            /* S, sequences in the caches (rows whose row_seq
+                               is outside [0, S) attend to nothing)             */
+  const int32_t* row_seq;   /* [R] or NULL                                      */
+  const void* q_bf16;       /* [R][H][512]                                      */
+  const uint8_t* codes;     /* [S][N][256]                                      */
+  const uint8_t* scales;    /* [S][N][32]                                       */
+  int64_t n_ent;            /* N                                                */
+  const int32_t* idx;       /* [R][top_k] selected entries, -1 skipped          */
+  int32_t top_k;            /* 0..2048                                          */
+  const uint8_t* swa;       /* [S][swa_cap][512] E4M3 or NULL                   */
+  int32_t swa_cap;          /* ring capacity (>= max swa_len)                   */
+  const int32_t* swa_start; /* [R] first slot, or NULL (0)                      */
+  const int32_t* swa_len;   /* [R] tokens in the window, or NULL (none)         */
+  float sm_scale;           /* softmax scale, <= 0 -> 1/sqrt(512)               */
+  float* out;               /* [R][H][512] float32                              */
+  float* lse;               /* [R][H] float32, or NULL                          */
+} csa2_attn_args;
+
+/* Workspace bytes csa2_sparse_attn_decode needs (0 on error or if none). */
+size_t csa2_sparse_attn_workspace(const csa2_attn_args* args);
+
+int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed): the built library loads,
+exports every function include/csa2.h declares, and its argument
+validation rejects bad requests with the documented status before anything
+touches the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_kv_cache_indexer_amd import csa2 as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(C._LIB_PATH), reason="libcsa2.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("csa2_kv_compress_quantize", "csa2_indexer_topk", "csa2_sparse_attn_decode",
+                     "csa2_index_block_summary"):
+        assert required in names
+    assert sorted(C.EXPORTS) == names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(C._LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_version_and_status_strings():
+    L = C.lib()
+    assert C.abi_version() == 1
+    assert C.status_string(0) == "ok"
+    assert C.status_string(3) == "workspace too small"
+    assert L.csa2_last_error() is not None
+
+
+def _idx_args(**kw):
+    a = C.IndexerArgs()
+    a.n_rows = 2
+    a.n_seq = 2
+    a.n_ent = 4096
+    a.top_k = 512
+    a.q = ctypes.c_void_p(0x1000)
+    a.keys = ctypes.c_void_p(0x2000)
+    a.out_idx = ctypes.c_void_p(0x3000)
+    a.keep_blocks = 2048
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@needs_lib
+def test_indexer_validation_without_gpu():
+    L = C.lib()
+    ws = ctypes.c_void_p(0x10000)
+    cases = [
+        (dict(top_k=0), 2), (dict(top_k=4096), 2), (dict(q=None), 1),
+        (dict(keys=ctypes.c_void_p(0x2001)), 1),
+        (dict(block_keys=ctypes.c_void_p(0x4000), cand=ctypes.c_void_p(0x5000), n_cand=4), 1),
+        (dict(block_keys=ctypes.c_void_p(0x4000), keep_blocks=0), 2),
+        (dict(cand=ctypes.c_void_p(0x5000), n_cand=0), 1),
+        (dict(n_ent=-1), 1), (dict(n_seq=-1), 1),
+    ]
+    for kw, status in cases:
+        a = _idx_args(**kw)
+        assert L.csa2_indexer_topk(ctypes.byref(a), ws, 1 << 30, None) == status, kw
+        assert C.last_error() != ""
+        assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) == 0
+    # too small a workspace is refused before any launch
+    a = _idx_args()
+    need = L.csa2_indexer_topk_workspace(ctypes.byref(a))
+    assert need >= 2 * 4096 * 4 + 2 * 4096 * 4
+    assert L.csa2_indexer_topk(ctypes.byref(a), ws, need - 1, None) == 3
+    # hierarchical workspace grows with the kept pool
+    ah = _idx_args(block_keys=ctypes.c_void_p(0x4000))
+    assert L.csa2_indexer_topk_workspace(ctypes.byref(ah)) > need
+
+
+@needs_lib
+def test_attn_and_cache_write_validation_without_gpu():
+    L = C.lib()
+    a = C.AttnArgs()
+    a.n_rows, a.n_heads, a.top_k = 1, 48, 512
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 2
+    a.n_heads = 64
+    a.q_bf16 = ctypes.c_void_p(0x1000)
+    a.out = ctypes.c_void_p(0x2000)
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 1   # idx/codes missing
+    a.idx, a.codes, a.scales = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000)
+    a.swa_len, a.swa_cap = ctypes.c_void_p(0x6000), 0
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 1   # bad swa_cap
+    a.swa_cap, a.swa = 128, ctypes.c_void_p(0x7000)
+    need = L.csa2_sparse_attn_workspace(ctypes.byref(a))
+    assert need > 0                                                         # one row -> key splits
+    assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 3
+    p = ctypes.c_void_p(0x1000)
+    assert L.csa2_kv_compress_quantize(p, None, 1, 16, 3, 0, p, p, 0, None) == 2
+    assert L.csa2_kv_compress_quantize(p, None, 1, 16, 2, 8, p, p, 0, None) == 1
+    assert L.csa2_kv_compress_quantize(None, None, 1, 16, 2, 0, p, p, 0, None) == 1
+    assert L.csa2_kv_compress_quantize(p, None, 0, 16, 2, 0, p, p, 0, None) == 0   # nothing to do
+    assert L.csa2_index_block_summary(p, 1, 17, 0, 4, p, None) == 1               # 3 blocks only
+    assert L.csa2_index_block_summary(p, 1, 17, 2, 2, p, None) == 0

@@ -1,0 +1,424 @@
+"""GPU parity: every C-ABI entry point against the oracle on seeded inputs,
+at sizes the oracle finishes in seconds, spanning several tiles/workgroups,
+ragged tails and the degenerate cases of the method."""
+
+import numpy as np
+import pytest
+import torch
+
+from fp4_kv_cache_indexer_amd import csa2 as C
+from fp4_kv_cache_indexer_amd import synth
+from oracle import csa2 as O
+from oracle import formats as F
+from parity import check_close, check_topk, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+THRESH = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    C.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# cache write
+# ---------------------------------------------------------------------------
+
+
+def near_boundary(yg, rel=4e-7):
+    """True if a float32 group sits within `rel` of a decision boundary of the
+    quantiser: amax/6 near an E4M3 rounding midpoint, or a value near a
+    threshold t*s of the E2M1 grid."""
+    amax = np.float32(np.abs(yg).max())
+    q = float(amax / np.float32(6))
+    mids = (F.E4M3_VALUES[0:0x7E] + F.E4M3_VALUES[1:0x7F]) / 2
+    if np.any(np.abs(mids - q) <= rel * max(q, 1e-30)):
+        return True
+    s = float(F.e4m3_decode(F.e4m3_rne_sat(np.float64(q))))
+    a = np.abs(yg)
+    return bool(np.any(np.abs(a[:, None] - s * np.array(THRESH)[None, :]) <= rel * a[:, None].clip(1e-30)))
+
+
+def cache_case(seed, S, T, dist="normal", gate=False):
+    g = synth.rng(seed, 7, synth.T_LATENT)
+    x = synth.latent_np(g, (S, T, 512), dist, synth.outlier_channels_np(seed, 7))
+    # edge rows: zeros, tiny, huge, mixed
+    x[0, 0] = 0.0
+    x[0, 1] = 1e-30
+    x[0, 2] = 3.0e38 * np.sign(x[0, 2])
+    x[0, 3, :16] = [1e-38] * 8 + [-2e-38] * 8
+    xb = synth.to_bf16_bits(x)
+    zb = synth.to_bf16_bits(synth.rng(seed, 7, synth.T_GATE).standard_normal((S, T, 512)).astype(np.float32)) if gate else None
+    return xb, zb
+
+
+@pytest.mark.parametrize("m,gate,S,T", [(1, False, 2, 1000), (2, False, 2, 1026), (2, True, 3, 2048),
+                                        (4, True, 1, 1024), (4, False, 1, 1030)])
+def test_kv_compress_quantize(m, gate, S, T):
+    say(f"kv_compress_quantize m={m} gate={gate} S={S} T={T}")
+    xb, zb = cache_case(11 + m, S, T, "t3" if gate else "normal", gate)
+    codes, scales = C.kv_compress_quantize(dev(xb), m, gate=None if zb is None else dev(zb))
+    torch.cuda.synchronize()
+    gc, gs = host(codes), host(scales)
+    E = T // m
+    total = mism = 0
+    for s in range(S):
+        rc, rs = O.kv_compress_quantize(xb[s], None if zb is None else zb[s], m)
+        assert rc.shape == gc[s].shape == (E, 256)
+        bad_groups = np.unique(np.concatenate([
+            np.nonzero((gc[s] != rc).reshape(E, 32, 8).any(axis=2).ravel())[0],
+            np.nonzero((gs[s] != rs).ravel())[0]]))
+        total += E * 32
+        if m == 1 or (m == 2 and not gate):
+            assert len(bad_groups) == 0, f"seq {s}: {len(bad_groups)} groups differ (must be bit-exact)"
+            continue
+        # pooled values are computed in float32 on the GPU: a group may only
+        # differ where the oracle's value sits on a decision boundary
+        x = F.bf16_bits_to_f64(xb[s])
+        z = None if zb is None else F.bf16_bits_to_f64(zb[s])
+        y = O.pool(x[:E * m], None if z is None else z[:E * m], m)
+        for gidx in bad_groups:
+            e, gg = divmod(int(gidx), 32)
+            assert near_boundary(y[e, gg * 16:(gg + 1) * 16]), f"seq {s} entry {e} group {gg} differs off-boundary"
+        mism += len(bad_groups)
+    say(f"  groups {total}, boundary mismatches {mism}")
+    assert mism <= max(2, total * 1e-3)
+
+
+def test_kv_compress_quantize_append_in_place():
+    say("kv_compress_quantize append with out_seq_stride")
+    xb, _ = cache_case(5, 3, 64, "normal")
+    full_c, full_s = C.kv_compress_quantize(dev(xb), 1)
+    codes = torch.zeros((3, 100, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((3, 100, 32), dtype=torch.uint8, device="cuda")
+    # write tokens 10..13 of every sequence into entries 50..53 of a 100-entry cache
+    xt = dev(xb)[:, 10:14].contiguous()
+    C.kv_compress_quantize(xt, 1, codes=codes[:, 50:], scales=scales[:, 50:], out_seq_stride=100)
+    torch.cuda.synchronize()
+    assert torch.equal(codes[:, 50:54], full_c[:, 10:14]) and torch.equal(scales[:, 50:54], full_s[:, 10:14])
+    assert int(codes[:, :50].sum()) == 0 and int(codes[:, 54:].sum()) == 0
+
+
+@pytest.mark.parametrize("N", [4096, 4093, 8, 5])
+def test_block_summary(N):
+    say(f"index_block_summary N={N}")
+    g = np.random.default_rng(N)
+    keys = synth.to_e4m3(g.standard_normal((3, N, 128)).astype(np.float32) * 4)
+    summ = C.index_block_summary(dev(keys))
+    torch.cuda.synchronize()
+    gsum = host(summ)
+    for s in range(3):
+        assert np.array_equal(gsum[s], O.block_summary(keys[s])), s
+    # refresh one block after changing its last key
+    keys2 = keys.copy()
+    keys2[:, N - 1] = synth.to_e4m3(g.standard_normal((3, 128)).astype(np.float32))
+    nb = (N + 7) // 8
+    C.index_block_summary(dev(keys2), summ=summ, blk_begin=nb - 1, blk_end=nb)
+    torch.cuda.synchronize()
+    gsum = host(summ)
+    for s in range(3):
+        assert np.array_equal(gsum[s], O.block_summary(keys2[s])), s
+
+
+# ---------------------------------------------------------------------------
+# indexer
+# ---------------------------------------------------------------------------
+
+
+def run_indexer(case, top_k, **kw):
+    q = dev(case["q"])
+    keys = dev(case["keys"])
+    args = dict(head_w=dev(case["w"]) if case.get("w") is not None else None)
+    if case.get("row_seq") is not None:
+        args["row_seq"] = dev(case["row_seq"].astype(np.int32))
+    if case.get("n_valid") is not None:
+        args["n_valid"] = dev(case["n_valid"].astype(np.int32))
+    R = case["q"].shape[0]
+    out_score = torch.empty((R, top_k), dtype=torch.float32, device="cuda")
+    args.update(kw)
+    idx = C.indexer_topk(q, keys, top_k, out_score=out_score, **args)
+    torch.cuda.synchronize()
+    return host(idx), host(out_score)
+
+
+def idx_case(seed, S, N, R, w=True, row_seq=None, n_valid=None, dup=False):
+    g = np.random.default_rng(seed)
+    keys = synth.to_e4m3(g.standard_normal((S, N, 128)).astype(np.float32))
+    if dup:   # exact ties: copies of a few keys spread over the cache
+        for s in range(S):
+            src = g.integers(0, N, 16)
+            for j, t in enumerate(src):
+                keys[s, g.integers(0, N, 40)] = keys[s, t]
+    q = synth.to_e4m3(g.standard_normal((R, 32, 128)).astype(np.float32))
+    ww = g.uniform(0.25, 1.0, (R, 32)).astype(np.float32) if w else None
+    return dict(keys=keys, q=q, w=ww, row_seq=row_seq, n_valid=n_valid)
+
+
+def check_flat_rows(case, gi, gsc, top_k):
+    R = case["q"].shape[0]
+    S, N = case["keys"].shape[:2]
+    diffs = 0
+    for r in range(R):
+        s = r if case["row_seq"] is None else int(case["row_seq"][r])
+        nv = N if case["n_valid"] is None else int(case["n_valid"][r])
+        w = None if case["w"] is None else case["w"][r]
+        sc = O.index_scores(case["q"][r], w, case["keys"][s][:nv])
+        ref = O.topk_select(sc, np.arange(nv), top_k)
+        diffs += check_topk(gi[r], ref, np.arange(nv), sc, top_k, f"row {r}")
+        sel = gi[r][gi[r] >= 0]
+        err = np.abs(gsc[r][:len(sel)] - sc[sel])
+        if len(sel):
+            say(f"  row {r}: score max abs err {err.max():.3e}, max rel {np.max(err / np.abs(sc[sel]).clip(1e-30)):.3e}")
+        assert np.all(err <= 2e-5 * np.abs(sc[sel]) + 1e-4), f"row {r} scores"
+    return diffs
+
+
+def test_indexer_flat_single_query_4096():
+    say("indexer flat N=4096 R=1 k=512")
+    case = idx_case(1, 1, 4096, 1, w=False)
+    gi, gsc = run_indexer(case, 512)
+    check_flat_rows(case, gi, gsc, 512)
+
+
+def test_indexer_flat_rows_ragged():
+    say("indexer flat S=3 R=6 ragged n_valid")
+    case = idx_case(2, 3, 5000, 6, row_seq=np.array([0, 1, 2, 0, 2, 1]),
+                    n_valid=np.array([5000, 100, 0, 3001, 513, 512]))
+    gi, gsc = run_indexer(case, 512)
+    check_flat_rows(case, gi, gsc, 512)
+    assert (gi[2] == -1).all() and (gi[1][100:] == -1).all()
+
+
+def test_indexer_flat_ties_and_topk_range():
+    for k in (1, 7, 512, 2048):
+        say(f"indexer flat ties k={k}")
+        case = idx_case(3 + k, 2, 3000, 2, dup=True)
+        gi, gsc = run_indexer(case, k)
+        check_flat_rows(case, gi, gsc, k)
+
+
+def test_indexer_hierarchical():
+    say("indexer hierarchical S=2 N=20003 keep=300 k=512")
+    case = idx_case(4, 2, 20003, 3, row_seq=np.array([0, 1, 1]), n_valid=np.array([20003, 20003, 9001]))
+    bk = np.stack([O.block_summary(case["keys"][s]) for s in range(2)])
+    blocks = torch.empty((3, 300), dtype=torch.int32, device="cuda")
+    gi, gsc = run_indexer(case, 512, block_keys=dev(bk), keep_blocks=300, out_blocks=blocks)
+    gb = host(blocks)
+    for r in range(3):
+        s = int(case["row_seq"][r])
+        nv = int(case["n_valid"][r])
+        q, w = case["q"][r], case["w"][r]
+        nb = (nv + 7) // 8
+        sb = O.index_scores(q, w, bk[s][:nb])
+        ref_idx, ref_blocks = O.indexer_topk_hier(q, w, case["keys"][s], bk[s], 512, nv, 300)
+        check_topk(gb[r], ref_blocks, np.arange(nb), sb, 300, f"row {r} blocks")
+        if np.array_equal(gb[r], ref_blocks):
+            pool = O.pool_positions(ref_blocks, nv)
+            sc = O.index_scores(q, w, case["keys"][s][pool])
+            check_topk(gi[r], ref_idx, pool, sc, 512, f"row {r} fine")
+        else:
+            # a near-tie at the coarse boundary changed the pool: the fine
+            # result must still be a valid top-k of the pool that was kept
+            check_topk_valid(gi[r], gb[r], q, w, case["keys"][s], nv, 512, f"row {r} fine")
+
+
+def check_topk_valid(ids, kept_blocks, q, w, keys, nv, k, what):
+    """Property check of a selection made from a pool of kept blocks: ids
+    ascending, inside the pool, and no pool entry outside the selection
+    scores above the lowest selected one by more than the tie band."""
+    pool = set(O.pool_positions(kept_blocks, nv).tolist())
+    ids = np.asarray(ids)
+    sel = ids[ids >= 0]
+    assert np.all(np.diff(sel) > 0) and set(sel.tolist()) <= pool, what
+    assert len(sel) == min(k, len(pool)), what
+    rest = np.array(sorted(pool - set(sel.tolist())), dtype=np.int64)
+    if len(rest) and len(sel):
+        lo = O.index_scores(q, w, keys[sel]).min()
+        hi = O.index_scores(q, w, keys[rest]).max()
+        assert hi <= lo + 1e-5 * abs(lo), what
+
+
+def test_indexer_hierarchical_covering_pool_equals_flat():
+    say("indexer hierarchical with a covering pool == flat")
+    case = idx_case(5, 1, 4000, 2)
+    bk = O.block_summary(case["keys"][0])[None]
+    gi_h, _ = run_indexer(case, 256, block_keys=dev(bk), keep_blocks=500)
+    gi_f, _ = run_indexer(case, 256)
+    assert np.array_equal(gi_h, gi_f)
+
+
+def test_indexer_candidates():
+    say("indexer candidate lists")
+    case = idx_case(6, 2, 3000, 2, n_valid=np.array([3000, 2000]))
+    g = np.random.default_rng(0)
+    cand = np.stack([g.permutation(3000)[:700] for _ in range(2)]).astype(np.int32)
+    cand[:, ::37] = -1
+    gi, gsc = run_indexer(case, 128, cand=dev(cand))
+    for r in range(2):
+        nv = int(case["n_valid"][r])
+        ids = cand[r][(cand[r] >= 0) & (cand[r] < nv)]
+        sc = O.index_scores(case["q"][r], case["w"][r], case["keys"][r][ids])
+        check_topk(gi[r], O.topk_select(sc, ids, 128), ids, sc, 128, f"row {r}")
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+
+def attn_case(seed, S, N, R, H, k, cap=128, dist="normal"):
+    c = synth.make_decode_case(seed=seed, cfg=50, S=S, N=N, H=H, R=R, swa_cap=cap, swa_len=cap,
+                               dist=dist, outliers=True)
+    codes = np.empty((S, N, 256), np.uint8)
+    scales = np.empty((S, N, 32), np.uint8)
+    for s in range(S):
+        codes[s], scales[s] = O.kv_compress_quantize(c.x_bits[s], None, 1)
+    g = np.random.default_rng(seed)
+    idx = np.stack([np.sort(g.choice(N, size=k, replace=False)) for _ in range(R)]).astype(np.int32)
+    return c, codes, scales, idx
+
+
+def run_attn(c, codes, scales, idx, swa_start, swa_len, sm_scale=0.0, row_seq=None):
+    if row_seq is None:
+        row_seq = np.arange(c.q.shape[0]) % c.S
+    out, lse = C.sparse_attn_decode(
+        dev(c.q), dev(codes), dev(scales), dev(idx), swa=dev(c.swa),
+        swa_start=dev(np.asarray(swa_start, np.int32)), swa_len=dev(np.asarray(swa_len, np.int32)),
+        row_seq=None if row_seq is None else dev(np.asarray(row_seq, np.int32)), sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+def check_attn_rows(c, codes, scales, idx, swa_start, swa_len, out, lse, sm_scale=None, row_seq=None):
+    worst = 0.0
+    for r in range(c.q.shape[0]):
+        s = r % c.S if row_seq is None else int(row_seq[r])
+        slots = O.swa_slots(swa_start[r], swa_len[r], c.swa.shape[1])
+        Ox, lx = O.sparse_attn(c.q[r], codes[s], scales[s], idx[r], c.swa[s], slots, sm_scale)
+        worst = max(worst, check_close(out[r], Ox, f"row {r} out"), check_close(lse[r], lx, f"row {r} lse"))
+    return worst
+
+
+def test_attn_single_query_h16():
+    say("sparse_attn H=16 N=4096 k=512 swa=128")
+    c, codes, scales, idx = attn_case(1, 1, 4096, 1, 16, 512)
+    out, lse = run_attn(c, codes, scales, idx, [0], [128])
+    say(f"  worst/bound {check_attn_rows(c, codes, scales, idx, [0], [128], out, lse):.3f}")
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_attn_rows_masks_and_wrap(H):
+    say(f"sparse_attn H={H} rows with -1 ids, short/wrapped windows")
+    c, codes, scales, idx = attn_case(2, 2, 3000, 4, H, 512, dist="t3")
+    idx[1, 100:300] = -1
+    idx[2, :] = -1
+    idx[3, 5] = 2999
+    start, ln = [0, 100, 5, 127], [128, 37, 0, 128]
+    out, lse = run_attn(c, codes, scales, idx, start, ln)
+    check_attn_rows(c, codes, scales, idx, start, ln, out, lse)
+    assert np.all(lse[2] == -np.inf) and np.all(out[2] == 0)
+
+
+def test_attn_custom_scale_and_row_mapping():
+    say("sparse_attn sm_scale=0.1 row_seq")
+    c, codes, scales, idx = attn_case(3, 2, 2048, 3, 64, 300)
+    rs = [1, 0, 1]
+    out, lse = run_attn(c, codes, scales, idx, [0, 0, 64], [128, 128, 64], sm_scale=0.1, row_seq=rs)
+    check_attn_rows(c, codes, scales, idx, [0, 0, 64], [128, 128, 64], out, lse, sm_scale=0.1, row_seq=rs)
+
+
+def test_attn_sparse_covering_all_equals_dense():
+    say("sparse_attn with k >= N: dense attention")
+    c, codes, scales, _ = attn_case(4, 1, 700, 1, 64, 10)
+    idx = np.arange(700, dtype=np.int32)[None]
+    idx = np.concatenate([idx, -np.ones((1, 4), np.int32)], axis=1)
+    out, lse = run_attn(c, codes, scales, idx, [0], [128])
+    check_attn_rows(c, codes, scales, idx, [0], [128], out, lse)
+
+
+def test_attn_no_keys():
+    say("sparse_attn without keys")
+    c, codes, scales, idx = attn_case(5, 1, 64, 2, 64, 16)
+    idx[:] = -1
+    out, lse = run_attn(c, codes, scales, idx, [0, 0], [0, 0])
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# layer groups and prefill rows
+# ---------------------------------------------------------------------------
+
+
+def test_layer_group_full_reuse_reindex():
+    say("layer group full/reuse x3/reindex/reuse x3, B=3 N=6000 H=64")
+    modes = ["full", "reuse", "reuse", "reuse", "reindex", "reuse", "reuse", "reuse"]
+    S, N, H, k = 3, 6000, 64, 512
+    base = synth.make_decode_case(seed=9, cfg=4, S=S, N=N, H=H)
+    codes = np.empty((S, N, 256), np.uint8)
+    scales = np.empty((S, N, 32), np.uint8)
+    for s in range(S):
+        codes[s], scales[s] = O.kv_compress_quantize(base.x_bits[s], None, 1)
+    layers = [synth.make_decode_case(seed=9, cfg=4, S=S, N=8, H=H, layer=L + 1) for L in range(len(modes))]
+    d_codes, d_scales, d_keys = dev(codes), dev(scales), dev(base.keys)
+    idx = None
+    for L, mode in enumerate(modes):
+        if mode in ("full", "reindex"):
+            idx = C.indexer_topk(dev(layers[L].q_idx), d_keys, k, head_w=dev(layers[L].w_idx))
+        out, lse = C.sparse_attn_decode(dev(layers[L].q), d_codes, d_scales, idx, swa=dev(layers[L].swa),
+                                        swa_len=dev(np.full(S, 128, np.int32)))
+        torch.cuda.synchronize()
+        gi, go, gl = host(idx), host(out), host(lse)
+        for r in range(S):
+            ref = O.layer_group(modes[:L + 1], [l.q[r] for l in layers], [l.q_idx[r] for l in layers],
+                                [l.w_idx[r] for l in layers], codes[r], scales[r], base.keys[r],
+                                [l.swa[r] for l in layers], O.swa_slots(0, 128, 128), k)[-1]
+            sc = O.index_scores(layers[L if mode != "reuse" else (0 if L < 4 else 4)].q_idx[r],
+                                None, base.keys[r])
+            check_topk(gi[r], ref[0], np.arange(N), sc, k, f"layer {L} row {r}")
+            if np.array_equal(gi[r], ref[0]):
+                check_close(go[r], ref[1], f"layer {L} row {r} out")
+                check_close(gl[r], ref[2], f"layer {L} row {r} lse")
+
+
+def test_prefill_rows_causal():
+    say("prefill rows: T=1024 tokens at m=2, 48 rows, causal n_valid, SWA ranges")
+    T, m, k, R = 1024, 2, 128, 48
+    g = synth.rng(3, 5, synth.T_LATENT)
+    xb = synth.to_bf16_bits(g.standard_normal((1, T, 512)).astype(np.float32))
+    zb = synth.to_bf16_bits(synth.rng(3, 5, synth.T_GATE).standard_normal((1, T, 512)).astype(np.float32))
+    codes, scales = O.kv_compress_quantize(xb[0], zb[0], m)      # the cache both sides read
+    codes, scales = codes[None], scales[None]
+    N = T // m
+    keys = synth.to_e4m3(synth.rng(3, 5, synth.T_KEYS).standard_normal((1, N, 128)).astype(np.float32))
+    swa = synth.to_e4m3(F.bf16_bits_to_f64(xb[0]).astype(np.float32))[None]   # window tokens, [1, T, 512]
+    pos = np.arange(T - R, T)
+    q_idx = synth.to_e4m3(synth.rng(3, 5, synth.T_QIDX).standard_normal((R, 32, 128)).astype(np.float32))
+    q = synth.to_bf16_bits(synth.rng(3, 5, synth.T_QATTN).standard_normal((R, 64, 512)).astype(np.float32))
+    views = [O.prefill_row_view(p, m) for p in pos]
+    nv = np.array([v[0] for v in views], np.int32)
+    lo = np.array([v[1] for v in views], np.int32)
+    ln = np.array([v[2] for v in views], np.int32)
+    row_seq = np.zeros(R, np.int32)
+    idx = C.indexer_topk(dev(q_idx), dev(keys), k, row_seq=dev(row_seq), n_valid=dev(nv))
+    out, lse = C.sparse_attn_decode(dev(q), dev(codes), dev(scales), idx, swa=dev(swa),
+                                    swa_start=dev(lo), swa_len=dev(ln), row_seq=dev(row_seq))
+    torch.cuda.synchronize()
+    gi, go, gl = host(idx), host(out), host(lse)
+    differ = 0
+    for r in range(R):
+        sc = O.index_scores(q_idx[r], None, keys[0][:nv[r]])
+        ref = O.topk_select(sc, np.arange(nv[r]), k)
+        check_topk(gi[r], ref, np.arange(nv[r]), sc, k, f"row {r}")
+        if not np.array_equal(gi[r], ref):
+            differ += 1        # a tie swapped: the attention inputs differ legitimately
+            continue
+        Ox, lx = O.sparse_attn(q[r], codes[0], scales[0], ref, swa[0], range(lo[r], lo[r] + ln[r]))
+        check_close(go[r], Ox, f"row {r} out")
+        check_close(gl[r], lx, f"row {r} lse")
+    assert differ <= 1
