@@ -1,0 +1,274 @@
+#!/usr/bin/env python
+"""Throughput of the CSA2 decode hot path on one MI355X.
+
+One step = one decode token for every row of the batch through the whole hot
+path: append the token's FP4 entry to the cache (kv_compress_quantize), refresh
+the block summary it falls in (index_block_summary), score + select with the
+indexer (indexer_topk; hierarchical at 1M context), then the joint sparse +
+window attention (sparse_attn_decode).  Inputs are seeded synthetic data,
+resident in HBM before the timed region; several independent input sets are
+rotated so the working set exceeds the 256 MB Infinity Cache.
+
+The timed region replays one captured HIP graph per input set (the form a
+serving loop would run).  An equal eager pass afterwards times the dominant
+kernel (the coarse indexer scan) with HIP events recorded by the library on
+the kernel's own stream; that duration gives the roofline line.  The
+cpu_baseline leg times the oracle on a bounded sample of the same workload.
+
+Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fp4_kv_cache_indexer_amd import csa2 as C  # noqa: E402
+
+METRIC = "decode sparse-attn queries/sec at 1M ctx; indexer HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # the configuration the metric is quoted on
+    "c3": dict(desc="hierarchical indexer at 1M context, batch 8: 1,048,576 FP4 entries/seq, "
+                    "8-position block summaries, keep 2048 blocks -> 16384-position pool, top-512, "
+                    "64 heads x 512 bf16 queries, SWA 128 fp8",
+               B=8, N=1 << 20, H=64, k=512, keep=2048, hier=True, m=1, dist="normal"),
+    "c2": dict(desc="flat indexer, batch 32: 65,536 FP4 entries/seq (131,072 tokens pooled at m=2), "
+                    "top-512, 64 heads, SWA 128 fp8, Student-t(3) latents",
+               B=32, N=1 << 16, H=64, k=512, keep=0, hier=False, m=2, dist="t3"),
+    "c1": dict(desc="single decode query, 4,096 FP4 entries, top-512, 16 heads, SWA 128 fp8",
+               B=1, N=4096, H=16, k=512, keep=0, hier=False, m=1, dist="normal"),
+}
+
+
+def e4m3(t):
+    return t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def latent(shape, gen, dist):
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    if dist == "t3":
+        # Student-t(3) = N / sqrt(chi2_3 / 3)
+        c = torch.randn(shape + (3,), generator=gen, device="cuda", dtype=torch.float32)
+        x = x / torch.sqrt((c * c).sum(-1) / 3.0)
+    return x
+
+
+class InputSet:
+    """One batch of caches and queries, all device-resident."""
+
+    def __init__(self, w, set_id, seed=0):
+        B, N, H, m = w["B"], w["N"], w["H"], w["m"]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1_000_003 * seed + 7919 * set_id + 17)
+        self.codes = torch.empty((B, N, 256), dtype=torch.uint8, device="cuda")
+        self.scales = torch.empty((B, N, 32), dtype=torch.uint8, device="cuda")
+        for b in range(B):
+            x = latent((1, N * m, 512), g, w["dist"]).to(torch.bfloat16)
+            z = torch.randn((1, N * m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+            C.kv_compress_quantize(x, m, gate=z, codes=self.codes[b:b + 1], scales=self.scales[b:b + 1])
+            if b == 0 and set_id == 0:
+                self.x0 = x[0]                       # kept for the oracle baseline
+                self.z0 = None if z is None else z[0]
+            del x, z
+        self.keys = torch.empty((B, N, 128), dtype=torch.uint8, device="cuda")
+        for b in range(B):
+            self.keys[b] = e4m3(torch.randn((N, 128), generator=g, device="cuda"))
+        self.summ = C.index_block_summary(self.keys) if w["hier"] else None
+        self.swa = e4m3(latent((B, 128, 512), g, w["dist"]))
+        self.swa_len = torch.full((B,), 128, dtype=torch.int32, device="cuda")
+        self.q_idx = e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
+        self.q = torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16)
+        self.x_new = latent((B, m, 512), g, w["dist"]).to(torch.bfloat16)
+        self.z_new = torch.randn((B, m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+        self.idx = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        self.ws_idx = torch.empty(max(256, C.indexer_topk_workspace(
+            self.q_idx, self.keys, w["k"], block_keys=self.summ, keep_blocks=w["keep"] or 2048)),
+            dtype=torch.uint8, device="cuda")
+        need = C.sparse_attn_workspace(self.q, self.idx, swa=self.swa, swa_len=self.swa_len, codes=self.codes)
+        self.ws_attn = torch.empty(max(256, need), dtype=torch.uint8, device="cuda")
+
+
+def step(w, s):
+    """One decode step for the whole batch (all hot-path rows)."""
+    N = w["N"]
+    # a0: the newest entry (m tokens pooled; m = 1 in the decoder layers)
+    C.kv_compress_quantize(s.x_new, w["m"], gate=s.z_new, codes=s.codes[:, N - 1:],
+                           scales=s.scales[:, N - 1:], out_seq_stride=N)
+    # a1: refresh the summary of the block holding that entry
+    if w["hier"]:
+        b = (N - 1) // 8
+        C.index_block_summary(s.keys, summ=s.summ, blk_begin=b, blk_end=b + 1)
+    # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context)
+    C.indexer_topk(s.q_idx, s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
+                   out_idx=s.idx, workspace=s.ws_idx)
+    # a4-a6: gather + dequant + joint sparse/window attention
+    C.sparse_attn_decode(s.q, s.codes, s.scales, s.idx, swa=s.swa, swa_len=s.swa_len, out=s.out,
+                         lse=s.lse, workspace=s.ws_attn)
+
+
+def scan_bytes(w):
+    """Algorithmic HBM bytes of one launch of the dominant kernel (the
+    indexer scan): the key rows it must read plus queries and weights."""
+    B, N = w["B"], w["N"]
+    rows = (N + 7) // 8 if w["hier"] else N
+    return B * (rows * 128 + 32 * 128 + 32 * 4)
+
+
+def cpu_baseline(w, s, seconds):
+    """Time the oracle on a bounded sample: decode steps of sequence 0 of the
+    first input set, with fresh seeded queries, until `seconds` elapse."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import csa2 as O
+
+    N, H, k = w["N"], w["H"], w["k"]
+    keys = s.keys[0].cpu().numpy()
+    x0 = s.x0.view(torch.int16).cpu().numpy().view(np.uint16)
+    z0 = None if s.z0 is None else s.z0.view(torch.int16).cpu().numpy().view(np.uint16)
+    swa = s.swa[0].cpu().numpy()
+    summ = O.block_summary(keys) if w["hier"] else None          # cache state (untimed)
+    g = np.random.default_rng(0)
+    n = 0
+    el = 0.0
+    while True:
+        q_idx = e4m3(torch.from_numpy(g.standard_normal((32, 128)).astype(np.float32)).cuda()).cpu().numpy()
+        q = torch.from_numpy(g.standard_normal((H, 512)).astype(np.float32)).to(torch.bfloat16)
+        q = q.view(torch.int16).numpy().view(np.uint16)
+        ts = time.perf_counter()
+        m = w["m"]
+        O.kv_compress_quantize(x0[-m:], None if z0 is None else z0[-m:], m)   # a0: the new entry
+        if w["hier"]:
+            O.block_summary(keys[(N - 1) // 8 * 8:])                   # a1: its block
+            idx, _ = O.indexer_topk_hier(q_idx, None, keys, summ, k, N, w["keep"])
+        else:
+            idx = O.indexer_topk_flat(q_idx, None, keys, k, N)
+        sel = idx[idx >= 0]
+        tok = (sel[:, None] * m + np.arange(m)[None, :]).reshape(-1)
+        codes, scales = O.kv_compress_quantize(x0[tok], None if z0 is None else z0[tok], m)
+        O.sparse_attn(q, codes, scales, np.arange(len(sel)), swa, O.swa_slots(0, 128, 128))
+        el += time.perf_counter() - ts
+        n += 1
+        if el >= seconds:
+            break
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode queries on sequence 0 of the {w['N']}-entry cache "
+                      f"(fresh seeded queries; oracle float64, NumPy/BLAS on {threads} threads"
+                      f"{', ' + model if model else ''}; {el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    C.lib()
+    print(f"[bench] workload {args.workload}: {w['desc']}", file=sys.stderr, flush=True)
+    t = time.perf_counter()
+    sets = [InputSet(w, i) for i in range(args.sets)]
+    torch.cuda.synchronize()
+    print(f"[bench] {args.sets} input sets ready in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
+
+    for i in range(max(1, args.warmup)):
+        step(w, sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    graphs = None
+    if not args.no_graph:
+        ref = [(s.idx.clone(), s.out.clone()) for s in sets]
+        graphs = []
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(w, s)
+            graphs.append(g)
+        # every replay must reproduce the eager step exactly
+        for _ in range(2):
+            for g, s, (ri, ro) in zip(graphs, sets, ref):
+                g.replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(s.idx, ri) and torch.equal(s.out, ro)):
+                    raise RuntimeError("graph replay differs from the eager step")
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(w, sets[i % len(sets)])
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / args.steps
+    qps = w["B"] * args.steps / (ms / 1e3)
+    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {qps:.0f} queries/s",
+          file=sys.stderr, flush=True)
+
+    # dominant kernel: the indexer scan (coarse stage when hierarchical)
+    site = "score_coarse" if w["hier"] else "score_flat"
+    C.kernel_timer_start(site, args.steps)
+    for i in range(args.steps):
+        step(w, sets[i % len(sets)])
+    n_l, tot_ms = C.kernel_timer_stop()
+    avg_s = tot_ms / max(1, n_l) / 1e3
+    achieved = scan_bytes(w) / avg_s / 1e9
+    print(f"[bench] {site}: {n_l} launches, avg {avg_s * 1e6:.2f} us, {achieved:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8/fp4 storage; fp16+bf16 MFMA, fp32 accumulation",
+        "data": "synthetic (seeded, device-generated)",
+        "config": {"workload": f"{args.workload}: {w['desc']}", "batch": w["B"],
+                   "entries_per_seq": w["N"], "heads": w["H"], "top_k": w["k"],
+                   "keep_blocks": w["keep"], "swa_window": 128, "input_sets_rotated": len(sets),
+                   "timed": "graph replays" if graphs else "eager launches"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"index_score_kernel ({site})", "avg_us": round(avg_s * 1e6, 3),
+                     "bytes_per_launch": scan_bytes(w)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

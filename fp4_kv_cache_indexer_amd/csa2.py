@@ -75,7 +75,11 @@ EXPORTS = (
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
     "csa2_indexer_topk_workspace", "csa2_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
+    "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
 )
+
+SITES = dict(kv_quant=1, block_summary=2, score_flat=3, score_coarse=4, score_pool=5,
+             score_cand=6, select=7, attn=8, attn_combine=9)
 
 
 def lib():
@@ -105,6 +109,10 @@ def lib():
     L.csa2_sparse_attn_workspace.argtypes = [ctypes.POINTER(AttnArgs)]
     L.csa2_sparse_attn_decode.restype = i32
     L.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
+    L.csa2_kernel_timer_start.restype = i32
+    L.csa2_kernel_timer_start.argtypes = [i32, i32]
+    L.csa2_kernel_timer_stop.restype = i32
+    L.csa2_kernel_timer_stop.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)]
     _lib = L
     return L
 
@@ -142,6 +150,19 @@ def status_string(st):
 
 def last_error():
     return lib().csa2_last_error().decode()
+
+
+def kernel_timer_start(site, max_launches):
+    """Time the next launches from one site (a name in SITES) with HIP events."""
+    _check(lib().csa2_kernel_timer_start(SITES[site], max_launches))
+
+
+def kernel_timer_stop():
+    """Returns (launches timed, total milliseconds)."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_float(0.0)
+    _check(lib().csa2_kernel_timer_stop(ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def kv_compress_quantize(x, m, gate=None, codes=None, scales=None, n_tok=None,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <vector>
 
 #include "csa2.h"
 #include "csa2_dev.h"
@@ -28,6 +29,32 @@ int32_t hip_fail(hipError_t e, const char* what) {
   return fail(CSA2_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- launch-site timer -----------------------------------------------------
+
+struct SiteTimer {
+  int32_t site = 0;
+  int32_t used = 0;
+  std::vector<hipEvent_t> ev;   // begin/end pairs
+};
+SiteTimer g_timer;
+
+void timer_mark(int32_t site, hipStream_t s, bool end) {
+  if (g_timer.site != site) return;
+  const size_t i = 2 * (size_t)g_timer.used + (end ? 1 : 0);
+  if (i >= g_timer.ev.size()) return;
+  hipEventRecord(g_timer.ev[i], s);
+  if (end) ++g_timer.used;
+}
+
+// Launch through f() with the site's timer events around it.
+template <class F>
+hipError_t timed(int32_t site, hipStream_t s, F f) {
+  timer_mark(site, s, false);
+  hipError_t e = f();
+  timer_mark(site, s, true);
+  return e;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -42,7 +69,7 @@ struct IndexerPlan {
   int32_t items0, items1;   // scores row lengths of stage 0 / 1
 };
 
-int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p) {
+int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptrs) {
   if (!a) return fail(CSA2_EINVAL, "indexer: args is NULL");
   if (a->n_rows < 0) return fail(CSA2_EINVAL, "indexer: n_rows < 0");
   if (a->n_seq < 0) return fail(CSA2_EINVAL, "indexer: n_seq < 0");
@@ -50,7 +77,7 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p) {
   if (a->top_k < 1 || a->top_k > CSA2_MAX_TOPK)
     return fail(CSA2_EUNSUPPORTED, "indexer: top_k %d outside [1, %d]", a->top_k, CSA2_MAX_TOPK);
   if (a->block_keys && a->cand) return fail(CSA2_EINVAL, "indexer: block_keys and cand are exclusive");
-  if (a->n_rows > 0) {
+  if (a->n_rows > 0 && check_ptrs) {
     if (!a->q || !a->keys || !a->out_idx) return fail(CSA2_EINVAL, "indexer: q, keys and out_idx are required");
     if (!aligned(a->q, 16) || !aligned(a->keys, 16)) return fail(CSA2_EINVAL, "indexer: q/keys not 16-byte aligned");
     if (!aligned(a->out_idx, 4) || (a->out_score && !aligned(a->out_score, 4)) ||
@@ -67,8 +94,8 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p) {
   if (a->block_keys) {
     if (a->keep_blocks < 1 || a->keep_blocks > CSA2_MAX_TOPK)
       return fail(CSA2_EUNSUPPORTED, "indexer: keep_blocks %d outside [1, %d]", a->keep_blocks, CSA2_MAX_TOPK);
-    if (!aligned(a->block_keys, 16)) return fail(CSA2_EINVAL, "indexer: block_keys not 16-byte aligned");
-    if (a->out_blocks && !aligned(a->out_blocks, 4)) return fail(CSA2_EINVAL, "indexer: out_blocks not aligned");
+    if (check_ptrs && !aligned(a->block_keys, 16)) return fail(CSA2_EINVAL, "indexer: block_keys not 16-byte aligned");
+    if (check_ptrs && a->out_blocks && !aligned(a->out_blocks, 4)) return fail(CSA2_EINVAL, "indexer: out_blocks not aligned");
     p->mode = 1;
     p->keep = a->keep_blocks;
     p->items0 = (int32_t)p->NB;
@@ -80,7 +107,7 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p) {
     p->off_blocks = take((size_t)p->R * p->keep * 4);
   } else if (a->cand) {
     if (a->n_cand < 1) return fail(CSA2_EINVAL, "indexer: n_cand < 1 with cand set");
-    if (!aligned(a->cand, 4)) return fail(CSA2_EINVAL, "indexer: cand not 4-byte aligned");
+    if (check_ptrs && !aligned(a->cand, 4)) return fail(CSA2_EINVAL, "indexer: cand not 4-byte aligned");
     p->mode = 2;
     p->items0 = a->n_cand;
     p->items1 = 0;
@@ -115,7 +142,7 @@ struct AttnPlan {
   size_t off_o, off_ml, total;
 };
 
-int32_t check_attn(const csa2_attn_args* a, AttnPlan* p) {
+int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   if (!a) return fail(CSA2_EINVAL, "attn: args is NULL");
   if (a->n_rows < 0) return fail(CSA2_EINVAL, "attn: n_rows < 0");
   if (a->n_seq < 0) return fail(CSA2_EINVAL, "attn: n_seq < 0");
@@ -127,7 +154,7 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p) {
   const bool has_swa = a->swa_len != nullptr;
   if (has_swa && (a->swa_cap < 1 || a->swa_cap > 65536))
     return fail(CSA2_EINVAL, "attn: swa_cap %d outside [1, 65536] with swa_len set", a->swa_cap);
-  if (a->n_rows > 0) {
+  if (a->n_rows > 0 && check_ptrs) {
     if (!a->q_bf16 || !a->out) return fail(CSA2_EINVAL, "attn: q_bf16 and out are required");
     if (!aligned(a->q_bf16, 16) || !aligned(a->out, 16)) return fail(CSA2_EINVAL, "attn: q/out not 16-byte aligned");
     if (a->top_k > 0 && (!a->idx || !a->codes || !a->scales))
@@ -201,9 +228,11 @@ int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int
   if (!aligned(x_bf16, 16) || (gate_bf16 && !aligned(gate_bf16, 16)))
     return fail(CSA2_EINVAL, "kv_compress_quantize: x/gate not 16-byte aligned");
   if (!aligned(codes, 8)) return fail(CSA2_EINVAL, "kv_compress_quantize: codes not 8-byte aligned");
-  hipError_t e = csa2::launch_kv_compress_quantize(x_bf16, gate_bf16, n_seq, n_ent, m, x_seq_stride,
-                                                   codes, scales, out_seq_stride,
-                                                   static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_KV_QUANT, s, [&] {
+    return csa2::launch_kv_compress_quantize(x_bf16, gate_bf16, n_seq, n_ent, m, x_seq_stride,
+                                             codes, scales, out_seq_stride, s);
+  });
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "kv_compress_quantize launch");
 }
 
@@ -219,21 +248,23 @@ int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_e
   if (n_seq == 0 || blk_end == blk_begin) return CSA2_OK;
   if (!keys || !summ) return fail(CSA2_EINVAL, "index_block_summary: NULL pointer");
   if (!aligned(keys, 4) || !aligned(summ, 4)) return fail(CSA2_EINVAL, "index_block_summary: misaligned");
-  hipError_t e = csa2::launch_block_summary(keys, n_seq, n_ent, blk_begin, blk_end, summ,
-                                            static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_BLOCK_SUMMARY, s, [&] {
+    return csa2::launch_block_summary(keys, n_seq, n_ent, blk_begin, blk_end, summ, s);
+  });
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "index_block_summary launch");
 }
 
 size_t csa2_indexer_topk_workspace(const csa2_indexer_args* a) {
   IndexerPlan p;
-  if (check_indexer(a, &p) != CSA2_OK) return 0;
+  if (check_indexer(a, &p, false) != CSA2_OK) return 0;
   return p.total;
 }
 
 int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   IndexerPlan p;
-  int32_t st = check_indexer(a, &p);
+  int32_t st = check_indexer(a, &p, true);
   if (st != CSA2_OK) return st;
   if (a->n_rows == 0) return CSA2_OK;
   if (ws_bytes < p.total || (p.total && !ws))
@@ -276,14 +307,17 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
     sa.scores = scores0;
     sa.hist = hist0;
     sa.chunk = score_chunk(p.items0, p.R);
-    if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer score");
+    if ((e = timed(p.mode == 0 ? CSA2_SITE_SCORE_FLAT : CSA2_SITE_SCORE_CAND, s,
+                   [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
+      return hip_fail(e, "indexer score");
     se.im = im0;
     se.k = a->top_k;
     se.scores = scores0;
     se.hist = hist0;
     se.out_idx = a->out_idx;
     se.out_score = a->out_score;
-    if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer select");
+    if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
+      return hip_fail(e, "indexer select");
     return CSA2_OK;
   }
 
@@ -298,14 +332,16 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   sa.scores = scores0;
   sa.hist = hist0;
   sa.chunk = score_chunk(p.items0, p.R);
-  if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer coarse score");
+  if ((e = timed(CSA2_SITE_SCORE_COARSE, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
+    return hip_fail(e, "indexer coarse score");
   se.im = im0;
   se.k = p.keep;
   se.scores = scores0;
   se.hist = hist0;
   se.out_idx = blocks;
   se.out_score = nullptr;
-  if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer coarse select");
+  if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
+    return hip_fail(e, "indexer coarse select");
 
   csa2::ItemMap im1{};
   im1.n_seq = a->n_seq;
@@ -322,27 +358,29 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   sa.scores = scores1;
   sa.hist = hist1;
   sa.chunk = score_chunk(p.items1, p.R);
-  if ((e = csa2::launch_index_score(sa, s)) != hipSuccess) return hip_fail(e, "indexer fine score");
+  if ((e = timed(CSA2_SITE_SCORE_POOL, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
+    return hip_fail(e, "indexer fine score");
   se.im = im1;
   se.k = a->top_k;
   se.scores = scores1;
   se.hist = hist1;
   se.out_idx = a->out_idx;
   se.out_score = a->out_score;
-  if ((e = csa2::launch_topk_select(se, s)) != hipSuccess) return hip_fail(e, "indexer fine select");
+  if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
+    return hip_fail(e, "indexer fine select");
   return CSA2_OK;
 }
 
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* a) {
   AttnPlan p;
-  if (check_attn(a, &p) != CSA2_OK) return 0;
+  if (check_attn(a, &p, false) != CSA2_OK) return 0;
   return p.total;
 }
 
 int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   AttnPlan p;
-  int32_t st = check_attn(a, &p);
+  int32_t st = check_attn(a, &p, true);
   if (st != CSA2_OK) return st;
   if (a->n_rows == 0) return CSA2_OK;
   if (ws_bytes < p.total || (p.total && !ws))
@@ -371,8 +409,48 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
   k.keys_per_split = p.keys_per_split;
   k.part_o = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_o) : nullptr;
   k.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ml) : nullptr;
-  hipError_t e = csa2::launch_sparse_attn(k, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? CSA2_OK : hip_fail(e, "sparse_attn launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_ATTN, s, [&] { return csa2::launch_sparse_attn(k, s); });
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+  e = timed(CSA2_SITE_ATTN_COMBINE, s, [&] { return csa2::launch_attn_combine(k, s); });
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "attn combine launch");
+}
+
+int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
+  g_err.clear();
+  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_ATTN_COMBINE)
+    return fail(CSA2_EINVAL, "kernel_timer_start: unknown site %d", site);
+  if (max_launches < 1 || max_launches > 1000000)
+    return fail(CSA2_EINVAL, "kernel_timer_start: max_launches %d outside [1, 1e6]", max_launches);
+  const size_t need = 2 * (size_t)max_launches;
+  while (g_timer.ev.size() < need) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return hip_fail(e, "kernel_timer_start: hipEventCreate");
+    g_timer.ev.push_back(ev);
+  }
+  g_timer.site = site;
+  g_timer.used = 0;
+  return CSA2_OK;
+}
+
+int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms) {
+  g_err.clear();
+  if (!n_launches || !total_ms) return fail(CSA2_EINVAL, "kernel_timer_stop: NULL output");
+  float tot = 0.0f;
+  for (int32_t i = 0; i < g_timer.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "kernel_timer_stop: hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "kernel_timer_stop: hipEventElapsedTime");
+    tot += ms;
+  }
+  *n_launches = g_timer.used;
+  *total_ms = tot;
+  g_timer.site = 0;
+  g_timer.used = 0;
+  return CSA2_OK;
 }
 
 }  // extern "C"

@@ -275,8 +275,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   const int hgroups = (a.n_heads + 63) / 64;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hgroups),
                      dim3(64 * waves), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_split == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream) {
+  if (a.n_rows == 0 || a.n_split == 1) return hipSuccess;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_rows * a.n_heads)), dim3(128), 0,
                      stream, a);
   return hipGetLastError();

@@ -88,5 +88,6 @@ struct AttnArgs {
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace csa2

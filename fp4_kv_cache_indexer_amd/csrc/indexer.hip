@@ -2,9 +2,14 @@
 // top_k 512) and its hierarchical block (2048 blocks x 8 positions)].
 //
 //   score:  I_t = sum_h w_h * max(0, q_h . k_t), q/k FP8 E4M3, float32
-//           accumulation.  [32 heads x 128] x [128 x 16 entries] per MFMA
-//           pair (v_mfma_f32_16x16x128_f8f6f4), streaming the 128-byte keys
-//           straight from HBM; the head reduction runs in the epilogue.  Each
+//           accumulation.  The 128-byte keys stream straight from HBM into
+//           registers, are widened to fp16 there (exact: every E4M3 value is
+//           an fp16 value) and meet the queries in v_mfma_f32_16x16x32_f16,
+//           [32 heads x 128] x [128 x 16 entries] per 8 MFMAs; the head
+//           reduction runs in the epilogue.  (gfx950's fp8 MFMAs were measured
+//           to sum their products with less than float32 precision -- up to
+//           ~1e-3 relative on heavy-tailed data -- which is as wide as the
+//           top-k tie band; the fp16 MFMA matches a float32 FMA chain.)  Each
 //           workgroup also histograms the top 12 bits of the order key of its
 //           scores in LDS and folds that into a per-row histogram.
 //   select: one workgroup per row.  The row histogram gives the bin that
@@ -75,6 +80,9 @@ constexpr int kScoreThreads = 256;
 constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kTilesPerIter = 4;   // 16-item tiles in flight per wave
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4 a = *reinterpret_cast<const uint4*>(p);
   const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
@@ -84,7 +92,18 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
   return v;
 }
 
+// 8 E4M3 bytes (two words, byte order = element order) widened to fp16.
+__device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w0, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w0, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w1, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w1, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int MODE>
 __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(ScoreArgs a) {
+  a.im.mode = MODE;                              // lets the item mapping fold away
   __shared__ uint32_t hist[kHistBins];
   const int r = blockIdx.y;
   const int64_t nv = row_valid(a.im, r);
@@ -100,12 +119,21 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(ScoreArgs a)
   const int64_t seq = row_seq_of(a.im, r);
   const uint8_t* kbase = a.keys + seq * a.seq_rows * kIdxDim + g * 32;
 
-  // MFMA A operands: indexer query rows n and 16+n, bytes [32g, 32g+32).
-  // The B operand (keys) uses the same byte split, so each lane's 32 bytes of
-  // q meet the same 32 key bytes and the full 128-term dot product results.
+  // MFMA A operands: indexer query rows n and 16+n, bytes [32g, 32g+32), as
+  // four fp16 k-slices of 8.  The B operand (keys) uses the same byte split,
+  // so each lane's query bytes meet the same key bytes and the four MFMAs
+  // together form the full 128-term dot product.
   const uint8_t* qr = a.q + (int64_t)r * kIdxHeads * kIdxDim + g * 32;
-  const v8i qa0 = load32(qr + n * kIdxDim);
-  const v8i qa1 = load32(qr + (16 + n) * kIdxDim);
+  v8h qa0[4], qa1[4];
+  {
+    const v8i q0 = load32(qr + n * kIdxDim);
+    const v8i q1 = load32(qr + (16 + n) * kIdxDim);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      qa0[u] = fp8x8_to_f16(q0[2 * u], q0[2 * u + 1]);
+      qa1[u] = fp8x8_to_f16(q1[2 * u], q1[2 * u + 1]);
+    }
+  }
   float w0[4], w1[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -132,10 +160,14 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(ScoreArgs a)
     }
 #pragma unroll
     for (int u = 0; u < kTilesPerIter; ++u) {
-      const v4f z = {0.f, 0.f, 0.f, 0.f};
       // D[h][entry] = sum_k q[h][k] * key[entry][k]; lane: entry n, heads 4g+i
-      const v4f d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa0, kb[u], z, 0, 0, 0, 0, 0, 0);
-      const v4f d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa1, kb[u], z, 0, 0, 0, 0, 0, 0);
+      v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const v8h kh = fp8x8_to_f16(kb[u][2 * v], kb[u][2 * v + 1]);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa0[v], kh, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa1[v], kh, d1, 0, 0, 0);
+      }
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -166,8 +198,13 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_kernel(ScoreArgs a)
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.im.n_items == 0) return hipSuccess;
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
-  hipLaunchKernelGGL(index_score_kernel, dim3((unsigned)chunks, (unsigned)a.n_rows),
-                     dim3(kScoreThreads), 0, stream, a);
+  const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
+  switch (a.im.mode) {
+    case kItemsFlat: hipLaunchKernelGGL(index_score_kernel<kItemsFlat>, grid, block, 0, stream, a); break;
+    case kItemsBlocks: hipLaunchKernelGGL(index_score_kernel<kItemsBlocks>, grid, block, 0, stream, a); break;
+    case kItemsPool: hipLaunchKernelGGL(index_score_kernel<kItemsPool>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(index_score_kernel<kItemsCand>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -168,7 +168,9 @@ typedef struct {
                                ascending, -1 padded), or NULL                   */
 } csa2_indexer_args;
 
-/* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error). */
+/* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error).
+ * Reads only the sizes and which of block_keys/cand are set; data pointers
+ * may still be NULL. */
 size_t csa2_indexer_topk_workspace(const csa2_indexer_args* args);
 
 int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
@@ -212,11 +214,36 @@ typedef struct {
   float* lse;               /* [R][H] float32, or NULL                          */
 } csa2_attn_args;
 
-/* Workspace bytes csa2_sparse_attn_decode needs (0 on error or if none). */
+/* Workspace bytes csa2_sparse_attn_decode needs (0 on error or if none).
+ * Reads only the sizes and whether swa_len is set. */
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* args);
 
 int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Instrumentation (for benchmarks and profiling; not needed for computing).
+ *
+ * csa2_kernel_timer_start(site, max_launches) arms a timer on one launch
+ * site: each of the next `max_launches` launches made from that site is
+ * bracketed by two HIP events recorded on the stream the kernel is launched
+ * on.  csa2_kernel_timer_stop() waits for those events, returns how many
+ * launches were timed and their summed duration in milliseconds, and
+ * disarms the timer.  One timer per process; arm it outside HIP graph
+ * capture.  Sites:
+ */
+#define CSA2_SITE_KV_QUANT 1       /* cache write                               */
+#define CSA2_SITE_BLOCK_SUMMARY 2  /* block summaries                           */
+#define CSA2_SITE_SCORE_FLAT 3     /* indexer scan, flat mode                   */
+#define CSA2_SITE_SCORE_COARSE 4   /* indexer scan over block summaries         */
+#define CSA2_SITE_SCORE_POOL 5     /* indexer scan over the kept blocks' pool   */
+#define CSA2_SITE_SCORE_CAND 6     /* indexer scan over a candidate list        */
+#define CSA2_SITE_SELECT 7         /* top-k selection (every stage)             */
+#define CSA2_SITE_ATTN 8           /* sparse + window attention                 */
+#define CSA2_SITE_ATTN_COMBINE 9   /* merge of the attention key splits         */
+
+int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches);
+int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);
 
 #ifdef __cplusplus
 }

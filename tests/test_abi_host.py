@@ -74,11 +74,16 @@ def test_indexer_validation_without_gpu():
         (dict(cand=ctypes.c_void_p(0x5000), n_cand=0), 1),
         (dict(n_ent=-1), 1), (dict(n_seq=-1), 1),
     ]
+    shape_errors = ("top_k", "keep_blocks", "n_cand", "n_ent", "n_seq")
     for kw, status in cases:
         a = _idx_args(**kw)
         assert L.csa2_indexer_topk(ctypes.byref(a), ws, 1 << 30, None) == status, kw
         assert C.last_error() != ""
-        assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) == 0
+        if any(k in kw for k in shape_errors) or "block_keys" in kw and "cand" in kw:
+            assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) == 0, kw
+    # the size query needs no data pointers
+    a = _idx_args(q=None, keys=None, out_idx=None)
+    assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) > 0
     # too small a workspace is refused before any launch
     a = _idx_args()
     need = L.csa2_indexer_topk_workspace(ctypes.byref(a))

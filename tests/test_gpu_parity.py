@@ -175,7 +175,7 @@ def check_flat_rows(case, gi, gsc, top_k):
         err = np.abs(gsc[r][:len(sel)] - sc[sel])
         if len(sel):
             say(f"  row {r}: score max abs err {err.max():.3e}, max rel {np.max(err / np.abs(sc[sel]).clip(1e-30)):.3e}")
-        assert np.all(err <= 2e-5 * np.abs(sc[sel]) + 1e-4), f"row {r} scores"
+        assert np.all(err <= 2e-6 * np.abs(sc[sel]) + 1e-5), f"row {r} scores"
     return diffs
 
 
