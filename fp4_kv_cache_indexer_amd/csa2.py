@@ -79,7 +79,7 @@ EXPORTS = (
 )
 
 SITES = dict(kv_quant=1, block_summary=2, score_flat=3, score_coarse=4, score_pool=5,
-             score_cand=6, select=7, attn=8, attn_combine=9)
+             score_cand=6, select=7, attn=8, attn_combine=9, filter=10, fill=11)
 
 
 def lib():

@@ -65,8 +65,10 @@ struct IndexerPlan {
   int mode;                 // 0 flat, 1 hierarchical, 2 candidate
   int64_t R, N, NB;
   int32_t keep;
-  size_t off_hist0, off_hist1, off_scores0, off_scores1, off_blocks, total;
-  int32_t items0, items1;   // scores row lengths of stage 0 / 1
+  int32_t items0, items1;   // items a row walks in stage 0 / 1
+  int32_t stride0, stride1; // score row strides (floats, multiple of 4)
+  int32_t chunks;           // filter chunks per row (max over stages)
+  size_t off_hist0, off_hist1, off_scores0, off_scores1, off_blocks, off_cand, off_count, total;
 };
 
 int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptrs) {
@@ -88,9 +90,7 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
   p->N = a->n_ent;
   p->NB = (a->n_ent + CSA2_BLOCK_POS - 1) / CSA2_BLOCK_POS;
   p->keep = 0;
-  size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
-  const size_t hist = (size_t)p->R * csa2::kHistBins * 4;
+  p->items1 = 0;
   if (a->block_keys) {
     if (a->keep_blocks < 1 || a->keep_blocks > CSA2_MAX_TOPK)
       return fail(CSA2_EUNSUPPORTED, "indexer: keep_blocks %d outside [1, %d]", a->keep_blocks, CSA2_MAX_TOPK);
@@ -100,35 +100,42 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
     p->keep = a->keep_blocks;
     p->items0 = (int32_t)p->NB;
     p->items1 = a->keep_blocks * CSA2_BLOCK_POS;
-    p->off_hist0 = take(hist);
-    p->off_hist1 = take(hist);
-    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
-    p->off_scores1 = take((size_t)p->R * p->items1 * 4);
-    p->off_blocks = take((size_t)p->R * p->keep * 4);
   } else if (a->cand) {
     if (a->n_cand < 1) return fail(CSA2_EINVAL, "indexer: n_cand < 1 with cand set");
     if (check_ptrs && !aligned(a->cand, 4)) return fail(CSA2_EINVAL, "indexer: cand not 4-byte aligned");
     p->mode = 2;
     p->items0 = a->n_cand;
-    p->items1 = 0;
-    p->off_hist0 = take(hist);
-    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
-    p->off_hist1 = p->off_scores1 = p->off_blocks = 0;
   } else {
     p->mode = 0;
     p->items0 = (int32_t)p->N;
-    p->items1 = 0;
-    p->off_hist0 = take(hist);
-    p->off_scores0 = take((size_t)p->R * p->items0 * 4);
-    p->off_hist1 = p->off_scores1 = p->off_blocks = 0;
   }
+  if (p->items0 > csa2::kMaxItems)
+    return fail(CSA2_EUNSUPPORTED, "indexer: %d items per row in one stage exceed %lld",
+                p->items0, (long long)csa2::kMaxItems);
+  p->stride0 = (int32_t)round_up((size_t)p->items0, 4);
+  p->stride1 = (int32_t)round_up((size_t)p->items1, 4);
+  const int64_t imax = p->items0 > p->items1 ? p->items0 : p->items1;
+  p->chunks = (int32_t)((imax + csa2::kFiltChunk - 1) / csa2::kFiltChunk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+  const size_t hist = (size_t)p->R * csa2::kHistBins * 4;
+  p->off_hist0 = take(hist);
+  p->off_hist1 = p->mode == 1 ? take(hist) : 0;
+  p->off_scores0 = take((size_t)p->R * p->stride0 * 4);
+  p->off_scores1 = p->mode == 1 ? take((size_t)p->R * p->stride1 * 4) : 0;
+  p->off_blocks = p->mode == 1 ? take((size_t)p->R * p->keep * 4) : 0;
+  p->off_cand = take((size_t)p->R * p->chunks * csa2::kFiltChunk * 8);
+  p->off_count = take((size_t)p->R * p->chunks * 4);
   p->total = off;
   return CSA2_OK;
 }
 
 int32_t score_chunk(int64_t n_items, int64_t rows) {
-  // aim at ~2048 workgroups in total; multiples of 256 items (4 waves x 4 tiles x 16)
-  const int64_t per_row_wgs = rows >= 2048 ? 1 : 2048 / rows;
+  // one full round of resident workgroups: as many chunks as fit on the
+  // device at once (no tail round), in multiples of 256 items
+  // (4 waves x 4 tiles x 16)
+  const int64_t slots = csa2::score_resident_wgs();
+  const int64_t per_row_wgs = rows >= slots ? 1 : slots / rows;
   int64_t c = (n_items + per_row_wgs - 1) / per_row_wgs;
   c = (c + 255) / 256 * 256;
   if (c < 256) c = 256;
@@ -168,8 +175,10 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   const int64_t hg = (a->n_heads + 63) / 64;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-  const int64_t max_split = (nk + 63) / 64;
+  const int64_t max_split = (nk + 63) / 64;        // at least 64 keys per split
   if (ns > max_split) ns = max_split;
+  const int64_t min_split = (nk + 1023) / 1024;    // at most 1024 selected ids staged per split
+  if (ns < min_split) ns = min_split;
   if (ns < 1) ns = 1;
   int64_t kps = (nk + ns - 1) / ns;
   kps = (kps + 31) / 32 * 32;
@@ -289,36 +298,50 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
 
   csa2::SelectArgs se{};
   se.n_rows = a->n_rows;
+  se.cand = reinterpret_cast<uint64_t*>(w + p.off_cand);
+  se.cand_count = reinterpret_cast<uint32_t*>(w + p.off_count);
+  se.n_chunks = p.chunks;
 
   uint32_t* hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist0);
   float* scores0 = reinterpret_cast<float*>(w + p.off_scores0);
+  // the two histograms of the hierarchical mode are adjacent: one fill
   const size_t nhist = (size_t)p.R * csa2::kHistBins * (p.mode == 1 ? 2 : 1);
-  // one fill covers both histograms in hierarchical mode (they are adjacent)
-  if ((e = csa2::launch_fill_u32(hist0, p.mode == 1 ? (p.off_scores0 - p.off_hist0) / 4 : nhist, 0u, s)) != hipSuccess)
+  if ((e = timed(CSA2_SITE_FILL, s, [&] { return csa2::launch_fill_u32(hist0, nhist, 0u, s); })) != hipSuccess)
     return hip_fail(e, "indexer fill");
+
+  // one top-k stage: score -> filter -> select
+  auto stage = [&](int site, const csa2::ItemMap& im, const uint8_t* keys, int64_t seq_rows, int32_t stride,
+                   float* scores, uint32_t* hist, int32_t k, int32_t* out_idx, float* out_score) -> int32_t {
+    hipError_t e2;
+    sa.im = im;
+    sa.keys = keys;
+    sa.seq_rows = seq_rows;
+    sa.row_stride = stride;
+    sa.scores = scores;
+    sa.hist = hist;
+    sa.chunk = score_chunk(im.n_items, p.R);
+    if ((e2 = timed(site, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
+      return hip_fail(e2, "indexer score");
+    se.im = im;
+    se.k = k;
+    se.row_stride = stride;
+    se.scores = scores;
+    se.hist = hist;
+    se.out_idx = out_idx;
+    se.out_score = out_score;
+    if ((e2 = timed(CSA2_SITE_FILTER, s, [&] { return csa2::launch_topk_filter(se, s); })) != hipSuccess)
+      return hip_fail(e2, "indexer filter");
+    if ((e2 = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
+      return hip_fail(e2, "indexer select");
+    return CSA2_OK;
+  };
 
   if (p.mode == 0 || p.mode == 2) {
     im0.mode = p.mode == 0 ? csa2::kItemsFlat : csa2::kItemsCand;
     im0.list = a->cand;
     im0.list_len = a->n_cand;
-    sa.im = im0;
-    sa.keys = a->keys;
-    sa.seq_rows = a->n_ent;
-    sa.scores = scores0;
-    sa.hist = hist0;
-    sa.chunk = score_chunk(p.items0, p.R);
-    if ((e = timed(p.mode == 0 ? CSA2_SITE_SCORE_FLAT : CSA2_SITE_SCORE_CAND, s,
-                   [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
-      return hip_fail(e, "indexer score");
-    se.im = im0;
-    se.k = a->top_k;
-    se.scores = scores0;
-    se.hist = hist0;
-    se.out_idx = a->out_idx;
-    se.out_score = a->out_score;
-    if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
-      return hip_fail(e, "indexer select");
-    return CSA2_OK;
+    return stage(p.mode == 0 ? CSA2_SITE_SCORE_FLAT : CSA2_SITE_SCORE_CAND, im0, a->keys, a->n_ent,
+                 p.stride0, scores0, hist0, a->top_k, a->out_idx, a->out_score);
   }
 
   // hierarchical: coarse blocks -> kept blocks -> pool positions -> top-k
@@ -326,49 +349,16 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   float* scores1 = reinterpret_cast<float*>(w + p.off_scores1);
   int32_t* blocks = a->out_blocks ? a->out_blocks : reinterpret_cast<int32_t*>(w + p.off_blocks);
   im0.mode = csa2::kItemsBlocks;
-  sa.im = im0;
-  sa.keys = a->block_keys;
-  sa.seq_rows = p.NB;
-  sa.scores = scores0;
-  sa.hist = hist0;
-  sa.chunk = score_chunk(p.items0, p.R);
-  if ((e = timed(CSA2_SITE_SCORE_COARSE, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
-    return hip_fail(e, "indexer coarse score");
-  se.im = im0;
-  se.k = p.keep;
-  se.scores = scores0;
-  se.hist = hist0;
-  se.out_idx = blocks;
-  se.out_score = nullptr;
-  if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
-    return hip_fail(e, "indexer coarse select");
-
-  csa2::ItemMap im1{};
-  im1.n_seq = a->n_seq;
-  im1.row_seq = a->row_seq;
+  if ((st = stage(CSA2_SITE_SCORE_COARSE, im0, a->block_keys, p.NB, p.stride0, scores0, hist0, p.keep,
+                  blocks, nullptr)) != CSA2_OK)
+    return st;
+  csa2::ItemMap im1 = im0;
   im1.mode = csa2::kItemsPool;
   im1.n_items = p.items1;
-  im1.n_valid = a->n_valid;
-  im1.n_ent = a->n_ent;
   im1.list = blocks;
   im1.list_len = p.keep;
-  sa.im = im1;
-  sa.keys = a->keys;
-  sa.seq_rows = a->n_ent;
-  sa.scores = scores1;
-  sa.hist = hist1;
-  sa.chunk = score_chunk(p.items1, p.R);
-  if ((e = timed(CSA2_SITE_SCORE_POOL, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
-    return hip_fail(e, "indexer fine score");
-  se.im = im1;
-  se.k = a->top_k;
-  se.scores = scores1;
-  se.hist = hist1;
-  se.out_idx = a->out_idx;
-  se.out_score = a->out_score;
-  if ((e = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
-    return hip_fail(e, "indexer fine select");
-  return CSA2_OK;
+  return stage(CSA2_SITE_SCORE_POOL, im1, a->keys, a->n_ent, p.stride1, scores1, hist1, a->top_k,
+               a->out_idx, a->out_score);
 }
 
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* a) {
@@ -418,7 +408,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
   g_err.clear();
-  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_ATTN_COMBINE)
+  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_FILL)
     return fail(CSA2_EINVAL, "kernel_timer_start: unknown site %d", site);
   if (max_launches < 1 || max_launches > 1000000)
     return fail(CSA2_EINVAL, "kernel_timer_start: max_launches %d outside [1, 1e6]", max_launches);

@@ -24,12 +24,22 @@ namespace csa2 {
 constexpr int kKeyChunk = 32;
 constexpr int kKrStride = kD * 2 + 16;          // bytes per key row in LDS (bf16 + pad)
 constexpr int kKtStride = kKeyChunk * 2 + 16;   // bytes per channel row in LDS
-constexpr int kAttnMaxWaves = 4;                // 16 heads per wave
+
+// Channel-major rows hold 4 slots of 16 bytes (8 keys each).  Slot s of row
+// c is stored at slot s ^ ((c >> 3) & 3): the transposing writes (lanes 8
+// rows apart) then spread over the banks, and the PV operand reads (16
+// consecutive rows) stay conflict-free.
+__device__ __forceinline__ int kt_off(int c, int byte) {
+  return c * kKtStride + ((((byte >> 4) ^ (c >> 3)) & 3) << 4) + (byte & 15);
+}
+
+constexpr int kMaxKeysPerSplit = 1024;          // selected ids staged in LDS per workgroup
 
 struct AttnShared {
   uint8_t kr[kKeyChunk * kKrStride];
   uint8_t kt[kD * kKtStride];
   int32_t kvalid[kKeyChunk];
+  int32_t sidx[kMaxKeysPerSplit];
 };
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -73,14 +83,26 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
+// The raw bytes one thread gathers for its 8 keys x 8 channels of a chunk.
+struct Gather {
+  uint32_t code[8];   // FP4: 8 channels (one word)
+  uint32_t scale[8];  // FP4: the group's E4M3 scale byte
+  uint2 swa[8];       // window token: 8 E4M3 bytes
+  int kind[8];        // 0 none, 1 selected entry, 2 window token
+};
+
+// One wave per SIMD: the 128 output accumulators live in AGPRs next to the
+// 64 query registers, so nothing spills.  Always 4 waves: every wave gathers
+// and dequantises; waves past the row's head count skip the MFMA work.
+__global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
-  const int tid = threadIdx.x, nthreads = blockDim.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.n_heads;
-  const int h = hg * 64 + wave * 16 + n;
+  const bool computes = hg * 64 + wave * 16 < H;
+  const int h = computes ? hg * 64 + wave * 16 + n : 0;
   const int64_t seq = a.row_seq ? a.row_seq[r] : r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;
@@ -92,57 +114,78 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
   const int k0 = split * a.keys_per_split;
   const int k1 = min(nk, k0 + a.keys_per_split);
 
+  const int32_t* idxr = a.idx ? a.idx + (int64_t)r * a.top_k : nullptr;
+  const uint8_t* codes_s = a.codes + (seq_ok ? seq : 0) * a.n_ent * (kD / 2);
+  const uint8_t* scales_s = a.scales + (seq_ok ? seq : 0) * a.n_ent * (kD / kGroup);
+  const uint8_t* swa_s = a.swa ? a.swa + (seq_ok ? seq : 0) * (int64_t)a.swa_cap * kD : nullptr;
+  const uint16_t* qrow = a.q + ((int64_t)r * H + h) * kD + 8 * g;
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q + (int64_t)r * H * kD);   // readable, discarded
+
+  // stage this split's selected ids
+  const int nsel_here = max(0, min(k1, nsel) - k0);
+  for (int i = tid; i < nsel_here; i += 256) sh.sidx[i] = idxr[k0 + i];
+
   // Q as the B operand of S^T = K Q^T: head n, channels ks*32 + 8g .. +8.
   v8bf qreg[kD / 32];
-  const uint16_t* qrow = a.q + ((int64_t)r * H + h) * kD + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < kD / 32; ++ks)
-    qreg[ks] = *reinterpret_cast<const v8bf*>(qrow + ks * 32);
+    qreg[ks] = computes ? *reinterpret_cast<const v8bf*>(qrow + ks * 32) : v8bf{};
 
   v4f acc[kD / 16];
 #pragma unroll
   for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int32_t* idxr = a.idx ? a.idx + (int64_t)r * a.top_k : nullptr;
-  const uint8_t* codes_s = a.codes + seq * a.n_ent * (kD / 2);
-  const uint8_t* scales_s = a.scales + seq * a.n_ent * (kD / kGroup);
-  const uint8_t* swa_s = a.swa ? a.swa + seq * (int64_t)a.swa_cap * kD : nullptr;
+  // this thread's unit of every chunk: keys t0..t0+7, channels c0..c0+7
+  const int cb = tid & 63, kg = tid >> 6;
+  const int c0 = cb * 8, t0 = kg * 8;
+  __syncthreads();                                   // sidx ready
 
+  // issue every load of a chunk at once (no data-dependent branches)
+  auto issue = [&](int kc, Gather& G) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = kc + t0 + j;
+      const bool in_range = key < k1;
+      const bool is_sel = in_range && key < nsel;
+      const int32_t p = is_sel ? sh.sidx[key - k0] : -1;
+      const bool ok = is_sel && p >= 0 && (int64_t)p < a.n_ent;
+      const bool is_swa = in_range && !is_sel;
+      int slot = swst + (key - nsel);
+      if (slot >= a.swa_cap) slot -= a.swa_cap;
+      const uint8_t* ca = ok ? codes_s + (int64_t)p * (kD / 2) + c0 / 2 : dummy;
+      const uint8_t* sa = ok ? scales_s + (int64_t)p * (kD / kGroup) + c0 / kGroup : dummy;
+      const uint8_t* wa = is_swa ? swa_s + (int64_t)slot * kD + c0 : dummy;
+      G.code[j] = *reinterpret_cast<const uint32_t*>(ca);
+      G.scale[j] = *sa;
+      G.swa[j] = *reinterpret_cast<const uint2*>(wa);
+      G.kind[j] = ok ? 1 : (is_swa ? 2 : 0);
+    }
+  };
+
+  Gather G;
+  if (k0 < k1) issue(k0, G);
   for (int kc = k0; kc < k1; kc += kKeyChunk) {
     __syncthreads();   // the previous chunk's LDS reads are done
-    // ---- gather + dequantise 32 keys x 512 channels: unit = (8 keys, 8 channels)
-    for (int u = tid; u < 256; u += nthreads) {
-      const int cb = u & 63, kg = u >> 6;
-      const int c0 = cb * 8, t0 = kg * 8;
+    // ---- dequantise the gathered bytes into LDS (bf16 key-major, fp16 channel-major)
+    {
       uint32_t rows[8][4];     // fp16 pairs of the 8 keys, transposed below
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int key = kc + t0 + j;
-        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int valid = 0;
-        if (key < k1) {
-          if (key < nsel) {
-            const int32_t p = idxr[key];
-            if (p >= 0 && (int64_t)p < a.n_ent) {
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(codes_s + (int64_t)p * (kD / 2) + c0 / 2);
-              const float sv = e4m3_to_f32(scales_s[(int64_t)p * (kD / kGroup) + c0 / kGroup]);
-              fp4x8_to_f32(w, sv, f);
-              valid = 1;
-            }
-          } else {
-            int slot = swst + (key - nsel);
-            if (slot >= a.swa_cap) slot -= a.swa_cap;
-            const uint2 w = *reinterpret_cast<const uint2*>(swa_s + (int64_t)slot * kD + c0);
-            fp8x8_to_f32(w.x, w.y, f);
-            valid = 1;
-          }
+        float f[8];
+        if (G.kind[j] == 1) {
+          fp4x8_to_f32(G.code[j], e4m3_to_f32(G.scale[j]), f);
+        } else if (G.kind[j] == 2) {
+          fp8x8_to_f32(G.swa[j].x, G.swa[j].y, f);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = 0.0f;
         }
         *reinterpret_cast<uint4*>(sh.kr + (t0 + j) * kKrStride + c0 * 2) =
             make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
 #pragma unroll
         for (int q = 0; q < 4; ++q) rows[j][q] = pack_f16_exact(f[2 * q], f[2 * q + 1]);
-        if (cb == 0) sh.kvalid[t0 + j] = valid;
+        if (cb == 0) sh.kvalid[t0 + j] = G.kind[j] != 0;
       }
       // transpose the 8x8 fp16 block: channel c0+cc gets keys t0..t0+7
 #pragma unroll
@@ -152,10 +195,14 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
         uint32_t t[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) t[q] = __builtin_amdgcn_perm(rows[2 * q + 1][d], rows[2 * q][d], sel);
-        *reinterpret_cast<uint4*>(sh.kt + (c0 + cc) * kKtStride + t0 * 2) = make_uint4(t[0], t[1], t[2], t[3]);
+        *reinterpret_cast<uint4*>(sh.kt + kt_off(c0 + cc, t0 * 2)) = make_uint4(t[0], t[1], t[2], t[3]);
       }
     }
     __syncthreads();
+    // the gather registers are free again: the next chunk's loads fly during
+    // this chunk's MFMAs and are consumed by the next dequantisation
+    if (kc + kKeyChunk < k1) issue(kc + kKeyChunk, G);
+    if (!computes) continue;
 
     // ---- S^T = K Q^T for the wave's 16 heads: lane holds head n, keys 4g+i and 16+4g+i
     float s[8];
@@ -204,9 +251,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
     // ---- O^T[c][h] += K^T P^T (fp16): A rows = channels, k-slot j <-> key 4g+j / 16+4g+j-4
 #pragma unroll
     for (int ct = 0; ct < kD / 16; ++ct) {
-      const uint8_t* trow = sh.kt + (ct * 16 + n) * kKtStride;
-      const uint2 lo = *reinterpret_cast<const uint2*>(trow + 8 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(trow + 32 + 8 * g);
+      const int c = ct * 16 + n;
+      const uint2 lo = *reinterpret_cast<const uint2*>(sh.kt + kt_off(c, 8 * g));
+      const uint2 hi = *reinterpret_cast<const uint2*>(sh.kt + kt_off(c, 32 + 8 * g));
       v8h ka;
       uint32_t* kaw = reinterpret_cast<uint32_t*>(&ka);
       kaw[0] = lo.x; kaw[1] = lo.y; kaw[2] = hi.x; kaw[3] = hi.y;
@@ -216,6 +263,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
     }
   }
 
+  if (!computes) return;
   // ---- finish: the full sum for head n lives across the 4 lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -271,10 +319,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  const int waves = min(kAttnMaxWaves, a.n_heads / 16);
   const int hgroups = (a.n_heads + 63) / 64;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hgroups),
-                     dim3(64 * waves), 0, stream, a);
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -37,8 +37,12 @@ struct ItemMap {
   int32_t list_len;
 };
 
+constexpr int kFiltChunk = 4096;          // items per filter workgroup
+constexpr int64_t kMaxItems = 1LL << 24;  // items one top-k stage walks per row
+
 struct ScoreArgs {
   ItemMap im;
+  int32_t row_stride;       // floats between score rows (multiple of 4)
   int32_t n_rows;
   int64_t n_seq;
   const int32_t* row_seq;
@@ -55,13 +59,19 @@ struct SelectArgs {
   ItemMap im;
   int32_t n_rows;
   int32_t k;
-  const float* scores;      // [R][n_items]
+  int32_t row_stride;       // floats between score rows (multiple of 4)
+  const float* scores;      // [R][row_stride]
   const uint32_t* hist;     // [R][kHistBins]
+  uint64_t* cand;           // [R][n_chunks][kFiltChunk] candidate composite keys
+  uint32_t* cand_count;     // [R][n_chunks]
+  int32_t n_chunks;         // ceil(n_items / kFiltChunk)
   int32_t* out_idx;         // [R][k]
   float* out_score;         // [R][k] or null
 };
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
+int score_resident_wgs();
+hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);
 
 struct AttnArgs {

@@ -144,7 +144,9 @@ int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_e
  *   candidate     cand != NULL: select among cand[r][0..n_cand) (distinct
  *                 entry ids; -1 and ids >= n_valid are skipped), e.g. a pool
  *                 kept from an earlier layer.
- * Supported: 1 <= top_k <= 2048, 1 <= keep_blocks <= 2048.
+ * Supported: 1 <= top_k <= 2048, 1 <= keep_blocks <= 2048, and at most
+ * 2^24 items per row in one stage (entries in flat mode, blocks in the
+ * coarse stage, candidates in candidate mode).
  */
 typedef struct {
   int32_t n_rows;           /* R >= 1                                           */
@@ -238,9 +240,11 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
 #define CSA2_SITE_SCORE_COARSE 4   /* indexer scan over block summaries         */
 #define CSA2_SITE_SCORE_POOL 5     /* indexer scan over the kept blocks' pool   */
 #define CSA2_SITE_SCORE_CAND 6     /* indexer scan over a candidate list        */
-#define CSA2_SITE_SELECT 7         /* top-k selection (every stage)             */
+#define CSA2_SITE_SELECT 7         /* top-k exact selection (every stage)       */
 #define CSA2_SITE_ATTN 8           /* sparse + window attention                 */
 #define CSA2_SITE_ATTN_COMBINE 9   /* merge of the attention key splits         */
+#define CSA2_SITE_FILTER 10        /* top-k candidate filter (every stage)      */
+#define CSA2_SITE_FILL 11          /* indexer histogram clear                   */
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches);
 int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);
