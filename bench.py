@@ -92,7 +92,7 @@ class InputSet:
         self.idx = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-        self.ws_idx = torch.empty(max(256, C.indexer_topk_workspace(
+        self.ws_idx = torch.zeros(max(256, C.indexer_topk_workspace(
             self.q_idx, self.keys, w["k"], block_keys=self.summ, keep_blocks=w["keep"] or 2048)),
             dtype=torch.uint8, device="cuda")
         need = C.sparse_attn_workspace(self.q, self.idx, swa=self.swa, swa_len=self.swa_len, codes=self.codes)

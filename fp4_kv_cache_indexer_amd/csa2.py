@@ -79,7 +79,7 @@ EXPORTS = (
 )
 
 SITES = dict(kv_quant=1, block_summary=2, score_flat=3, score_coarse=4, score_pool=5,
-             score_cand=6, select=7, attn=8, attn_combine=9, filter=10, fill=11)
+             score_cand=6, select=7, attn=8, attn_combine=9, filter=10)
 
 
 def lib():
@@ -240,7 +240,8 @@ def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_
     L = lib()
     need = L.csa2_indexer_topk_workspace(ctypes.byref(a))
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        # must be zero before first use; the library leaves it zeroed after
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(L.csa2_indexer_topk(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out_idx
 

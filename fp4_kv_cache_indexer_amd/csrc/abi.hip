@@ -281,7 +281,6 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   if (!aligned(ws, 256)) return fail(CSA2_EINVAL, "indexer: workspace not 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e;
 
   csa2::ItemMap im0{};
   im0.n_seq = a->n_seq;
@@ -302,12 +301,10 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   se.cand_count = reinterpret_cast<uint32_t*>(w + p.off_count);
   se.n_chunks = p.chunks;
 
+  // histograms start at zero (the caller zeroes the workspace once) and the
+  // select kernel leaves them zeroed again
   uint32_t* hist0 = reinterpret_cast<uint32_t*>(w + p.off_hist0);
   float* scores0 = reinterpret_cast<float*>(w + p.off_scores0);
-  // the two histograms of the hierarchical mode are adjacent: one fill
-  const size_t nhist = (size_t)p.R * csa2::kHistBins * (p.mode == 1 ? 2 : 1);
-  if ((e = timed(CSA2_SITE_FILL, s, [&] { return csa2::launch_fill_u32(hist0, nhist, 0u, s); })) != hipSuccess)
-    return hip_fail(e, "indexer fill");
 
   // one top-k stage: score -> filter -> select
   auto stage = [&](int site, const csa2::ItemMap& im, const uint8_t* keys, int64_t seq_rows, int32_t stride,
@@ -329,6 +326,11 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
     se.hist = hist;
     se.out_idx = out_idx;
     se.out_score = out_score;
+    if (im.n_items <= csa2::kRowMaxItems || p.R >= csa2::kRowMinRows) {
+      if ((e2 = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_row(se, s); })) != hipSuccess)
+        return hip_fail(e2, "indexer top-k");
+      return CSA2_OK;
+    }
     if ((e2 = timed(CSA2_SITE_FILTER, s, [&] { return csa2::launch_topk_filter(se, s); })) != hipSuccess)
       return hip_fail(e2, "indexer filter");
     if ((e2 = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_select(se, s); })) != hipSuccess)
@@ -408,7 +410,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
   g_err.clear();
-  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_FILL)
+  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_FILTER)
     return fail(CSA2_EINVAL, "kernel_timer_start: unknown site %d", site);
   if (max_launches < 1 || max_launches > 1000000)
     return fail(CSA2_EINVAL, "kernel_timer_start: max_launches %d outside [1, 1e6]", max_launches);

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // this thread's unit of every chunk: keys t0..t0+7, channels c0..c0+7
   const int cb = tid & 63, kg = tid >> 6;
   const int c0 = cb * 8, t0 = kg * 8;
-  __syncthreads();                                   // sidx ready
+  lds_barrier();                                     // sidx ready (q loads stay in flight)
 
   // issue every load of a chunk at once (no data-dependent branches)
   auto issue = [&](int kc, Gather& G) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   Gather G;
   if (k0 < k1) issue(k0, G);
   for (int kc = k0; kc < k1; kc += kKeyChunk) {
-    __syncthreads();   // the previous chunk's LDS reads are done
+    lds_barrier();     // the previous chunk's LDS reads are done
     // ---- dequantise the gathered bytes into LDS (bf16 key-major, fp16 channel-major)
     {
       uint32_t rows[8][4];     // fp16 pairs of the 8 keys, transposed below
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint4*>(sh.kt + kt_off(c0 + cc, t0 * 2)) = make_uint4(t[0], t[1], t[2], t[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // the gather registers are free again: the next chunk's loads fly during
     // this chunk's MFMAs and are consumed by the next dequantisation
     if (kc + kKeyChunk < k1) issue(kc + kKeyChunk, G);

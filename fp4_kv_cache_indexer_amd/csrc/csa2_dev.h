@@ -92,4 +92,14 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (vmcnt(0)), which
+// drains prefetches issued before it; use this one where only LDS data is
+// exchanged across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace csa2

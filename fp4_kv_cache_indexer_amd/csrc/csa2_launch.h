@@ -15,7 +15,6 @@ hipError_t launch_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_en
                                 int64_t blk_begin, int64_t blk_end, uint8_t* summ,
                                 hipStream_t stream);
 
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream);
 
 // Which items a row of the score/select kernels walks and how they map to
 // cache positions.
@@ -61,7 +60,7 @@ struct SelectArgs {
   int32_t k;
   int32_t row_stride;       // floats between score rows (multiple of 4)
   const float* scores;      // [R][row_stride]
-  const uint32_t* hist;     // [R][kHistBins]
+  uint32_t* hist;           // [R][kHistBins], zeroed after use
   uint64_t* cand;           // [R][n_chunks][kFiltChunk] candidate composite keys
   uint32_t* cand_count;     // [R][n_chunks]
   int32_t n_chunks;         // ceil(n_items / kFiltChunk)
@@ -73,6 +72,11 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
 int score_resident_wgs();
 hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);
+// whole-row top-k (filter + select in one workgroup per row); preferred up to
+// kRowMaxItems items per row or from kRowMinRows rows
+constexpr int64_t kRowMaxItems = 1 << 15;
+constexpr int32_t kRowMinRows = 256;
+hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream);
 
 struct AttnArgs {
   int32_t n_rows, n_heads;

@@ -12,14 +12,13 @@
 //           top-k tie band; the fp16 MFMA matches a float32 FMA chain.)  Each
 //           workgroup also histograms the top 12 bits of the order key of its
 //           scores in LDS and folds that into a per-row histogram.
-//   filter: many workgroups per row.  Each reads the row histogram, finds
+//   top-k:  many workgroups per row.  Each reads the row histogram, finds
 //           the bin holding the k-th largest score and compacts the items of
 //           its chunk in that bin or above, in item order, as composite keys
-//           (order key of the score, ~position).
-//   select: one workgroup per row over those candidates (a few thousand):
-//           an MSB-first radix select finds the k-th largest composite key
-//           exactly (ties -> lower position), and the kept candidates are
-//           written in candidate order, which is ascending position.
+//           (order key of the score, ~position).  The row's last workgroup
+//           then finds the k-th largest composite key exactly with an
+//           MSB-first radix select (ties -> lower position) and writes the
+//           kept candidates in candidate order, which is ascending position.
 #include "csa2_dev.h"
 #include "csa2_launch.h"
 
@@ -61,19 +60,6 @@ __device__ __forceinline__ int64_t item_pos(const ItemMap& im, int r, int64_t i,
   return (c >= 0 && (int64_t)c < nv) ? (int64_t)c : -1;
 }
 
-__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  const size_t blocks = min((n + 255) / 256, (size_t)4096);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, v);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // score kernel
 // ---------------------------------------------------------------------------
@@ -110,7 +96,10 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
 
 // DB: double-buffer the tile groups of a wave; MINW: waves per SIMD the
 // register budget must allow.
-template <int MODE, bool DB = false, int MINW = 4, int U = kTilesPerIter>
+// G > 0: the chunk is exactly G groups per wave and the group loop is fully
+// unrolled (straight-line code lets the compiler keep the next group's loads
+// in flight exactly); G == 0: runtime trip count.
+template <int MODE, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0>
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
   __shared__ uint32_t hist[kHistBins];
@@ -213,15 +202,30 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   v8i kA[U], kB[U];
   int32_t pA[U], pB[U];
   int64_t t0 = (int64_t)wave * U;
-  if (DB) {
+  if (G > 0) {
+    // straight-line: load group i+1 before computing group i
+    load_group(t0, kA, pA);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int64_t ti = t0 + i * gstride;
+      if (i + 1 < G) {
+        if (i & 1) load_group(ti + gstride, kA, pA); else load_group(ti + gstride, kB, pB);
+      }
+      // keep the next group's loads above this group's arithmetic
+      __builtin_amdgcn_sched_barrier(0);
+      if (i & 1) compute_group(ti, kB); else compute_group(ti, kA);
+    }
+  } else if (DB) {
     if (t0 < ntiles) load_group(t0, kA, pA);
     for (; t0 < ntiles; t0 += 2 * gstride) {
       const int64_t t1 = t0 + gstride;
       if (t1 < ntiles) load_group(t1, kB, pB);
+      __builtin_amdgcn_sched_barrier(0);
       compute_group(t0, kA);
       if (t1 >= ntiles) break;
       const int64_t t2 = t1 + gstride;
       if (t2 < ntiles) load_group(t2, kA, pA);
+      __builtin_amdgcn_sched_barrier(0);
       compute_group(t1, kB);
     }
   } else {
@@ -274,9 +278,6 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
 
 constexpr int kFiltThreads = 256;
 constexpr int kFiltRound = kFiltThreads * 4;           // items per compaction round
-constexpr int kSelThreads = 1024;
-constexpr int kSelCap = 12288;                         // candidates held in LDS
-constexpr int kMaxChunks = kMaxItems / kFiltChunk;
 
 // Composite order key: score order first, then lower position first.
 __device__ __forceinline__ uint64_t comp_key(uint32_t okey, int64_t pos) {
@@ -287,6 +288,16 @@ __device__ __forceinline__ float comp_score(uint64_t K) { return order_key_inv((
 
 // Exclusive prefix sum over a workgroup of NT threads (wave64); `total`
 // receives the sum.  Uses wsum[NT/64] of shared scratch; ends synchronised.
+// Branch-free: an in-bounds float4 load (the row's stride is a multiple of 4
+// and i0 is too) with lanes past the row's items set to NaN.  A branch around
+// a tail path would make the compiler wait for each load before the next.
+__device__ __forceinline__ float4 load_items4(const float* srow, int64_t i0, int64_t n_row, int64_t stride) {
+  const float4 t = *reinterpret_cast<const float4*>(srow + (i0 < stride ? i0 : 0));
+  const float nan = __uint_as_float(0x7FC00000u);
+  return make_float4(i0 + 0 < n_row ? t.x : nan, i0 + 1 < n_row ? t.y : nan,
+                     i0 + 2 < n_row ? t.z : nan, i0 + 3 < n_row ? t.w : nan);
+}
+
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -297,7 +308,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     if (lane >= d) x += y;
   }
   if (lane == 63) wsum[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int off = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
@@ -306,24 +317,122 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     tot += t;
   }
   total = tot;
-  __syncthreads();
+  lds_barrier();
   return off + x - v;
 }
 
-// Filter: workgroup (chunk c, row r) finds the histogram bin holding the
-// row's k-th largest score, then writes every item of its chunk in that bin
-// or above -- a superset of the chunk's share of the top-k -- as composite
-// keys, compacted in item order, plus their count.
+constexpr int kStageCap = 4096;     // boundary-bin candidates staged in LDS
+
+constexpr int kRegKeys = 32;       // candidates per thread held in registers by the select
+constexpr int kMaxChunks = kMaxItems / kFiltChunk;
+
+struct TopkShared {
+  int wsum[kFiltThreads / 64];
+  int pair[3], n_stage;
+  int digit, above, dcount;
+  uint32_t hist[256];
+  int coff[kMaxChunks + 1];          // first flattened candidate of each chunk
+  union {
+    uint64_t stage[kStageCap];                                 // radix select
+    struct { int32_t pos[kMaxTopK]; float score[kMaxTopK]; } sel;  // candidate-mode sort
+  } u;
+};
+
+// One radix step's decision, taken by wave 0 from sh.hist[0..256): the digit
+// whose keys hold the need-th largest key (digits descending), the count of
+// keys above it and its own count.
+template <class SH>
+__device__ __forceinline__ void pick_digit(SH& sh, int need) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    uint32_t h[4], l = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { h[i] = sh.hist[4 * tid + i]; l += h[i]; }
+    uint32_t x = l;                                    // sum over lanes >= tid
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_down(x, d);
+      if (tid + d < 64) x += y;
+    }
+    uint32_t cum = x - l;
+    for (int i = 3; i >= 0; --i) {
+      if (cum < (uint32_t)need && cum + h[i] >= (uint32_t)need) {
+        sh.digit = 4 * tid + i; sh.above = (int)cum; sh.dcount = (int)h[i];
+      }
+      cum += h[i];
+    }
+  }
+}
+
+// Radix digits below the 12 histogram bits of a composite key: six 8-bit
+// digits, then one 4-bit digit.
+__device__ __forceinline__ int digit_shift(int step) { return step < 6 ? 44 - 8 * step : 0; }
+__device__ __forceinline__ int digit_width(int step) { return step < 6 ? 8 : 4; }
+
+// Threshold bin of a row from its score histogram: b*, the bin holding the
+// kk-th largest score (kk = min(k, visible items)), the count of items in the
+// bins above it and the count in b* or above; b* = -1 when every visible item
+// is kept.
+struct RowThreshold {
+  int bstar, c_above, n_cand;
+  uint32_t kk;
+};
+
+template <int NT>
+__device__ __forceinline__ void hist_load(const uint32_t* gh, uint32_t (&hv)[kHistBins / NT]) {
+#pragma unroll
+  for (int i = 0; i < kHistBins / NT; ++i) hv[i] = gh[(kHistBins / NT) * threadIdx.x + i];
+}
+
+template <int NT>
+__device__ __forceinline__ RowThreshold hist_threshold(const uint32_t (&hv)[kHistBins / NT], int k, int* wsum,
+                                                       int* sh3) {
+  const int tid = threadIdx.x;
+  constexpr int kBpt = kHistBins / NT;                         // bins per thread
+  uint32_t loc = 0;
+#pragma unroll
+  for (int i = 0; i < kBpt; ++i) loc += hv[i];
+  int tot_i;
+  const int below = block_excl_scan<NT>((int)loc, wsum, tot_i);   // bins of threads < tid
+  const uint32_t total = (uint32_t)tot_i;
+  if (tid == 0) { sh3[0] = -1; sh3[1] = 0; sh3[2] = (int)total; }
+  lds_barrier();
+  const uint32_t kk = min((uint32_t)k, total);
+  if (kk < total) {
+    const uint32_t above = total - (uint32_t)below - loc;      // bins of threads > tid
+    if (above < kk && above + loc >= kk) {
+      uint32_t cum = above;
+      for (int b = kBpt - 1; b >= 0; --b) {
+        if (cum + hv[b] >= kk) {
+          sh3[0] = kBpt * tid + b; sh3[1] = (int)cum; sh3[2] = (int)(cum + hv[b]);
+          break;
+        }
+        cum += hv[b];
+      }
+    }
+  }
+  lds_barrier();
+  return RowThreshold{sh3[0], sh3[1], sh3[2], kk};
+}
+
+template <int NT>
+__device__ __forceinline__ RowThreshold row_threshold(const uint32_t* gh, int k, int* wsum, int* sh3) {
+  uint32_t hv[kHistBins / NT];
+  hist_load<NT>(gh, hv);
+  return hist_threshold<NT>(hv, k, wsum, sh3);
+}
+
+// Filter.  Workgroup (chunk c, row r) finds b* and writes every item of its
+// chunk in b* or above -- a superset of the chunk's share of the top-k -- as
+// composite keys, compacted in item order, plus their count.
 __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a) {
-  __shared__ uint32_t sc[kFiltThreads];
   __shared__ int wsum[kFiltThreads / 64];
-  (void)sc;
-  __shared__ int s_bstar;
+  __shared__ int pair[3];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = row_valid(a.im, r);
   const int64_t n_row = row_items(a.im, nv);
   const int64_t c0 = (int64_t)c * kFiltChunk;
-  if (c0 >= n_row) return;                                   // uniform
+  if (c0 >= n_row) return;                                     // uniform
   const int64_t c1 = min(c0 + (int64_t)kFiltChunk, n_row);
 
   // this thread's items, 4 consecutive per round, loaded before the scan
@@ -332,47 +441,10 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
   float v[kRounds][4];
 #pragma unroll
   for (int rd = 0; rd < kRounds; ++rd) {
-    const int64_t i0 = c0 + (int64_t)rd * kFiltRound + 4 * tid;
-    if (i0 + 3 < c1) {
-      const float4 q = *reinterpret_cast<const float4*>(srow + i0);   // rows are 16-byte aligned
-      v[rd][0] = q.x; v[rd][1] = q.y; v[rd][2] = q.z; v[rd][3] = q.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[rd][j] = (i0 + j < c1) ? srow[i0 + j] : __uint_as_float(0x7FC00000u);
-    }
+    const float4 q = load_items4(srow, c0 + (int64_t)rd * kFiltRound + 4 * tid, c1, a.row_stride);
+    v[rd][0] = q.x; v[rd][1] = q.y; v[rd][2] = q.z; v[rd][3] = q.w;
   }
-
-  // threshold bin from the row histogram (16 bins per thread)
-  const uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  uint32_t hv[kHistBins / kFiltThreads];
-  uint32_t loc = 0;
-#pragma unroll
-  for (int i = 0; i < kHistBins / kFiltThreads; ++i) {
-    hv[i] = gh[(kHistBins / kFiltThreads) * tid + i];
-    loc += hv[i];
-  }
-  // suffix sums: scan the reversed thread order
-  int tot_i;
-  const int rev_ex = block_excl_scan<kFiltThreads>((int)loc, wsum, tot_i);   // sum over threads < tid
-  (void)rev_ex;
-  sc[tid] = loc;
-  if (tid == 0) s_bstar = -1;
-  __syncthreads();
-  const uint32_t total = (uint32_t)tot_i;
-  const uint32_t kk = min((uint32_t)a.k, total);
-  if (kk < total) {
-    // items in bins above this thread's 16 = total - (threads <= tid)
-    const uint32_t above = total - (uint32_t)rev_ex - loc;
-    if (above < kk && above + loc >= kk) {
-      uint32_t cum = above;
-      for (int b = kHistBins / kFiltThreads - 1; b >= 0; --b) {
-        if (cum + hv[b] >= kk) { s_bstar = (kHistBins / kFiltThreads) * tid + b; break; }
-        cum += hv[b];
-      }
-    }
-  }
-  __syncthreads();
-  const int bstar = s_bstar;
+  const RowThreshold th = row_threshold<kFiltThreads>(a.hist + (int64_t)r * kHistBins, a.k, wsum, pair);
 
   // compaction in item order
   uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk;
@@ -385,7 +457,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ok[j] = order_key(v[rd][j]);
-      const bool keep = (v[rd][j] == v[rd][j]) && (int)(ok[j] >> (32 - kHistBits)) >= bstar;
+      const bool keep = (v[rd][j] == v[rd][j]) && (int)(ok[j] >> (32 - kHistBits)) >= th.bstar;
       flag |= (int)keep << j;
     }
     int tot;
@@ -399,141 +471,394 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
   if (tid == 0) a.cand_count[(int64_t)r * a.n_chunks + c] = (uint32_t)written;
 }
 
-hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream) {
-  if (a.n_rows == 0 || a.n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)a.n_chunks, (unsigned)a.n_rows),
-                     dim3(kFiltThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-struct SelShared {
-  uint64_t key[kSelCap];
-  int32_t sel_pos[kMaxTopK];     // candidate mode: kept ids before sorting
-  float sel_score[kMaxTopK];
-  uint32_t chunk_off[kMaxChunks + 1];
-  uint32_t hist[256];
-  uint32_t suf[257];
-  int wsum[kSelThreads / 64];
-  int digit, above, dcount;
-};
-
-// Select: exact top-k of the row's candidates (MSB-first radix on the
-// composite keys), written in candidate order, which is ascending position.
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  SelShared& sh = *reinterpret_cast<SelShared*>(smem_raw);
+// Select.  One workgroup per row settles the k-th composite key T exactly:
+// its top 12 bits are b*, the rest is found digit by digit (MSB first) among
+// the candidates of bin b*.  The kept candidates (keys >= T) are written in
+// candidate order, which is ascending position (candidate mode sorts).  The
+// row's histogram is then cleared for the next call.
+__global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a) {
+  __shared__ TopkShared sh;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = row_valid(a.im, r);
   const int64_t n_row = row_items(a.im, nv);
-  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
-  const uint32_t* cnt = a.cand_count + (int64_t)r * a.n_chunks;
-  const uint64_t* crow = a.cand + (int64_t)r * a.n_chunks * kFiltChunk;
   int32_t* oi = a.out_idx + (int64_t)r * a.k;
   float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
-
-  // row histogram: valid items, the bin b* holding the k-th largest score and
-  // the count of items above it (4 bins per thread)
-  const uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  uint32_t hv[kHistBins / kSelThreads];
-  uint32_t loc = 0;
-#pragma unroll
-  for (int i = 0; i < kHistBins / kSelThreads; ++i) {
-    hv[i] = gh[(kHistBins / kSelThreads) * tid + i];
-    loc += hv[i];
+  if (n_row == 0) {                                            // uniform: nothing visible
+    for (int j = tid; j < a.k; j += kFiltThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.0f;
+    }
+    return;
   }
-  int tot_valid;
-  const int below = block_excl_scan<kSelThreads>((int)loc, sh.wsum, tot_valid);
-  const int kk = min(a.k, tot_valid);
-  if (tid == 0) { sh.digit = -1; sh.above = 0; }
-  __syncthreads();
-  if (kk < tot_valid) {
-    const uint32_t above = (uint32_t)(tot_valid - below) - loc;
-    if (above < (uint32_t)kk && above + loc >= (uint32_t)kk) {
-      uint32_t cum = above;
-      for (int b = kHistBins / kSelThreads - 1; b >= 0; --b) {
-        if (cum + hv[b] >= (uint32_t)kk) { sh.digit = (kHistBins / kSelThreads) * tid + b; sh.above = (int)cum; break; }
-        cum += hv[b];
+  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
+  uint32_t* gh = a.hist + (int64_t)r * kHistBins;
+  const RowThreshold th = row_threshold<kFiltThreads>(gh, a.k, sh.wsum, sh.pair);
+  const int bstar = th.bstar, c_above = th.c_above;
+  const uint32_t kk = th.kk;
+  const int64_t crow0 = (int64_t)r * a.n_chunks * kFiltChunk;
+  const uint32_t* cnt = a.cand_count + (int64_t)r * a.n_chunks;
+
+  // flattened candidate offsets: chunk ch holds [coff[ch], coff[ch + 1])
+  int n_cand;
+  {
+    constexpr int kCpt = kMaxChunks / kFiltThreads;
+    int cc[kCpt], loc = 0;
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) {
+      const int ch = kCpt * tid + i;
+      cc[i] = ch < nch ? (int)cnt[ch] : 0;
+      loc += cc[i];
+    }
+    int base = block_excl_scan<kFiltThreads>(loc, sh.wsum, n_cand);
+#pragma unroll
+    for (int i = 0; i < kCpt; ++i) {
+      const int ch = kCpt * tid + i;
+      if (ch < nch) sh.coff[ch] = base;
+      base += cc[i];
+    }
+    if (tid == 0) sh.coff[nch] = n_cand;
+    __syncthreads();
+  }
+
+  // threshold T: the kk-th largest composite key (kept keys are >= T); its
+  // top 12 bits are b*, the rest is found digit by digit among the
+  // candidates of bin b*
+  const bool sort = a.im.mode == kItemsCand;
+  uint64_t T = 0;
+  int nsel;
+  if (n_cand <= kFiltThreads * kRegKeys) {                   // uniform
+    // each thread holds a run of kRegKeys consecutive candidates
+    const int j0 = tid * kRegKeys;
+    const int nm = max(0, min(kRegKeys, n_cand - j0));
+    uint64_t K[kRegKeys];
+    {
+      int lo = 0, hi = nch;                                  // last chunk with coff <= j0
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sh.coff[mid] <= j0) lo = mid; else hi = mid;
+      }
+      int ch = lo;
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i) {
+        K[i] = 0;
+        if (i < nm) {
+          while (sh.coff[ch + 1] <= j0 + i) ++ch;
+          K[i] = a.cand[crow0 + (int64_t)ch * kFiltChunk + (j0 + i - sh.coff[ch])];
+        }
       }
     }
-  }
-  __syncthreads();
-  const int bstar = sh.digit;
-  const int c_above = sh.above;
-
-  // chunk offsets of the filtered candidates
-  int C = 0;
-  {
-    int running = 0;
-    for (int base = 0; base < nch; base += kSelThreads) {
-      const int i = base + tid;
-      const int v = i < nch ? (int)cnt[i] : 0;
-      int t;
-      const int ex = block_excl_scan<kSelThreads>(v, sh.wsum, t);
-      if (i < nch) sh.chunk_off[i] = (uint32_t)(running + ex);
-      running += t;
+    if (bstar >= 0) {
+      int need = (int)kk - c_above;
+      uint64_t prefix = (uint64_t)bstar;
+      for (int step = 0; step < 7; ++step) {
+        const int dshift = digit_shift(step), w = digit_width(step);
+        const uint32_t dmask = (1u << w) - 1u;
+        sh.hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i)
+          if (i < nm && (K[i] >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K[i] >> dshift) & dmask], 1u);
+        __syncthreads();
+        pick_digit(sh, need);
+        __syncthreads();
+        need -= sh.above;
+        prefix = (prefix << w) | (uint64_t)sh.digit;
+        const bool done = sh.dcount == need || dshift == 0;  // every key with this prefix is kept
+        __syncthreads();
+        if (done) {
+          T = prefix << dshift;
+          break;
+        }
+      }
     }
-    C = running;
-    if (tid == 0) sh.chunk_off[nch] = (uint32_t)C;
-  }
-  __syncthreads();
-  const bool in_lds = C <= kSelCap;
-
-  // candidate j -> composite key (binary search over the chunk offsets)
-  auto gkey = [&](int j) -> uint64_t {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int)sh.chunk_off[mid] <= j) lo = mid; else hi = mid - 1;
+    // kept keys, written in candidate order
+    int nk = 0;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) nk += (i < nm && kk > 0 && K[i] >= T) ? 1 : 0;
+    int nout;
+    int slot = block_excl_scan<kFiltThreads>(nk, sh.wsum, nout);
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      if (i < nm && kk > 0 && K[i] >= T) {
+        if (slot < a.k) {
+          if (sort) {
+            sh.u.sel.pos[slot] = comp_pos(K[i]);
+            sh.u.sel.score[slot] = comp_score(K[i]);
+          } else {
+            oi[slot] = comp_pos(K[i]);
+            if (os) os[slot] = comp_score(K[i]);
+          }
+        }
+        ++slot;
+      }
     }
-    return crow[(int64_t)lo * kFiltChunk + (j - (int)sh.chunk_off[lo])];
-  };
-  if (in_lds) {
-    for (int j = tid; j < C; j += kSelThreads) sh.key[j] = gkey(j);
-  }
-  __syncthreads();
-  auto key_at = [&](int j) -> uint64_t { return in_lds ? sh.key[j] : gkey(j); };
-
-  // threshold T: the kk-th largest composite key (all kept keys are >= T).
-  // Its top 12 bits are b*; the rest is found digit by digit among the
-  // candidates of bin b*.
-  uint64_t T = 0;
-  if (bstar >= 0) {
-    int need = kk - c_above;
-    uint64_t prefix = (uint64_t)bstar;
-    // remaining 52 bits: six 8-bit digits, then one 4-bit digit
-    for (int step = 0; step < 7; ++step) {
-      const int dshift = step < 6 ? 44 - 8 * step : 0;     // digit = bits [dshift, dshift + w)
-      const int w = step < 6 ? 8 : 4;
-      const uint32_t dmask = (1u << w) - 1u;
-      for (int b = tid; b < 256; b += kSelThreads) sh.hist[b] = 0u;
+    nsel = min(nout, a.k);
+  } else {
+    // many candidates (wide ties): walk them in global memory, staging the
+    // candidates of bin b* in LDS when they fit
+    if (bstar >= 0) {
+      if (tid == 0) sh.n_stage = 0;
       __syncthreads();
-      for (int j = tid; j < C; j += kSelThreads) {
-        const uint64_t K = key_at(j);
+      for (int ch = 0; ch < nch; ++ch) {
+        const int cn = (int)cnt[ch];
+        for (int j = tid; j < cn; j += kFiltThreads) {
+          const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
+          if ((int)(K >> 52) == bstar) {
+            const int slot = atomicAdd(&sh.n_stage, 1);
+            if (slot < kStageCap) sh.u.stage[slot] = K;
+          }
+        }
+      }
+      __syncthreads();
+      const int n_st = sh.n_stage;
+      const bool staged = n_st <= kStageCap;
+      int need = (int)kk - c_above;
+      uint64_t prefix = (uint64_t)bstar;
+      for (int step = 0; step < 7; ++step) {
+        const int dshift = digit_shift(step), w = digit_width(step);
+        const uint32_t dmask = (1u << w) - 1u;
+        sh.hist[tid] = 0u;
+        __syncthreads();
+        if (staged) {
+          for (int j = tid; j < n_st; j += kFiltThreads) {
+            const uint64_t K = sh.u.stage[j];
+            if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
+          }
+        } else {
+          for (int ch = 0; ch < nch; ++ch) {
+            const int cn = (int)cnt[ch];
+            for (int j = tid; j < cn; j += kFiltThreads) {
+              const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
+              if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
+            }
+          }
+        }
+        __syncthreads();
+        pick_digit(sh, need);
+        __syncthreads();
+        need -= sh.above;
+        prefix = (prefix << w) | (uint64_t)sh.digit;
+        const bool done = sh.dcount == need || dshift == 0;
+        __syncthreads();
+        if (done) {
+          T = prefix << dshift;
+          break;
+        }
+      }
+    }
+    int nout = 0;
+    for (int base = 0; base < n_cand; base += kFiltThreads) {
+      const int j = base + tid;
+      uint64_t K = 0;
+      bool keep = false;
+      if (j < n_cand && kk > 0) {
+        int lo = 0, hi = nch;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (sh.coff[mid] <= j) lo = mid; else hi = mid;
+        }
+        K = a.cand[crow0 + (int64_t)lo * kFiltChunk + (j - sh.coff[lo])];
+        keep = K >= T;
+      }
+      int t;
+      const int slot = nout + block_excl_scan<kFiltThreads>(keep ? 1 : 0, sh.wsum, t);
+      if (keep && slot < a.k) {
+        if (sort) {
+          sh.u.sel.pos[slot] = comp_pos(K);
+          sh.u.sel.score[slot] = comp_score(K);
+        } else {
+          oi[slot] = comp_pos(K);
+          if (os) os[slot] = comp_score(K);
+        }
+      }
+      nout += t;
+    }
+    nsel = min(nout, a.k);
+  }
+
+  // candidate mode: the caller's list has any order, sort by position
+  if (sort) {
+    int n2 = 1;
+    while (n2 < nsel) n2 <<= 1;
+    for (int i = nsel + tid; i < n2; i += kFiltThreads) { sh.u.sel.pos[i] = 0x7FFFFFFF; sh.u.sel.score[i] = 0.f; }
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < n2; i += kFiltThreads) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool up = (i & size) == 0;
+            const int32_t pi = sh.u.sel.pos[i], pj = sh.u.sel.pos[j];
+            if ((pi > pj) == up) {
+              sh.u.sel.pos[i] = pj; sh.u.sel.pos[j] = pi;
+              const float t2 = sh.u.sel.score[i]; sh.u.sel.score[i] = sh.u.sel.score[j]; sh.u.sel.score[j] = t2;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int j = tid; j < nsel; j += kFiltThreads) {
+      oi[j] = sh.u.sel.pos[j];
+      if (os) os[j] = sh.u.sel.score[j];
+    }
+  }
+  for (int j = nsel + tid; j < a.k; j += kFiltThreads) {
+    oi[j] = -1;
+    if (os) os[j] = 0.0f;
+  }
+
+  // leave the row's histogram zeroed for the next call
+  for (int b = tid; b < kHistBins; b += kFiltThreads) gh[b] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Whole-row top-k: one workgroup of 1024 threads per row does filter and
+// select together when the row is short enough to stream through one CU
+// (used up to kRowMaxItems items, or with many rows).  The number of
+// candidates -- items in bin b* or above -- is known from the histogram
+// before any score is read, so they go to LDS when they fit, else to the
+// row's candidate area in the workspace; the same code serves both.
+// ---------------------------------------------------------------------------
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowCap = 12288;                 // candidates held in LDS
+constexpr int kRowU = 2;                       // float4 loads per thread per round
+constexpr int kRowSub = kRowThreads * 4;       // items per sub-round
+constexpr int kRowRound = kRowSub * kRowU;     // items per round (one barrier)
+
+struct RowShared {
+  uint64_t cbuf[kRowCap];
+  int32_t sel_pos[kMaxTopK];
+  float sel_score[kMaxTopK];
+  int wtot[2][kRowU][kRowWaves];
+  int wsum[kRowWaves];
+  uint32_t hist[256];
+  int pair[3];
+  int digit, above, dcount;
+};
+
+// Raw loads of one round (addresses clamped into the row; masking happens in
+// row_compact), unconditional so that nothing waits on them before use.  In
+// pool mode each thread's 4 items of a sub-round share one block, whose id
+// comes with them (other modes load a discarded word of the score row).
+__device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float* srow, int64_t base,
+                                         float4 (&v)[kRowU], int32_t (&blk)[kRowU]) {
+  const bool pool = a.im.mode == kItemsPool;
+  const int32_t* lrow = pool ? a.im.list + (int64_t)r * a.im.list_len : reinterpret_cast<const int32_t*>(srow);
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * threadIdx.x;
+    v[u] = *reinterpret_cast<const float4*>(srow + (i0 < a.row_stride ? i0 : 0));
+    blk[u] = lrow[pool && (i0 >> 3) < a.im.list_len ? (i0 >> 3) : 0];
+  }
+}
+
+// Appends the round's items in bin b* or above to cbuf in item order: wave
+// offsets from ballots, round offsets from the per-wave totals in LDS.
+__device__ __forceinline__ int row_compact(const SelectArgs& a, int r, int64_t nv, int64_t n_row, int64_t base,
+                                           int bstar,
+                                           const float4 (&v)[kRowU], const int32_t (&blk)[kRowU], uint64_t* cbuf,
+                                           int cap, int written, int parity, RowShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t ok[kRowU][4];
+  int fl[kRowU], off[kRowU];
+  const float nan = __uint_as_float(0x7FC00000u);
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * tid;
+    const float x[4] = {i0 + 0 < n_row ? v[u].x : nan, i0 + 1 < n_row ? v[u].y : nan,
+                        i0 + 2 < n_row ? v[u].z : nan, i0 + 3 < n_row ? v[u].w : nan};
+    fl[u] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[u][j] = order_key(x[j]);
+      const bool keep = (x[j] == x[j]) && (int)(ok[u][j] >> (32 - kHistBits)) >= bstar;
+      fl[u] |= (int)keep << j;
+    }
+    int o = 0, t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t b = __ballot((fl[u] >> j) & 1);
+      o += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+      t += __popcll(b);
+    }
+    off[u] = o;
+    if (lane == 0) sh.wtot[parity][u][wave] = t;
+  }
+  lds_barrier();                               // the next round's loads stay in flight
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const int t = sh.wtot[parity][u][w];
+      pre += w < wave ? t : 0;
+      tot += t;
+    }
+    int slot = written + pre + off[u];
+    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * tid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((fl[u] >> j) & 1) {
+        // kept items are visible ones: pool positions come from the block id
+        const int64_t pos = a.im.mode == kItemsPool   ? (int64_t)blk[u] * kBlockPos + ((i0 + j) & 7)
+                            : a.im.mode == kItemsCand ? item_pos(a.im, r, i0 + j, nv)
+                                                      : i0 + j;
+        if (slot < cap) cbuf[slot] = comp_key(ok[u][j], pos);
+        ++slot;
+      }
+    written += tot;
+  }
+  return written;
+}
+
+// Collect, select and write one row with the candidates in cbuf (LDS or
+// global).  Returns the number of ids written to the output (<= k).
+__device__ __forceinline__ int row_select(const SelectArgs& a, int r, int64_t nv, int64_t n_row,
+                                          const RowThreshold& th, float4 (&va)[kRowU], int32_t (&ba)[kRowU],
+                                          uint64_t* cbuf, int cap,
+                                          RowShared& sh, int32_t* oi, float* os, bool sort) {
+  const int tid = threadIdx.x;
+  const float* srow = a.scores + (int64_t)r * a.row_stride;
+
+  // 1. candidates in item order, loads one round ahead (va holds round 0)
+  int written = 0, parity = 0;
+  float4 vb[kRowU];
+  int32_t bb[kRowU];
+  for (int64_t base = 0; base < n_row; base += 2 * kRowRound) {
+    row_load(a, r, srow, base + kRowRound, vb, bb);
+    written = row_compact(a, r, nv, n_row, base, th.bstar, va, ba, cbuf, cap, written, parity, sh);
+    parity ^= 1;
+    if (base + kRowRound >= n_row) break;
+    row_load(a, r, srow, base + 2 * kRowRound, va, ba);
+    written = row_compact(a, r, nv, n_row, base + kRowRound, th.bstar, vb, bb, cbuf, cap, written, parity, sh);
+    parity ^= 1;
+  }
+  __syncthreads();
+  const int n_cand = min(written, cap);        // equal to th.n_cand: the histogram counted these items
+
+  // 2. threshold key T among the candidates of bin b*
+  uint64_t T = 0;
+  if (th.bstar >= 0) {
+    int need = (int)th.kk - th.c_above;
+    uint64_t prefix = (uint64_t)th.bstar;
+    for (int step = 0; step < 7; ++step) {
+      const int dshift = digit_shift(step), w = digit_width(step);
+      const uint32_t dmask = (1u << w) - 1u;
+      if (tid < 256) sh.hist[tid] = 0u;
+      __syncthreads();
+      for (int j = tid; j < n_cand; j += kRowThreads) {
+        const uint64_t K = cbuf[j];
         if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
       }
       __syncthreads();
-      if (tid < 64) {                                      // one wave finds the digit
-        uint32_t h[4], l = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { h[i] = sh.hist[4 * tid + i]; l += h[i]; }
-        uint32_t x = l;                                    // sum over lanes >= tid
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t y = __shfl_down(x, d);
-          if (tid + d < 64) x += y;
-        }
-        uint32_t cum = x - l;
-        for (int i = 3; i >= 0; --i) {
-          if (cum < (uint32_t)need && cum + h[i] >= (uint32_t)need) {
-            sh.digit = 4 * tid + i; sh.above = (int)cum; sh.dcount = (int)h[i];
-          }
-          cum += h[i];
-        }
-      }
+      pick_digit(sh, need);
       __syncthreads();
       need -= sh.above;
       prefix = (prefix << w) | (uint64_t)sh.digit;
-      const bool done = sh.dcount == need || dshift == 0;  // every key with this prefix is kept
+      const bool done = sh.dcount == need || dshift == 0;    // every key with this prefix is kept
       __syncthreads();
       if (done) {
         T = prefix << dshift;
@@ -542,36 +867,67 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
     }
   }
 
-  // write the kept keys in candidate order -- ascending position, except in
-  // candidate mode, where the caller's list has any order and a sort follows
-  const bool sort = a.im.mode == kItemsCand;
-  int written = 0;
-  for (int base = 0; base < C; base += kSelThreads) {
-    const int j = base + tid;
-    uint64_t K = 0;
-    const bool keep = j < C && kk > 0 && (K = key_at(j)) >= T;
-    int t;
-    const int slot = written + block_excl_scan<kSelThreads>(keep ? 1 : 0, sh.wsum, t);
-    if (keep && slot < a.k) {
-      if (sort) {
-        sh.sel_pos[slot] = comp_pos(K);
-        sh.sel_score[slot] = comp_score(K);
-      } else {
-        oi[slot] = comp_pos(K);
-        if (os) os[slot] = comp_score(K);
+  // 3. kept keys (>= T) in candidate order: each thread a run of them
+  const int per = (n_cand + kRowThreads - 1) / kRowThreads;
+  const int j0 = tid * per, j1 = min(j0 + per, n_cand);
+  int nk = 0;
+  if (th.kk > 0)
+    for (int j = j0; j < j1; ++j) nk += cbuf[j] >= T ? 1 : 0;
+  int nout;
+  int slot = block_excl_scan<kRowThreads>(nk, sh.wsum, nout);
+  if (th.kk > 0) {
+    for (int j = j0; j < j1; ++j) {
+      const uint64_t K = cbuf[j];
+      if (K >= T) {
+        if (slot < a.k) {
+          if (sort) {
+            sh.sel_pos[slot] = comp_pos(K);
+            sh.sel_score[slot] = comp_score(K);
+          } else {
+            oi[slot] = comp_pos(K);
+            if (os) os[slot] = comp_score(K);
+          }
+        }
+        ++slot;
       }
     }
-    written += t;
   }
-  const int nsel = min(written, a.k);
-  if (sort) {
+  return min(nout, a.k);
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
+  extern __shared__ __align__(16) unsigned char row_smem[];
+  RowShared& sh = *reinterpret_cast<RowShared*>(row_smem);
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = row_valid(a.im, r);
+  const int64_t n_row = row_items(a.im, nv);
+  int32_t* oi = a.out_idx + (int64_t)r * a.k;
+  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
+  uint32_t* gh = a.hist + (int64_t)r * kHistBins;
+  const bool sort = a.im.mode == kItemsCand;
+  int nsel = 0;
+  if (n_row > 0) {                                             // uniform
+    uint32_t hv[kHistBins / kRowThreads];
+    hist_load<kRowThreads>(gh, hv);
+    float4 va[kRowU];                                          // the first round's scores fly
+    int32_t ba[kRowU];                                         // during the threshold search
+    row_load(a, r, a.scores + (int64_t)r * a.row_stride, 0, va, ba);
+    const RowThreshold th = hist_threshold<kRowThreads>(hv, a.k, sh.wsum, sh.pair);
+    if (th.n_cand <= kRowCap)
+      nsel = row_select(a, r, nv, n_row, th, va, ba, sh.cbuf, kRowCap, sh, oi, os, sort);
+    else
+      nsel = row_select(a, r, nv, n_row, th, va, ba, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
+                        a.n_chunks * kFiltChunk, sh, oi, os, sort);
+  }
+  if (sort) {                                                  // candidate lists come in any order
+    __syncthreads();
     int n2 = 1;
     while (n2 < nsel) n2 <<= 1;
-    for (int i = nsel + tid; i < n2; i += kSelThreads) { sh.sel_pos[i] = 0x7FFFFFFF; sh.sel_score[i] = 0.f; }
+    for (int i = nsel + tid; i < n2; i += kRowThreads) { sh.sel_pos[i] = 0x7FFFFFFF; sh.sel_score[i] = 0.f; }
     __syncthreads();
     for (int size = 2; size <= n2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < n2; i += kSelThreads) {
+        for (int i = tid; i < n2; i += kRowThreads) {
           const int j = i ^ stride;
           if (j > i) {
             const bool up = (i & size) == 0;
@@ -585,29 +941,40 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
         __syncthreads();
       }
     }
-    for (int j = tid; j < nsel; j += kSelThreads) {
+    for (int j = tid; j < nsel; j += kRowThreads) {
       oi[j] = sh.sel_pos[j];
       if (os) os[j] = sh.sel_score[j];
     }
   }
-  for (int j = nsel + tid; j < a.k; j += kSelThreads) {
+  for (int j = nsel + tid; j < a.k; j += kRowThreads) {
     oi[j] = -1;
     if (os) os[j] = 0.0f;
   }
+  // leave the row's histogram zeroed for the next call
+  if (n_row > 0)
+    for (int b = tid; b < kHistBins; b += kRowThreads) gh[b] = 0u;
+}
+
+hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream) {
+  if (a.n_rows == 0) return hipSuccess;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)sizeof(RowShared));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.n_rows), dim3(kRowThreads), sizeof(RowShared), stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream) {
+  if (a.n_rows == 0 || a.n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)a.n_chunks, (unsigned)a.n_rows),
+                     dim3(kFiltThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(SelShared));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.n_rows), dim3(kSelThreads),
-                     sizeof(SelShared), stream, a);
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.n_rows), dim3(kFiltThreads), 0, stream, a);
   return hipGetLastError();
 }
 

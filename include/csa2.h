@@ -172,7 +172,15 @@ typedef struct {
 
 /* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error).
  * Reads only the sizes and which of block_keys/cand are set; data pointers
- * may still be NULL. */
+ * may still be NULL.
+ *
+ * The indexer workspace must be ZERO-FILLED before its first use.  It holds
+ * per-row score histograms that each call builds up from zero and leaves at
+ * zero when its kernels complete, so later calls
+ * with the same n_rows and the same mode (flat, hierarchical or candidate)
+ * can reuse it without clearing it again, also from a captured HIP graph.
+ * Zero it again before a call with another n_rows or mode, and after a call
+ * that returned CSA2_EHIP or a device fault. */
 size_t csa2_indexer_topk_workspace(const csa2_indexer_args* args);
 
 int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
@@ -244,7 +252,6 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
 #define CSA2_SITE_ATTN 8           /* sparse + window attention                 */
 #define CSA2_SITE_ATTN_COMBINE 9   /* merge of the attention key splits         */
 #define CSA2_SITE_FILTER 10        /* top-k candidate filter (every stage)      */
-#define CSA2_SITE_FILL 11          /* indexer histogram clear                   */
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches);
 int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);

@@ -267,6 +267,66 @@ def test_indexer_candidates():
         check_topk(gi[r], O.topk_select(sc, ids, 128), ids, sc, 128, f"row {r}")
 
 
+def test_indexer_flat_long_rows():
+    """Rows longer than one workgroup streams (2^18 items) with few rows take
+    the multi-workgroup filter + select path."""
+    say("indexer flat N=300000 R=2 k=2048 (filter + select path)")
+    case = idx_case(12, 1, 300000, 2, row_seq=np.array([0, 0]), n_valid=np.array([300000, 262145]))
+    gi, gsc = run_indexer(case, 2048)
+    check_flat_rows(case, gi, gsc, 2048)
+
+
+def test_indexer_wide_tie_bins():
+    """Boundary bins far larger than the workgroup's staging buffer: every
+    key equal (one bin holds the whole row) and three distinct keys (three
+    bins of ~7000 entries); ties go to the lower entry id."""
+    say("indexer flat, boundary bin of 20000 / ~7000 equal scores")
+    g = np.random.default_rng(11)
+    S, N = 2, 20000
+    base = synth.to_e4m3(g.standard_normal((3, 128)).astype(np.float32))
+    keys = np.empty((S, N, 128), np.uint8)
+    keys[0] = base[0]
+    keys[1] = base[g.integers(0, 3, N)]
+    q = synth.to_e4m3(g.standard_normal((2, 32, 128)).astype(np.float32))
+    case = dict(keys=keys, q=q, w=None, row_seq=None, n_valid=None)
+    for k in (512, 2048):
+        gi, gsc = run_indexer(case, k)
+        check_flat_rows(case, gi, gsc, k)
+    assert np.array_equal(gi[0], np.arange(2048))
+
+
+def test_indexer_workspace_reuse():
+    """One zeroed workspace serves many calls of the same shape and mode:
+    the top-k kernel leaves its histograms and counters cleared, so a call
+    repeated after calls on other data gives the same, correct result."""
+    say("indexer workspace reuse: flat, hierarchical, candidates")
+    caseA = idx_case(21, 2, 9000, 3, row_seq=np.array([0, 1, 1]), n_valid=np.array([9000, 4097, 0]))
+    caseB = idx_case(22, 2, 9000, 3, row_seq=np.array([1, 0, 0]), n_valid=np.array([8000, 9000, 300]))
+    cand = np.stack([np.random.default_rng(r).permutation(9000)[:5000] for r in range(3)]).astype(np.int32)
+    bk = {id(c): np.stack([O.block_summary(c["keys"][s]) for s in range(2)]) for c in (caseA, caseB)}
+    modes = {
+        "flat": lambda c: {},
+        "hier": lambda c: dict(block_keys=dev(bk[id(c)]), keep_blocks=200),
+        "cand": lambda c: dict(cand=dev(cand)),
+    }
+    for name, extra in modes.items():
+        ws = torch.zeros(C.indexer_topk_workspace(dev(caseA["q"]), dev(caseA["keys"]), 256, **{
+            k: v for k, v in extra(caseA).items() if k in ("block_keys", "keep_blocks", "cand")}),
+            dtype=torch.uint8, device="cuda")
+        first = run_indexer(caseA, 256, workspace=ws, **extra(caseA))
+        for _ in range(2):
+            other = run_indexer(caseB, 256, workspace=ws, **extra(caseB))
+        again = run_indexer(caseA, 256, workspace=ws, **extra(caseA))
+        fresh = run_indexer(caseA, 256, **extra(caseA))
+        fresh_b = run_indexer(caseB, 256, **extra(caseB))
+        for got, ref in ((again, first), (first, fresh), (other, fresh_b)):
+            assert np.array_equal(got[0], ref[0]), name
+            assert np.array_equal(got[1][got[0] >= 0], ref[1][ref[0] >= 0]), name
+        if name == "flat":
+            check_flat_rows(caseA, *first, 256)
+            check_flat_rows(caseB, *other, 256)
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
