@@ -2,19 +2,19 @@
 // [daiw "four factors" table: one 512-dim latent shared by all query heads;
 //  0539edu §3: top_k 512, 128-token FP8 window].
 //
-// Keys = values = the latent.  A workgroup owns (row, 64 heads, a range of
-// keys).  Per chunk of 32 keys it gathers the selected FP4 entries (288 B
-// each) and the FP8 window tokens, dequantises them exactly to bf16 into LDS
-// in two layouts -- key-major bf16 for QK^T and channel-major fp16 for PV
-// (every dequantised value is exact in both) -- and runs
+// Keys = values = the latent.  A workgroup of 512 threads owns (row, up to
+// 64 heads, a range of keys).  Per chunk of 32 keys it gathers the selected
+// FP4 entries (288 B each) and the FP8 window tokens, dequantises them
+// exactly into LDS in two layouts -- key-major bf16 for QK^T and
+// channel-major fp16 for PV (every dequantised value is exact in both) --
+// and runs
 //   S^T[t][h] = sum_c K[t][c] Q[h][c]           (v_mfma_f32_16x16x32_bf16)
 //   O^T[c][h] += sum_t K[t][c] P[h][t]          (v_mfma_f32_16x16x32_f16)
-// P is rounded to fp16 (11 significant bits) for the PV product.
-// with an online softmax in float32.  Computing the transposed products puts
-// one head per lane (lane % 16) in both the score tile and the output tile,
-// so the softmax statistics never leave the lane group and P feeds the PV
-// MFMA straight from registers.  Rows with few keys per workgroup are split
-// over several workgroups whose (O, max, sum) partials are merged by
+// with an online softmax in float32; P is rounded to fp16 (11 significant
+// bits) for the PV product and the normaliser sums the rounded weights.  The
+// transposed products put one head per lane (lane % 16) in both the score
+// and the output tiles.  Rows with few keys per workgroup are split over
+// several workgroups whose (O, max, sum) partials are merged by
 // attn_combine_kernel.
 #include "csa2_dev.h"
 #include "csa2_launch.h"
@@ -34,10 +34,18 @@ __device__ __forceinline__ int kt_off(int c, int byte) {
 }
 
 constexpr int kMaxKeysPerSplit = 1024;          // selected ids staged in LDS per workgroup
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kHeadsPerWG = 64;                 // up to 4 head groups of 16 per workgroup
+constexpr int kMaxPvTiles = (kD / 16) * (kHeadsPerWG / 16) / kAttnWaves;   // 16 channel tiles
+constexpr int kPsStride = kKeyChunk * 2 + 16;   // bytes per head row of P (fp16 + pad)
 
 struct AttnShared {
   uint8_t kr[kKeyChunk * kKrStride];
   uint8_t kt[kD * kKtStride];
+  uint8_t ps[kHeadsPerWG * kPsStride];
+  float alpha[kHeadsPerWG];     // rescale factor of the current chunk per head
+  float lsum[kHeadsPerWG];      // final softmax sum per head
   int32_t kvalid[kKeyChunk];
   int32_t sidx[kMaxKeysPerSplit];
 };
@@ -83,26 +91,38 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// The raw bytes one thread gathers for its 8 keys x 8 channels of a chunk.
+// The raw bytes one thread gathers for its 4 keys x 8 channels of a chunk.
 struct Gather {
-  uint32_t code[8];   // FP4: 8 channels (one word)
-  uint32_t scale[8];  // FP4: the group's E4M3 scale byte
-  uint2 swa[8];       // window token: 8 E4M3 bytes
-  int kind[8];        // 0 none, 1 selected entry, 2 window token
+  uint32_t code[4];   // FP4: 8 channels (one word)
+  uint32_t scale[4];  // FP4: the group's E4M3 scale byte
+  uint2 swa[4];       // window token: 8 E4M3 bytes
+  int kind[4];        // 0 none, 1 selected entry, 2 window token
 };
 
-// One wave per SIMD: the 128 output accumulators live in AGPRs next to the
-// 64 query registers, so nothing spills.  Always 4 waves: every wave gathers
-// and dequantises; waves past the row's head count skip the MFMA work.
-__global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
-  __shared__ AttnShared sh;
-  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+// Per chunk, waves hg < HG (one per 16-head group) compute that group's
+// scores for all 32 keys, so the online softmax stays inside the wave: each
+// keeps the running max and sum of its heads in registers and hands the
+// fp16 weights P and the rescale factor of its heads to the other waves
+// through LDS.  All 8 waves then share the PV product: wave w owns one head
+// group and a block of channel tiles, so every lane rescales its
+// accumulators by a single factor.
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char attn_smem[];
+  AttnShared& sh = *reinterpret_cast<AttnShared*>(attn_smem);
+  const int split = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.n_heads;
-  const bool computes = hg * 64 + wave * 16 < H;
-  const int h = computes ? hg * 64 + wave * 16 + n : 0;
+  const int hbase = blockIdx.z * kHeadsPerWG;
+  const int HG = min(kHeadsPerWG, H - hbase) / 16;          // head groups here: 1, 2 or 4
+  const bool qk_wave = wave < HG;
+  // PV: waves per head group, head group and first channel tile of this wave
+  const int wph = kAttnWaves / HG;
+  const int pv_hg = wave / wph;
+  const int pv_tiles = (kD / 16) / wph;
+  const int pv_ct0 = (wave % wph) * pv_tiles;
+
   const int64_t seq = a.row_seq ? a.row_seq[r] : r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;
@@ -118,33 +138,37 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   const uint8_t* codes_s = a.codes + (seq_ok ? seq : 0) * a.n_ent * (kD / 2);
   const uint8_t* scales_s = a.scales + (seq_ok ? seq : 0) * a.n_ent * (kD / kGroup);
   const uint8_t* swa_s = a.swa ? a.swa + (seq_ok ? seq : 0) * (int64_t)a.swa_cap * kD : nullptr;
-  const uint16_t* qrow = a.q + ((int64_t)r * H + h) * kD + 8 * g;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q + (int64_t)r * H * kD);   // readable, discarded
 
   // stage this split's selected ids
   const int nsel_here = max(0, min(k1, nsel) - k0);
-  for (int i = tid; i < nsel_here; i += 256) sh.sidx[i] = idxr[k0 + i];
+  for (int i = tid; i < nsel_here; i += kAttnThreads) sh.sidx[i] = idxr[k0 + i];
 
-  // Q as the B operand of S^T = K Q^T: head n, channels ks*32 + 8g .. +8.
+  // QK waves: Q as the B operand of S^T = K Q^T, head n of the group,
+  // channels ks*32 + 8g .. +8
   v8bf qreg[kD / 32];
+  {
+    const int hq = hbase + (qk_wave ? wave : 0) * 16 + n;
+    const uint16_t* qrow = a.q + ((int64_t)r * H + hq) * kD + 8 * g;
 #pragma unroll
-  for (int ks = 0; ks < kD / 32; ++ks)
-    qreg[ks] = computes ? *reinterpret_cast<const v8bf*>(qrow + ks * 32) : v8bf{};
+    for (int ks = 0; ks < kD / 32; ++ks)
+      qreg[ks] = qk_wave ? *reinterpret_cast<const v8bf*>(qrow + ks * 32) : v8bf{};
+  }
+  float m_run = -INFINITY, l_run = 0.0f;                     // QK waves: head n of group `wave`
 
-  v4f acc[kD / 16];
+  v4f acc[kMaxPvTiles];
 #pragma unroll
-  for (int ct = 0; ct < kD / 16; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int t = 0; t < kMaxPvTiles; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // this thread's unit of every chunk: keys t0..t0+7, channels c0..c0+7
-  const int cb = tid & 63, kg = tid >> 6;
-  const int c0 = cb * 8, t0 = kg * 8;
+  // this thread's unit of every chunk: keys t0..t0+3, channels c0..c0+7
+  const int cb = tid & 63, kq = tid >> 6;
+  const int c0 = cb * 8, t0 = kq * 4;
   lds_barrier();                                     // sidx ready (q loads stay in flight)
 
   // issue every load of a chunk at once (no data-dependent branches)
   auto issue = [&](int kc, Gather& G) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int key = kc + t0 + j;
       const bool in_range = key < k1;
       const bool is_sel = in_range && key < nsel;
@@ -169,9 +193,9 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     lds_barrier();     // the previous chunk's LDS reads are done
     // ---- dequantise the gathered bytes into LDS (bf16 key-major, fp16 channel-major)
     {
-      uint32_t rows[8][4];     // fp16 pairs of the 8 keys, transposed below
+      uint32_t rows[4][4];     // fp16 pairs of the 4 keys, transposed below
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         float f[8];
         if (G.kind[j] == 1) {
           fp4x8_to_f32(G.code[j], e4m3_to_f32(G.scale[j]), f);
@@ -187,128 +211,159 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         for (int q = 0; q < 4; ++q) rows[j][q] = pack_f16_exact(f[2 * q], f[2 * q + 1]);
         if (cb == 0) sh.kvalid[t0 + j] = G.kind[j] != 0;
       }
-      // transpose the 8x8 fp16 block: channel c0+cc gets keys t0..t0+7
+      // transpose the 4x8 fp16 block: channel c0+cc gets keys t0..t0+3
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
         const int d = cc >> 1;
         const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t t[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = __builtin_amdgcn_perm(rows[2 * q + 1][d], rows[2 * q][d], sel);
-        *reinterpret_cast<uint4*>(sh.kt + kt_off(c0 + cc, t0 * 2)) = make_uint4(t[0], t[1], t[2], t[3]);
+        const uint32_t w0 = __builtin_amdgcn_perm(rows[1][d], rows[0][d], sel);
+        const uint32_t w1 = __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel);
+        *reinterpret_cast<uint2*>(sh.kt + kt_off(c0 + cc, t0 * 2)) = make_uint2(w0, w1);
       }
     }
     lds_barrier();
     // the gather registers are free again: the next chunk's loads fly during
     // this chunk's MFMAs and are consumed by the next dequantisation
     if (kc + kKeyChunk < k1) issue(kc + kKeyChunk, G);
-    if (!computes) continue;
 
-    // ---- S^T = K Q^T for the wave's 16 heads: lane holds head n, keys 4g+i and 16+4g+i
-    float s[8];
+    // ---- QK waves: S^T = K Q^T for the group's 16 heads; lane holds head n,
+    // keys 4g+i (tile 0) and 16+4g+i (tile 1)
+    if (qk_wave) {
+      float s[8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f st = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = sh.kr + (mt * 16 + n) * kKrStride + 16 * g;
+      for (int mt = 0; mt < 2; ++mt) {
+        v4f st = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t* krow = sh.kr + (mt * 16 + n) * kKrStride + 16 * g;
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const v8bf ka = *reinterpret_cast<const v8bf*>(krow + ks * 64);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ks], st, 0, 0, 0);
+        for (int ks = 0; ks < kD / 32; ++ks) {
+          const v8bf ka = *reinterpret_cast<const v8bf*>(krow + ks * 64);
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ks], st, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[mt * 4 + i] = st[i];
       }
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[mt * 4 + i] = st[i];
-    }
-    float mx = -INFINITY;
+      for (int j = 0; j < 8; ++j) {
+        const int t = (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4);
+        s[j] = sh.kvalid[t] ? s[j] * a.sm_scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+      uint32_t pw[4];
+      float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4);
-      s[j] = sh.kvalid[t] ? s[j] * a.sm_scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[j]);
+      for (int j = 0; j < 8; j += 2) {
+        const float p0 = (s[j] == -INFINITY) ? 0.0f : exp2f(s[j] - m_new);
+        const float p1 = (s[j + 1] == -INFINITY) ? 0.0f : exp2f(s[j + 1] - m_new);
+        pw[j >> 1] = pack_f16_rne(p0, p1);
+        // the normaliser sums the weights exactly as the PV product sees them
+        psum += (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] & 0xFFFFu)) +
+                (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] >> 16));
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      uint8_t* prow = sh.ps + (wave * 16 + n) * kPsStride;
+      *reinterpret_cast<uint2*>(prow + 8 * g) = make_uint2(pw[0], pw[1]);        // keys 4g..4g+3
+      *reinterpret_cast<uint2*>(prow + 32 + 8 * g) = make_uint2(pw[2], pw[3]);   // keys 16+4g..
+      if (g == 0) sh.alpha[wave * 16 + n] = alpha;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-    uint32_t pw[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const float p0 = (s[j] == -INFINITY) ? 0.0f : exp2f(s[j] - m_new);
-      const float p1 = (s[j + 1] == -INFINITY) ? 0.0f : exp2f(s[j + 1] - m_new);
-      pw[j >> 1] = pack_f16_rne(p0, p1);
-      // the normaliser sums the weights exactly as the PV product sees them
-      psum += (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] & 0xFFFFu)) +
-              (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] >> 16));
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    v8h pb;
-    {
-      uint32_t* pbw = reinterpret_cast<uint32_t*>(&pb);
-      pbw[0] = pw[0]; pbw[1] = pw[1]; pbw[2] = pw[2]; pbw[3] = pw[3];
-    }
+    lds_barrier();
 
-    // ---- O^T[c][h] += K^T P^T (fp16): A rows = channels, k-slot j <-> key 4g+j / 16+4g+j-4
+    // ---- all waves: O^T[c][h] += K^T P^T (fp16) over the wave's channel
+    // tiles; k-slot j of lane group g is key 8g+j in both operands
+    {
+      const float alpha = sh.alpha[pv_hg * 16 + n];
+      const v8h pb = *reinterpret_cast<const v8h*>(sh.ps + (pv_hg * 16 + n) * kPsStride + 16 * g);
 #pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const int c = ct * 16 + n;
-      const uint2 lo = *reinterpret_cast<const uint2*>(sh.kt + kt_off(c, 8 * g));
-      const uint2 hi = *reinterpret_cast<const uint2*>(sh.kt + kt_off(c, 32 + 8 * g));
-      v8h ka;
-      uint32_t* kaw = reinterpret_cast<uint32_t*>(&ka);
-      kaw[0] = lo.x; kaw[1] = lo.y; kaw[2] = hi.x; kaw[3] = hi.y;
-      v4f o = acc[ct];
-      o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pb, o, 0, 0, 0);
+      for (int t = 0; t < kMaxPvTiles; ++t) {
+        if (t < pv_tiles) {
+          const int c = (pv_ct0 + t) * 16 + n;
+          const v8h ka = *reinterpret_cast<const v8h*>(sh.kt + kt_off(c, 16 * g));
+          v4f o = acc[t];
+          o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pb, o, 0, 0, 0);
+        }
+      }
     }
   }
 
-  if (!computes) return;
-  // ---- finish: the full sum for head n lives across the 4 lane groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const int64_t rh = (int64_t)r * H + h;
-  if (a.n_split == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* orow = a.out + rh * kD + 4 * g;
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const v4f o = acc[ct];
-      *reinterpret_cast<float4*>(orow + ct * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-    }
-    if (a.lse && g == 0)
-      a.lse[rh] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-  } else {
-    const int64_t base = ((int64_t)split * a.n_rows * H + rh);
-    float* orow = a.part_o + base * kD + 4 * g;
-#pragma unroll
-    for (int ct = 0; ct < kD / 16; ++ct) {
-      const v4f o = acc[ct];
-      *reinterpret_cast<float4*>(orow + ct * 16) = make_float4(o[0], o[1], o[2], o[3]);
-    }
-    if (g == 0) {
+  // ---- finish: QK waves hand the sums of their heads to the PV waves
+  if (qk_wave && g == 0) {
+    sh.lsum[wave * 16 + n] = l_run;
+    const int64_t rh = (int64_t)r * H + hbase + wave * 16 + n;
+    if (a.n_split == 1) {
+      if (a.lse) a.lse[rh] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      const int64_t base = (int64_t)split * a.n_rows * H + rh;
       a.part_ml[base * 2] = m_run;
       a.part_ml[base * 2 + 1] = l_run;
+    }
+  }
+  lds_barrier();
+  const int64_t rh = (int64_t)r * H + hbase + pv_hg * 16 + n;
+  if (a.n_split == 1) {
+    const float l = sh.lsum[pv_hg * 16 + n];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* orow = a.out + rh * kD + 4 * g;
+#pragma unroll
+    for (int t = 0; t < kMaxPvTiles; ++t) {
+      if (t < pv_tiles) {
+        const v4f o = acc[t];
+        *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      }
+    }
+  } else {
+    const int64_t base = (int64_t)split * a.n_rows * H + rh;
+    float* orow = a.part_o + base * kD + 4 * g;
+#pragma unroll
+    for (int t = 0; t < kMaxPvTiles; ++t) {
+      if (t < pv_tiles) {
+        const v4f o = acc[t];
+        *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
 
 // Merge the key-split partials of one (row, head): 128 threads x 4 channels.
+// The partials are read in batches of 8 splits with unconditional (clamped)
+// loads, so each batch costs one memory latency.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int64_t rh = blockIdx.x;
   const int64_t RH = (int64_t)a.n_rows * a.n_heads;
+  const int ns = a.n_split;
   float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.part_ml[(s * RH + rh) * 2]);
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(s * RH + rh) * 2]);
+  constexpr int kB = 8;
   float L = 0.0f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < a.n_split; ++s) {
-    const float ms = a.part_ml[(s * RH + rh) * 2];
-    const float ls = a.part_ml[(s * RH + rh) * 2 + 1];
-    if (ms == -INFINITY || ls == 0.0f) continue;
-    const float f = exp2f(ms - M);
-    L += ls * f;
-    const float4 p = *reinterpret_cast<const float4*>(a.part_o + (s * RH + rh) * kD + 4 * threadIdx.x);
-    o.x += p.x * f; o.y += p.y * f; o.z += p.z * f; o.w += p.w * f;
+  for (int s0 = 0; s0 < ns; s0 += kB) {
+    float4 p[kB];
+    float ms[kB], ls[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int64_t sj = min(s0 + j, ns - 1);
+      p[j] = *reinterpret_cast<const float4*>(a.part_o + (sj * RH + rh) * kD + 4 * threadIdx.x);
+      ms[j] = a.part_ml[(sj * RH + rh) * 2];
+      ls[j] = a.part_ml[(sj * RH + rh) * 2 + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      // splits past the end, and splits that saw no key, weigh nothing
+      const bool use = s0 + j < ns && ms[j] != -INFINITY && ls[j] != 0.0f;
+      const float f = use ? exp2f(ms[j] - M) : 0.0f;
+      L += use ? ls[j] * f : 0.0f;
+      o.x += use ? p[j].x * f : 0.0f;
+      o.y += use ? p[j].y * f : 0.0f;
+      o.z += use ? p[j].z * f : 0.0f;
+      o.w += use ? p[j].w * f : 0.0f;
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   *reinterpret_cast<float4*>(a.out + rh * kD + 4 * threadIdx.x) =
@@ -319,9 +374,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  const int hgroups = (a.n_heads + 63) / 64;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hgroups),
-                     dim3(256), 0, stream, a);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_attn_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)sizeof(AttnShared));
+  if (attr != hipSuccess) return attr;
+  const int hblocks = (a.n_heads + kHeadsPerWG - 1) / kHeadsPerWG;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hblocks),
+                     dim3(kAttnThreads), sizeof(AttnShared), stream, a);
   return hipGetLastError();
 }
 
