@@ -94,7 +94,7 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
 // The raw bytes one thread gathers for its 4 keys x 8 channels of a chunk.
 struct Gather {
   uint32_t code[4];   // FP4: 8 channels (one word)
-  uint32_t scale[4];  // FP4: the group's E4M3 scale byte
+  uint32_t scale[4];  // FP4: the aligned word holding the group's E4M3 scale byte
   uint2 swa[4];       // window token: 8 E4M3 bytes
   int kind[4];        // 0 none, 1 selected entry, 2 window token
 };
@@ -140,9 +140,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   const uint8_t* swa_s = a.swa ? a.swa + (seq_ok ? seq : 0) * (int64_t)a.swa_cap * kD : nullptr;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q + (int64_t)r * H * kD);   // readable, discarded
 
-  // stage this split's selected ids
-  const int nsel_here = max(0, min(k1, nsel) - k0);
-  for (int i = tid; i < nsel_here; i += kAttnThreads) sh.sidx[i] = idxr[k0 + i];
+  // stage the selected ids this split may use; the count depends on top_k
+  // only, so these loads start at once, beside the row parameters
+  const int nst = max(0, min(k0 + a.keys_per_split, a.top_k) - k0);
+  for (int i = tid; i < nst; i += kAttnThreads) sh.sidx[i] = idxr[k0 + i];
 
   // QK waves: Q as the B operand of S^T = K Q^T, head n of the group,
   // channels ks*32 + 8g .. +8
@@ -163,7 +164,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   // this thread's unit of every chunk: keys t0..t0+3, channels c0..c0+7
   const int cb = tid & 63, kq = tid >> 6;
   const int c0 = cb * 8, t0 = kq * 4;
-  lds_barrier();                                     // sidx ready (q loads stay in flight)
+  // sidx ready.  Also retire the Q loads here (issued with the id loads):
+  // left pending into the loop, every wait for them would drain the next
+  // chunk's prefetched gathers as well.
+  lds_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
 
   // issue every load of a chunk at once (no data-dependent branches)
   auto issue = [&](int kc, Gather& G) {
@@ -178,10 +183,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       int slot = swst + (key - nsel);
       if (slot >= a.swa_cap) slot -= a.swa_cap;
       const uint8_t* ca = ok ? codes_s + (int64_t)p * (kD / 2) + c0 / 2 : dummy;
-      const uint8_t* sa = ok ? scales_s + (int64_t)p * (kD / kGroup) + c0 / kGroup : dummy;
+      const uint8_t* sa = ok ? scales_s + (int64_t)p * (kD / kGroup) + ((c0 / kGroup) & ~3) : dummy;
       const uint8_t* wa = is_swa ? swa_s + (int64_t)slot * kD + c0 : dummy;
       G.code[j] = *reinterpret_cast<const uint32_t*>(ca);
-      G.scale[j] = *sa;
+      G.scale[j] = *reinterpret_cast<const uint32_t*>(sa);   // byte extracted when used
       G.swa[j] = *reinterpret_cast<const uint2*>(wa);
       G.kind[j] = ok ? 1 : (is_swa ? 2 : 0);
     }
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       for (int j = 0; j < 4; ++j) {
         float f[8];
         if (G.kind[j] == 1) {
-          fp4x8_to_f32(G.code[j], e4m3_to_f32(G.scale[j]), f);
+          fp4x8_to_f32(G.code[j], e4m3_to_f32((G.scale[j] >> (8 * ((c0 / kGroup) & 3))) & 0xFFu), f);
         } else if (G.kind[j] == 2) {
           fp8x8_to_f32(G.swa[j].x, G.swa[j].y, f);
         } else {

@@ -323,11 +323,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 
 constexpr int kStageCap = 4096;     // boundary-bin candidates staged in LDS
 
-constexpr int kRegKeys = 32;       // candidates per thread held in registers by the select
+constexpr int kSelThreads = 1024;  // select workgroup
+constexpr int kRegKeys = 8;        // candidates per thread held in registers by the select
 constexpr int kMaxChunks = kMaxItems / kFiltChunk;
 
 struct TopkShared {
-  int wsum[kFiltThreads / 64];
+  int wsum[kSelThreads / 64];
   int pair[3], n_stage;
   int digit, above, dcount;
   uint32_t hist[256];
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
 // the candidates of bin b*.  The kept candidates (keys >= T) are written in
 // candidate order, which is ascending position (candidate mode sorts).  The
 // row's histogram is then cleared for the next call.
-__global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) {
   __shared__ TopkShared sh;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = row_valid(a.im, r);
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
   int32_t* oi = a.out_idx + (int64_t)r * a.k;
   float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
   if (n_row == 0) {                                            // uniform: nothing visible
-    for (int j = tid; j < a.k; j += kFiltThreads) {
+    for (int j = tid; j < a.k; j += kSelThreads) {
       oi[j] = -1;
       if (os) os[j] = 0.0f;
     }
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
   }
   const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  const RowThreshold th = row_threshold<kFiltThreads>(gh, a.k, sh.wsum, sh.pair);
+  const RowThreshold th = row_threshold<kSelThreads>(gh, a.k, sh.wsum, sh.pair);
   const int bstar = th.bstar, c_above = th.c_above;
   const uint32_t kk = th.kk;
   const int64_t crow0 = (int64_t)r * a.n_chunks * kFiltChunk;
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
   // flattened candidate offsets: chunk ch holds [coff[ch], coff[ch + 1])
   int n_cand;
   {
-    constexpr int kCpt = kMaxChunks / kFiltThreads;
+    constexpr int kCpt = kMaxChunks / kSelThreads;
     int cc[kCpt], loc = 0;
 #pragma unroll
     for (int i = 0; i < kCpt; ++i) {
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
       cc[i] = ch < nch ? (int)cnt[ch] : 0;
       loc += cc[i];
     }
-    int base = block_excl_scan<kFiltThreads>(loc, sh.wsum, n_cand);
+    int base = block_excl_scan<kSelThreads>(loc, sh.wsum, n_cand);
 #pragma unroll
     for (int i = 0; i < kCpt; ++i) {
       const int ch = kCpt * tid + i;
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
   const bool sort = a.im.mode == kItemsCand;
   uint64_t T = 0;
   int nsel;
-  if (n_cand <= kFiltThreads * kRegKeys) {                   // uniform
+  if (n_cand <= kSelThreads * kRegKeys) {                   // uniform
     // each thread holds a run of kRegKeys consecutive candidates
     const int j0 = tid * kRegKeys;
     const int nm = max(0, min(kRegKeys, n_cand - j0));
@@ -553,7 +554,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
       for (int step = 0; step < 7; ++step) {
         const int dshift = digit_shift(step), w = digit_width(step);
         const uint32_t dmask = (1u << w) - 1u;
-        sh.hist[tid] = 0u;
+        if (tid < 256) sh.hist[tid] = 0u;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kRegKeys; ++i)
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
 #pragma unroll
     for (int i = 0; i < kRegKeys; ++i) nk += (i < nm && kk > 0 && K[i] >= T) ? 1 : 0;
     int nout;
-    int slot = block_excl_scan<kFiltThreads>(nk, sh.wsum, nout);
+    int slot = block_excl_scan<kSelThreads>(nk, sh.wsum, nout);
 #pragma unroll
     for (int i = 0; i < kRegKeys; ++i) {
       if (i < nm && kk > 0 && K[i] >= T) {
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
       __syncthreads();
       for (int ch = 0; ch < nch; ++ch) {
         const int cn = (int)cnt[ch];
-        for (int j = tid; j < cn; j += kFiltThreads) {
+        for (int j = tid; j < cn; j += kSelThreads) {
           const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
           if ((int)(K >> 52) == bstar) {
             const int slot = atomicAdd(&sh.n_stage, 1);
@@ -617,17 +618,17 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
       for (int step = 0; step < 7; ++step) {
         const int dshift = digit_shift(step), w = digit_width(step);
         const uint32_t dmask = (1u << w) - 1u;
-        sh.hist[tid] = 0u;
+        if (tid < 256) sh.hist[tid] = 0u;
         __syncthreads();
         if (staged) {
-          for (int j = tid; j < n_st; j += kFiltThreads) {
+          for (int j = tid; j < n_st; j += kSelThreads) {
             const uint64_t K = sh.u.stage[j];
             if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
           }
         } else {
           for (int ch = 0; ch < nch; ++ch) {
             const int cn = (int)cnt[ch];
-            for (int j = tid; j < cn; j += kFiltThreads) {
+            for (int j = tid; j < cn; j += kSelThreads) {
               const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
               if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
             }
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
       }
     }
     int nout = 0;
-    for (int base = 0; base < n_cand; base += kFiltThreads) {
+    for (int base = 0; base < n_cand; base += kSelThreads) {
       const int j = base + tid;
       uint64_t K = 0;
       bool keep = false;
@@ -661,7 +662,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
         keep = K >= T;
       }
       int t;
-      const int slot = nout + block_excl_scan<kFiltThreads>(keep ? 1 : 0, sh.wsum, t);
+      const int slot = nout + block_excl_scan<kSelThreads>(keep ? 1 : 0, sh.wsum, t);
       if (keep && slot < a.k) {
         if (sort) {
           sh.u.sel.pos[slot] = comp_pos(K);
@@ -680,11 +681,11 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
   if (sort) {
     int n2 = 1;
     while (n2 < nsel) n2 <<= 1;
-    for (int i = nsel + tid; i < n2; i += kFiltThreads) { sh.u.sel.pos[i] = 0x7FFFFFFF; sh.u.sel.score[i] = 0.f; }
+    for (int i = nsel + tid; i < n2; i += kSelThreads) { sh.u.sel.pos[i] = 0x7FFFFFFF; sh.u.sel.score[i] = 0.f; }
     __syncthreads();
     for (int size = 2; size <= n2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < n2; i += kFiltThreads) {
+        for (int i = tid; i < n2; i += kSelThreads) {
           const int j = i ^ stride;
           if (j > i) {
             const bool up = (i & size) == 0;
@@ -698,18 +699,18 @@ __global__ __launch_bounds__(kFiltThreads) void topk_select_kernel(SelectArgs a)
         __syncthreads();
       }
     }
-    for (int j = tid; j < nsel; j += kFiltThreads) {
+    for (int j = tid; j < nsel; j += kSelThreads) {
       oi[j] = sh.u.sel.pos[j];
       if (os) os[j] = sh.u.sel.score[j];
     }
   }
-  for (int j = nsel + tid; j < a.k; j += kFiltThreads) {
+  for (int j = nsel + tid; j < a.k; j += kSelThreads) {
     oi[j] = -1;
     if (os) os[j] = 0.0f;
   }
 
   // leave the row's histogram zeroed for the next call
-  for (int b = tid; b < kHistBins; b += kFiltThreads) gh[b] = 0u;
+  for (int b = tid; b < kHistBins; b += kSelThreads) gh[b] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -974,7 +975,7 @@ hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.n_rows), dim3(kFiltThreads), 0, stream, a);
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)a.n_rows), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
