@@ -10,8 +10,9 @@
 // and runs
 //   S^T[t][h] = sum_c K[t][c] Q[h][c]           (v_mfma_f32_16x16x32_bf16)
 //   O^T[c][h] += sum_t K[t][c] P[h][t]          (v_mfma_f32_16x16x32_f16)
-// with an online softmax in float32; P is rounded to fp16 (11 significant
-// bits) for the PV product and the normaliser sums the rounded weights.  The
+// with an online softmax in float32; P enters the PV product as the sum of
+// two fp16 terms (about 22 significant bits, two MFMAs on the same K
+// operand) and the normaliser sums the weights as that product sees them.  The
 // transposed products put one head per lane (lane % 16) in both the score
 // and the output tiles.  Rows with few keys per workgroup are split over
 // several workgroups whose (O, max, sum) partials are merged by
@@ -38,7 +39,8 @@ constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kHeadsPerWG = 64;                 // up to 4 head groups of 16 per workgroup
 constexpr int kMaxPvTiles = (kD / 16) * (kHeadsPerWG / 16) / kAttnWaves;   // 16 channel tiles
-constexpr int kPsStride = kKeyChunk * 2 + 16;   // bytes per head row of P (fp16 + pad)
+constexpr int kPsLo = kKeyChunk * 2;            // offset of P's low fp16 terms in a head row
+constexpr int kPsStride = kKeyChunk * 4 + 16;   // bytes per head row of P (hi + lo fp16 + pad)
 
 struct AttnShared {
   uint8_t kr[kKeyChunk * kKrStride];
@@ -258,24 +260,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-      uint32_t pw[4];
+      // P as the sum of two fp16 terms, hi = fp16(p) and lo = fp16(p - hi),
+      // which carries about 22 significant bits into the PV product
+      uint32_t ph[4], pl[4];
       float psum = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const float p0 = (s[j] == -INFINITY) ? 0.0f : exp2f(s[j] - m_new);
         const float p1 = (s[j + 1] == -INFINITY) ? 0.0f : exp2f(s[j + 1] - m_new);
-        pw[j >> 1] = pack_f16_rne(p0, p1);
+        const uint32_t h = pack_f16_rne(p0, p1);
+        const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+        const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
+        const uint32_t l = pack_f16_rne(p0 - h0, p1 - h1);
+        const float l0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(l & 0xFFFFu));
+        const float l1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(l >> 16));
+        ph[j >> 1] = h;
+        pl[j >> 1] = l;
         // the normaliser sums the weights exactly as the PV product sees them
-        psum += (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] & 0xFFFFu)) +
-                (float)__builtin_bit_cast(_Float16, (uint16_t)(pw[j >> 1] >> 16));
+        psum += (h0 + l0) + (h1 + l1);
       }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       uint8_t* prow = sh.ps + (wave * 16 + n) * kPsStride;
-      *reinterpret_cast<uint2*>(prow + 8 * g) = make_uint2(pw[0], pw[1]);        // keys 4g..4g+3
-      *reinterpret_cast<uint2*>(prow + 32 + 8 * g) = make_uint2(pw[2], pw[3]);   // keys 16+4g..
+      *reinterpret_cast<uint2*>(prow + 8 * g) = make_uint2(ph[0], ph[1]);                 // keys 4g..4g+3
+      *reinterpret_cast<uint2*>(prow + 32 + 8 * g) = make_uint2(ph[2], ph[3]);            // keys 16+4g..
+      *reinterpret_cast<uint2*>(prow + kPsLo + 8 * g) = make_uint2(pl[0], pl[1]);
+      *reinterpret_cast<uint2*>(prow + kPsLo + 32 + 8 * g) = make_uint2(pl[2], pl[3]);
       if (g == 0) sh.alpha[wave * 16 + n] = alpha;
     }
     lds_barrier();
@@ -284,7 +296,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
     // tiles; k-slot j of lane group g is key 8g+j in both operands
     {
       const float alpha = sh.alpha[pv_hg * 16 + n];
-      const v8h pb = *reinterpret_cast<const v8h*>(sh.ps + (pv_hg * 16 + n) * kPsStride + 16 * g);
+      const uint8_t* prow = sh.ps + (pv_hg * 16 + n) * kPsStride + 16 * g;
+      const v8h pb = *reinterpret_cast<const v8h*>(prow);
+      const v8h pbl = *reinterpret_cast<const v8h*>(prow + kPsLo);
 #pragma unroll
       for (int t = 0; t < kMaxPvTiles; ++t) {
         if (t < pv_tiles) {
@@ -292,6 +306,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
           const v8h ka = *reinterpret_cast<const v8h*>(sh.kt + kt_off(c, 16 * g));
           v4f o = acc[t];
           o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
+          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pbl, o, 0, 0, 0);
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pb, o, 0, 0, 0);
         }
       }

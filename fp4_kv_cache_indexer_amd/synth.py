@@ -27,6 +27,8 @@ def rng(seed, cfg, tensor, layer=0):
 
 
 def torch_gen(seed, cfg, tensor, layer=0, device="cuda"):
+    """Seeded torch generator; ``layer`` also serves as a per-sequence index
+    when a large tensor is drawn one sequence at a time."""
     g = torch.Generator(device=device)
     g.manual_seed(((seed * 1_000_003 + cfg) * 1_000_033 + tensor) * 1_000_037 + layer)
     return g
@@ -62,6 +64,25 @@ def latent_np(g, shape, dist="normal", outlier_channels=None, outlier_gain=8.0):
     if outlier_channels is not None:
         x[..., outlier_channels] *= outlier_gain
     return x
+
+
+def latent_dev(shape, gen, dist="normal", outlier_channels=None, outlier_gain=8.0, device="cuda"):
+    """Device-side token latents (float32) with the distributions of
+    ``latent_np``: N(0,1), or Student-t (nu=3) drawn as N / sqrt(chi2_3 / 3)."""
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if dist == "t3":
+        c = torch.randn(tuple(shape) + (3,), generator=gen, device=device, dtype=torch.float32)
+        x = x / torch.sqrt((c * c).sum(-1) / 3.0)
+    elif dist != "normal":
+        raise ValueError(dist)
+    if outlier_channels is not None:
+        x[..., torch.as_tensor(np.asarray(outlier_channels), device=device)] *= outlier_gain
+    return x
+
+
+def bf16_host_bits(t):
+    """bfloat16 device tensor -> numpy uint16 bit patterns."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def outlier_channels_np(seed, cfg, n=4, dim=512):

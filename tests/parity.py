@@ -13,8 +13,11 @@ import sys
 import numpy as np
 import torch
 
+from oracle import formats as F
+
 TOPK_REL = 1e-5
 ATOL, RTOL = 2e-3, 1e-2
+E2M1_THRESH = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)   # midpoints of the E2M1 magnitudes
 
 
 def say(*a):
@@ -71,3 +74,19 @@ def check_close(gpu, ref, what=""):
     worst = np.max(err / lim) if err.size else 0.0
     assert np.all(err <= lim), f"{what}: {np.sum(err > lim)} elements outside tolerance (worst {worst:.3g} of the bound)"
     return worst
+
+
+def near_boundary(yg, rel=4e-7):
+    """True if a float32 group of 16 pooled values sits within `rel` of a
+    decision boundary of the quantiser: amax/6 near an E4M3 rounding
+    midpoint, or a value near a midpoint t*s of the E2M1 grid.  Pooling with
+    gates runs in float32 on the GPU and in float64 in the oracle, so only
+    such groups may quantise differently."""
+    amax = np.float32(np.abs(yg).max())
+    q = float(amax / np.float32(6))
+    mids = (F.E4M3_VALUES[0:0x7E] + F.E4M3_VALUES[1:0x7F]) / 2
+    if np.any(np.abs(mids - q) <= rel * max(q, 1e-30)):
+        return True
+    s = float(F.e4m3_decode(F.e4m3_rne_sat(np.float64(q))))
+    a = np.abs(yg)
+    return bool(np.any(np.abs(a[:, None] - s * np.array(E2M1_THRESH)[None, :]) <= rel * a[:, None].clip(1e-30)))

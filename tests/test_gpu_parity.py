@@ -10,12 +10,9 @@ from fp4_kv_cache_indexer_amd import csa2 as C
 from fp4_kv_cache_indexer_amd import synth
 from oracle import csa2 as O
 from oracle import formats as F
-from parity import check_close, check_topk, dev, host, say
+from parity import check_close, check_topk, dev, host, near_boundary, say
 
 pytestmark = pytest.mark.gpu
-
-THRESH = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -29,20 +26,6 @@ def _gpu():
 # ---------------------------------------------------------------------------
 # cache write
 # ---------------------------------------------------------------------------
-
-
-def near_boundary(yg, rel=4e-7):
-    """True if a float32 group sits within `rel` of a decision boundary of the
-    quantiser: amax/6 near an E4M3 rounding midpoint, or a value near a
-    threshold t*s of the E2M1 grid."""
-    amax = np.float32(np.abs(yg).max())
-    q = float(amax / np.float32(6))
-    mids = (F.E4M3_VALUES[0:0x7E] + F.E4M3_VALUES[1:0x7F]) / 2
-    if np.any(np.abs(mids - q) <= rel * max(q, 1e-30)):
-        return True
-    s = float(F.e4m3_decode(F.e4m3_rne_sat(np.float64(q))))
-    a = np.abs(yg)
-    return bool(np.any(np.abs(a[:, None] - s * np.array(THRESH)[None, :]) <= rel * a[:, None].clip(1e-30)))
 
 
 def cache_case(seed, S, T, dist="normal", gate=False):
