@@ -10,7 +10,9 @@ resident in HBM before the timed region; several independent input sets are
 rotated so the working set exceeds the 256 MB Infinity Cache.
 
 The timed region replays one captured HIP graph per input set (the form a
-serving loop would run).  An equal eager pass afterwards times the dominant
+serving loop would run).  (Running the cache append on a second stream,
+joined before the attention, was measured slower inside the graph: about
+13 us per step more for 3-5 us of overlapped work.)  An equal eager pass afterwards times the dominant
 kernel (the coarse indexer scan) with HIP events recorded by the library on
 the kernel's own stream; that duration gives the roofline line.  The
 cpu_baseline leg times the oracle on a bounded sample of the same workload.
@@ -31,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fp4_kv_cache_indexer_amd import csa2 as C  # noqa: E402
+from fp4_kv_cache_indexer_amd import synth  # noqa: E402
 
 METRIC = "decode sparse-attn queries/sec at 1M ctx; indexer HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
@@ -49,19 +52,6 @@ WORKLOADS = {
 }
 
 
-def e4m3(t):
-    return t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
-
-
-def latent(shape, gen, dist):
-    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
-    if dist == "t3":
-        # Student-t(3) = N / sqrt(chi2_3 / 3)
-        c = torch.randn(shape + (3,), generator=gen, device="cuda", dtype=torch.float32)
-        x = x / torch.sqrt((c * c).sum(-1) / 3.0)
-    return x
-
-
 class InputSet:
     """One batch of caches and queries, all device-resident."""
 
@@ -72,7 +62,7 @@ class InputSet:
         self.codes = torch.empty((B, N, 256), dtype=torch.uint8, device="cuda")
         self.scales = torch.empty((B, N, 32), dtype=torch.uint8, device="cuda")
         for b in range(B):
-            x = latent((1, N * m, 512), g, w["dist"]).to(torch.bfloat16)
+            x = synth.latent_dev((1, N * m, 512), g, w["dist"]).to(torch.bfloat16)
             z = torch.randn((1, N * m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
             C.kv_compress_quantize(x, m, gate=z, codes=self.codes[b:b + 1], scales=self.scales[b:b + 1])
             if b == 0 and set_id == 0:
@@ -81,13 +71,13 @@ class InputSet:
             del x, z
         self.keys = torch.empty((B, N, 128), dtype=torch.uint8, device="cuda")
         for b in range(B):
-            self.keys[b] = e4m3(torch.randn((N, 128), generator=g, device="cuda"))
+            self.keys[b] = synth.to_e4m3(torch.randn((N, 128), generator=g, device="cuda"))
         self.summ = C.index_block_summary(self.keys) if w["hier"] else None
-        self.swa = e4m3(latent((B, 128, 512), g, w["dist"]))
+        self.swa = synth.to_e4m3(synth.latent_dev((B, 128, 512), g, w["dist"]))
         self.swa_len = torch.full((B,), 128, dtype=torch.int32, device="cuda")
-        self.q_idx = e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
+        self.q_idx = synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
         self.q = torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16)
-        self.x_new = latent((B, m, 512), g, w["dist"]).to(torch.bfloat16)
+        self.x_new = synth.latent_dev((B, m, 512), g, w["dist"]).to(torch.bfloat16)
         self.z_new = torch.randn((B, m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
         self.idx = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
@@ -117,6 +107,93 @@ def step(w, s):
                          lse=s.lse, workspace=s.ws_attn)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_coarse_c3_traffic.md")
+# the sources that define the scan kernel (its traffic is re-measured when they change)
+SCAN_SOURCES = [os.path.join(ROOT, "fp4_kv_cache_indexer_amd", "csrc", f)
+                for f in ("score.hip", "items.h", "csa2_dev.h", "csa2_launch.h")]
+
+
+def scan_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is none for this
+    workload or the kernel source has changed since the counters were taken."""
+    import re
+    if workload != "c3" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    mb = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    mh = re.search(r"^source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not mb or not mh:
+        return None
+    if scan_source_sha256() != mh.group(1):
+        return None
+    return float(mb.group(1))
+
+
+def prof_summary(d):
+    """Markdown tables from the rocprofv3 CSV output under directory d:
+    kernel durations (*_kernel_stats.csv) and mean counter values per
+    dispatch (*_counter_collection.csv), for this library's kernels and the
+    copy kernel of --copy-probe-mib."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def short(name):
+        return name if len(name) <= 90 else name[:87] + "..."
+
+    keep = ("csa2::", "neg_kernel")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"), recursive=True)):
+        durs = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            if any(k in r["Kernel_Name"] for k in keep):
+                durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"kernel durations ({os.path.relpath(f, d)}; the median is the steady-state step, "
+              f"the maximum includes building the caches)\n")
+        print("| kernel | launches | median us | mean us | min us | max us |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for k, v in sorted(durs.items(), key=lambda kv: -float(np.median(kv[1]))):
+            print(f"| {short(k)} | {len(v)} | {np.median(v):.2f} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        print()
+    for f in sorted(glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True)):
+        agg = defaultdict(lambda: defaultdict(list))
+        grid = {}
+        for r in csv.DictReader(open(f)):
+            if any(k in r["Kernel_Name"] for k in keep):
+                agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                grid[r["Kernel_Name"]] = r.get("Grid_Size", "")
+        print(f"counters, mean per dispatch ({os.path.relpath(f, d)})\n")
+        print("| kernel | grid | counter | dispatches | mean |")
+        print("|---|---:|---|---:|---:|")
+        for k, cs in agg.items():
+            for c, v in sorted(cs.items()):
+                print(f"| {short(k)} | {grid[k]} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+        print()
+    print(f"source_sha256 of the scan kernel's sources ({', '.join(os.path.basename(f) for f in SCAN_SOURCES)}): "
+          f"{scan_source_sha256()}")
+
+
+def copy_probe(mib):
+    """A plain copy-like kernel of known size for scaling the HBM counters:
+    out = -in over `mib` MiB of float32 (reads and writes mib MiB each)."""
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: 3 x neg over {mib} MiB float32", file=sys.stderr, flush=True)
+
+
 def scan_bytes(w):
     """Algorithmic HBM bytes of one launch of the dominant kernel (the
     indexer scan): the key rows it must read plus queries and weights."""
@@ -142,7 +219,7 @@ def cpu_baseline(w, s, seconds):
     n = 0
     el = 0.0
     while True:
-        q_idx = e4m3(torch.from_numpy(g.standard_normal((32, 128)).astype(np.float32)).cuda()).cpu().numpy()
+        q_idx = synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32))
         q = torch.from_numpy(g.standard_normal((H, 512)).astype(np.float32)).to(torch.bfloat16)
         q = q.view(torch.int16).numpy().view(np.uint16)
         ts = time.perf_counter()
@@ -184,7 +261,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a copy kernel of this size (for scaling rocprofv3 HBM counters)")
+    ap.add_argument("--prof-summary", metavar="DIR",
+                    help="print markdown summaries of the rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
+    if args.prof_summary:
+        prof_summary(args.prof_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the multi-GPU sharding is a design note only)", file=sys.stderr)
@@ -249,6 +333,10 @@ def main():
     print(f"[bench] {site}: {n_l} launches, avg {avg_s * 1e6:.2f} us, {achieved:.0f} GB/s algorithmic",
           file=sys.stderr, flush=True)
 
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+
+    traffic = measured_traffic(args.workload)
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -260,7 +348,7 @@ def main():
                    "keep_blocks": w["keep"], "swa_window": 128, "input_sets_rotated": len(sets),
                    "timed": "graph replays" if graphs else "eager launches"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"index_score_kernel ({site})", "avg_us": round(avg_s * 1e6, 3),
                      "bytes_per_launch": scan_bytes(w)},
         "cpu_baseline": None,

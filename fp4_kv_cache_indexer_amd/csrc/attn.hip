@@ -352,15 +352,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
 }
 
 // Merge the key-split partials of one (row, head): 128 threads x 4 channels.
-// The partials are read in batches of 8 splits with unconditional (clamped)
-// loads, so each batch costs one memory latency.
+// Up to 16 splits are read in one batch of unconditional (clamped) loads --
+// maxima, sums and outputs together -- so the merge costs one memory
+// latency; more splits take further batches against a first pass for the
+// overall maximum.
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int64_t rh = blockIdx.x;
   const int64_t RH = (int64_t)a.n_rows * a.n_heads;
   const int ns = a.n_split;
+  constexpr int kB = 16;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(s * RH + rh) * 2]);
-  constexpr int kB = 8;
+  if (ns > kB)
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(s * RH + rh) * 2]);
   float L = 0.0f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < ns; s0 += kB) {
@@ -372,6 +375,10 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
       p[j] = *reinterpret_cast<const float4*>(a.part_o + (sj * RH + rh) * kD + 4 * threadIdx.x);
       ms[j] = a.part_ml[(sj * RH + rh) * 2];
       ls[j] = a.part_ml[(sj * RH + rh) * 2 + 1];
+    }
+    if (ns <= kB) {
+#pragma unroll
+      for (int j = 0; j < kB; ++j) M = fmaxf(M, ms[j]);   // clamped slots repeat a real split
     }
 #pragma unroll
     for (int j = 0; j < kB; ++j) {

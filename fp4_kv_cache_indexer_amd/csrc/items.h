@@ -1,0 +1,48 @@
+// Row and item mapping shared by the indexer's score and top-k kernels: the
+// sequence and visible entries of a query row, and the position (entry or
+// block id) behind each item a row walks in flat, block, pool and candidate
+// mode.
+#pragma once
+
+#include "csa2_dev.h"
+#include "csa2_launch.h"
+
+namespace csa2 {
+
+// ---------------------------------------------------------------------------
+// item <-> position mapping
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
+  return im.row_seq ? (int64_t)im.row_seq[r] : (int64_t)r;
+}
+
+// Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's
+// sequence is not in the cache.
+__device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r) {
+  const int64_t seq = row_seq_of(im, r);
+  if (seq < 0 || seq >= im.n_seq) return 0;
+  const int64_t nv = im.n_valid ? (int64_t)im.n_valid[r] : im.n_ent;
+  return nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
+}
+
+__device__ __forceinline__ int64_t row_items(const ItemMap& im, int64_t nv) {
+  if (im.mode == kItemsFlat) return nv;
+  if (im.mode == kItemsBlocks) return (nv + kBlockPos - 1) / kBlockPos;
+  return im.n_items;
+}
+
+// Position (entry or block id) of item i of row r, or -1 if the item is not
+// visible to the row.
+__device__ __forceinline__ int64_t item_pos(const ItemMap& im, int r, int64_t i, int64_t nv) {
+  if (im.mode == kItemsFlat || im.mode == kItemsBlocks) return i;
+  if (im.mode == kItemsPool) {
+    const int32_t b = im.list[(int64_t)r * im.list_len + (i >> 3)];
+    const int64_t p = (int64_t)b * kBlockPos + (i & 7);
+    return (b >= 0 && p < nv) ? p : -1;
+  }
+  const int32_t c = im.list[(int64_t)r * im.list_len + i];
+  return (c >= 0 && (int64_t)c < nv) ? (int64_t)c : -1;
+}
+
+}  // namespace csa2

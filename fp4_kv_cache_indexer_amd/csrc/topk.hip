@@ -1,279 +1,26 @@
-// Sparse indexer + exact top-k [0539edu §3: csa2.indexer (32 heads x 128,
-// top_k 512) and its hierarchical block (2048 blocks x 8 positions)].
+// Exact top-k of the indexer scores [0539edu §3: top_k 512; hierarchical
+// block: keep 2048 blocks; ties go to the lower position].
 //
-//   score:  I_t = sum_h w_h * max(0, q_h . k_t), q/k FP8 E4M3, float32
-//           accumulation.  The 128-byte keys stream straight from HBM into
-//           registers, are widened to fp16 there (exact: every E4M3 value is
-//           an fp16 value) and meet the queries in v_mfma_f32_16x16x32_f16,
-//           [32 heads x 128] x [128 x 16 entries] per 8 MFMAs; the head
-//           reduction runs in the epilogue.  (gfx950's fp8 MFMAs were measured
-//           to sum their products with less than float32 precision -- up to
-//           ~1e-3 relative on heavy-tailed data -- which is as wide as the
-//           top-k tie band; the fp16 MFMA matches a float32 FMA chain.)  Each
-//           workgroup also histograms the top 12 bits of the order key of its
-//           scores in LDS and folds that into a per-row histogram.
-//   top-k:  many workgroups per row.  Each reads the row histogram, finds
-//           the bin holding the k-th largest score and compacts the items of
-//           its chunk in that bin or above, in item order, as composite keys
-//           (order key of the score, ~position).  The row's last workgroup
-//           then finds the k-th largest composite key exactly with an
-//           MSB-first radix select (ties -> lower position) and writes the
-//           kept candidates in candidate order, which is ascending position.
+// Items are ranked by a composite key (order key of the score, ~position),
+// so the k largest keys are the k highest scores with ties to the lower
+// position.  The score kernel's per-row histogram of the top 12 bits gives
+// the bin b* holding the k-th score; items in b* or above are candidates.
+//   long rows:  a filter kernel (many workgroups per row) compacts each
+//               chunk's candidates in item order; one 1024-thread workgroup
+//               per row then settles the k-th composite key exactly with an
+//               MSB-first radix select over the candidates of bin b* and
+//               writes the kept ones in candidate order (ascending position).
+//   short rows: one 1024-thread workgroup per row does both, with the
+//               candidates in LDS (the workspace when they do not fit).
+// The select leaves the row histogram zeroed for the next call.
 #include "csa2_dev.h"
 #include "csa2_launch.h"
+#include "items.h"
 
 namespace csa2 {
 
 // ---------------------------------------------------------------------------
-// item <-> position mapping
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
-  return im.row_seq ? (int64_t)im.row_seq[r] : (int64_t)r;
-}
-
-// Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's
-// sequence is not in the cache.
-__device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r) {
-  const int64_t seq = row_seq_of(im, r);
-  if (seq < 0 || seq >= im.n_seq) return 0;
-  const int64_t nv = im.n_valid ? (int64_t)im.n_valid[r] : im.n_ent;
-  return nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
-}
-
-__device__ __forceinline__ int64_t row_items(const ItemMap& im, int64_t nv) {
-  if (im.mode == kItemsFlat) return nv;
-  if (im.mode == kItemsBlocks) return (nv + kBlockPos - 1) / kBlockPos;
-  return im.n_items;
-}
-
-// Position (entry or block id) of item i of row r, or -1 if the item is not
-// visible to the row.
-__device__ __forceinline__ int64_t item_pos(const ItemMap& im, int r, int64_t i, int64_t nv) {
-  if (im.mode == kItemsFlat || im.mode == kItemsBlocks) return i;
-  if (im.mode == kItemsPool) {
-    const int32_t b = im.list[(int64_t)r * im.list_len + (i >> 3)];
-    const int64_t p = (int64_t)b * kBlockPos + (i & 7);
-    return (b >= 0 && p < nv) ? p : -1;
-  }
-  const int32_t c = im.list[(int64_t)r * im.list_len + i];
-  return (c >= 0 && (int64_t)c < nv) ? (int64_t)c : -1;
-}
-
-// ---------------------------------------------------------------------------
-// score kernel
-// ---------------------------------------------------------------------------
-
-constexpr int kScoreThreads = 256;
-constexpr int kScoreWaves = kScoreThreads / 64;
-constexpr int kTilesPerIter = 4;   // 16-item tiles per group
-// Chosen by measurement on the 8 x 131072-block coarse scan: double-buffered
-// groups of 4 tiles, register budget for 2 waves per SIMD (28.7 us vs
-// 29.8-37 us for the single-buffered, larger-group and tighter-budget forms).
-constexpr bool kScoreDB = true;
-constexpr int kScoreMinW = 2;
-
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v8i load32(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-  v8i v;
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  return v;
-}
-
-// 8 E4M3 bytes (two words, byte order = element order) widened to fp16.
-__device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
-  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w0, 1.0f, false);
-  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w0, 1.0f, true);
-  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w1, 1.0f, false);
-  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w1, 1.0f, true);
-  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// DB: double-buffer the tile groups of a wave; MINW: waves per SIMD the
-// register budget must allow.
-// G > 0: the chunk is exactly G groups per wave and the group loop is fully
-// unrolled (straight-line code lets the compiler keep the next group's loads
-// in flight exactly); G == 0: runtime trip count.
-template <int MODE, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0>
-__global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
-  a.im.mode = MODE;                              // lets the item mapping fold away
-  __shared__ uint32_t hist[kHistBins];
-  const int r = blockIdx.y;
-  const int64_t nv = row_valid(a.im, r);
-  const int64_t n_row = row_items(a.im, nv);
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
-  if (c0 >= n_row) return;                       // uniform for the workgroup
-  const int64_t c1 = min(c0 + (int64_t)a.chunk, n_row);
-
-  for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) hist[b] = 0u;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t seq = row_seq_of(a.im, r);
-  const uint8_t* kbase = a.keys + seq * a.seq_rows * kIdxDim + g * 32;
-
-  // MFMA A operands: indexer query rows n and 16+n, bytes [32g, 32g+32), as
-  // four fp16 k-slices of 8.  The B operand (keys) uses the same byte split,
-  // so each lane's query bytes meet the same key bytes and the four MFMAs
-  // together form the full 128-term dot product.
-  const uint8_t* qr = a.q + (int64_t)r * kIdxHeads * kIdxDim + g * 32;
-  v8h qa0[4], qa1[4];
-  {
-    const v8i q0 = load32(qr + n * kIdxDim);
-    const v8i q1 = load32(qr + (16 + n) * kIdxDim);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qa0[u] = fp8x8_to_f16(q0[2 * u], q0[2 * u + 1]);
-      qa1[u] = fp8x8_to_f16(q1[2 * u], q1[2 * u + 1]);
-    }
-  }
-  float w0[4], w1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w0[i] = a.w ? a.w[r * kIdxHeads + 4 * g + i] : 1.0f;
-    w1[i] = a.w ? a.w[r * kIdxHeads + 16 + 4 * g + i] : 1.0f;
-  }
-  float* srow = a.scores + (int64_t)r * a.row_stride;
-  __syncthreads();
-
-  // A wave works on groups of U tiles of 16 items (U a multiple of 4).
-  // Loads are unconditional (an invisible item reads a visible row and its
-  // score is masked when written).
-  const int64_t ntiles = (c1 - c0 + 15) / 16;
-  const int64_t gstride = (int64_t)kScoreWaves * U;
-  const int32_t p0 = (int32_t)item_pos(a.im, r, c0, nv);
-  const int32_t safe_pos = p0 >= 0 ? p0 : 0;
-  auto load_group = [&](int64_t t0, v8i* kb, int32_t* pos) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t item = c0 + (t0 + u) * 16 + n;
-      pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
-      kb[u] = load32(kbase + (int64_t)(pos[u] >= 0 ? pos[u] : safe_pos) * kIdxDim);
-    }
-  };
-  auto compute_group = [&](int64_t t0, const v8i* kb) {
-#pragma unroll
-    for (int u4 = 0; u4 < U; u4 += 4) {
-      float p[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        // D[h][entry] = sum_k q[h][k] * key[entry][k]; lane: entry n, heads 4g+i
-        v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const v8h kh = fp8x8_to_f16(kb[u4 + u][2 * v], kb[u4 + u][2 * v + 1]);
-          d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa0[v], kh, d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa1[v], kh, d1, 0, 0, 0);
-        }
-        float sp = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sp = fmaf(w0[i], fmaxf(d0[i], 0.0f), sp);
-          sp = fmaf(w1[i], fmaxf(d1[i], 0.0f), sp);
-        }
-        p[u] = sp;
-      }
-      // transpose-reduce: lane (n, g) ends with the full score of tile
-      // u4 + g, entry n (sum over the four head groups) after three lane
-      // exchanges
-      const bool b0 = g & 1, b1 = (g >> 1) & 1;
-      float keep0 = b0 ? p[1] : p[0], send0 = b0 ? p[0] : p[1];
-      float keep1 = b0 ? p[3] : p[2], send1 = b0 ? p[2] : p[3];
-      keep0 += __shfl_xor(send0, 16);
-      keep1 += __shfl_xor(send1, 16);
-      float sc = b1 ? keep1 : keep0;
-      sc += __shfl_xor(b1 ? keep0 : keep1, 32);
-      const int64_t item = c0 + (t0 + u4 + g) * 16 + n;
-      if (item < c1) {
-        if (item_pos(a.im, r, item, nv) >= 0) {
-          srow[item] = sc;
-          atomicAdd(&hist[order_key(sc) >> (32 - kHistBits)], 1u);
-        } else {
-          srow[item] = __uint_as_float(0x7FC00000u);   // not visible
-        }
-      }
-    }
-  };
-  v8i kA[U], kB[U];
-  int32_t pA[U], pB[U];
-  int64_t t0 = (int64_t)wave * U;
-  if (G > 0) {
-    // straight-line: load group i+1 before computing group i
-    load_group(t0, kA, pA);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int64_t ti = t0 + i * gstride;
-      if (i + 1 < G) {
-        if (i & 1) load_group(ti + gstride, kA, pA); else load_group(ti + gstride, kB, pB);
-      }
-      // keep the next group's loads above this group's arithmetic
-      __builtin_amdgcn_sched_barrier(0);
-      if (i & 1) compute_group(ti, kB); else compute_group(ti, kA);
-    }
-  } else if (DB) {
-    if (t0 < ntiles) load_group(t0, kA, pA);
-    for (; t0 < ntiles; t0 += 2 * gstride) {
-      const int64_t t1 = t0 + gstride;
-      if (t1 < ntiles) load_group(t1, kB, pB);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_group(t0, kA);
-      if (t1 >= ntiles) break;
-      const int64_t t2 = t1 + gstride;
-      if (t2 < ntiles) load_group(t2, kA, pA);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_group(t1, kB);
-    }
-  } else {
-    for (; t0 < ntiles; t0 += gstride) {
-      load_group(t0, kA, pA);
-      compute_group(t0, kA);
-    }
-  }
-  __syncthreads();
-  uint32_t* ghist = a.hist + (int64_t)r * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
-    const uint32_t c = hist[b];
-    if (c) atomicAdd(&ghist[b], c);
-  }
-}
-
-// Workgroups of one score kernel that fit on the device at once.
-int score_resident_wgs() {
-  static int cached = 0;
-  if (cached) return cached;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_score_kernel<kItemsBlocks, kScoreDB, kScoreMinW>,
-                                                   kScoreThreads, 0) != hipSuccess ||
-      cus <= 0 || per_cu <= 0) {
-    (void)hipGetLastError();
-    return 1024;
-  }
-  cached = cus * per_cu;
-  return cached;
-}
-
-hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
-  if (a.n_rows == 0 || a.im.n_items == 0) return hipSuccess;
-  const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
-  const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
-  switch (a.im.mode) {
-    case kItemsFlat: hipLaunchKernelGGL((index_score_kernel<kItemsFlat, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    case kItemsBlocks: hipLaunchKernelGGL((index_score_kernel<kItemsBlocks, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    case kItemsPool: hipLaunchKernelGGL((index_score_kernel<kItemsPool, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((index_score_kernel<kItemsCand, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-  }
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// top-k: filter (many workgroups per row) + select (one workgroup per row)
+// filter (many workgroups per row) + select (one workgroup per row)
 // ---------------------------------------------------------------------------
 
 constexpr int kFiltThreads = 256;
