@@ -45,6 +45,8 @@ class IndexerArgs(ctypes.Structure):
         ("out_idx", ctypes.c_void_p),
         ("out_score", ctypes.c_void_p),
         ("out_blocks", ctypes.c_void_p),
+        ("cand_blocks", ctypes.c_void_p),
+        ("n_cand_blocks", ctypes.c_int32),
     ]
 
 
@@ -197,7 +199,7 @@ def index_block_summary(keys, summ=None, blk_begin=0, blk_end=None, stream=None)
 
 
 def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
-                    out_idx, out_score, out_blocks):
+                    out_idx, out_score, out_blocks, cand_blocks=None):
     a = IndexerArgs()
     a.n_rows = q.shape[0]
     a.n_seq = keys.shape[0]
@@ -215,28 +217,32 @@ def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_b
     a.out_idx = _ptr(out_idx)
     a.out_score = _ptr(out_score)
     a.out_blocks = _ptr(out_blocks)
+    a.cand_blocks = _ptr(cand_blocks)
+    a.n_cand_blocks = 0 if cand_blocks is None else cand_blocks.shape[1]
     return a
 
 
-def indexer_topk_workspace(q, keys, top_k, block_keys=None, keep_blocks=2048, cand=None):
+def indexer_topk_workspace(q, keys, top_k, block_keys=None, keep_blocks=2048, cand=None, cand_blocks=None):
     a = _indexer_struct(q, keys, top_k, None, None, None, block_keys, keep_blocks, cand,
-                        None, None, None)
+                        None, None, None, cand_blocks)
     return lib().csa2_indexer_topk_workspace(ctypes.byref(a))
 
 
 def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_keys=None,
                  keep_blocks=2048, cand=None, out_idx=None, out_score=None, out_blocks=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, cand_blocks=None):
     """q uint8 [R, 32, 128]; keys uint8 [S, N, 128].  Returns out_idx int32
-    [R, top_k] (ascending, -1 padded)."""
+    [R, top_k] (ascending, -1 padded).  cand_blocks int32 [R, B]: select among
+    the positions of these blocks (e.g. a Full layer's out_blocks)."""
     for t, nm in ((q, "q"), (keys, "keys"), (head_w, "head_w"), (row_seq, "row_seq"),
-                  (n_valid, "n_valid"), (block_keys, "block_keys"), (cand, "cand")):
+                  (n_valid, "n_valid"), (block_keys, "block_keys"), (cand, "cand"),
+                  (cand_blocks, "cand_blocks")):
         _dev(t, nm)
     R = q.shape[0]
     if out_idx is None:
         out_idx = torch.empty((R, top_k), dtype=torch.int32, device=q.device)
     a = _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
-                        out_idx, out_score, out_blocks)
+                        out_idx, out_score, out_blocks, cand_blocks)
     L = lib()
     need = L.csa2_indexer_topk_workspace(ctypes.byref(a))
     if workspace is None:

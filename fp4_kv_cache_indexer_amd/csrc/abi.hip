@@ -62,7 +62,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---- indexer workspace layout ---------------------------------------------
 
 struct IndexerPlan {
-  int mode;                 // 0 flat, 1 hierarchical, 2 candidate
+  int mode;                 // 0 flat, 1 hierarchical, 2 candidate, 3 block pool
   int64_t R, N, NB;
   int32_t keep;
   int32_t items0, items1;   // items a row walks in stage 0 / 1
@@ -78,7 +78,8 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
   if (a->n_ent < 0 || a->n_ent > 0x7FFFFFF0LL) return fail(CSA2_EINVAL, "indexer: n_ent out of range");
   if (a->top_k < 1 || a->top_k > CSA2_MAX_TOPK)
     return fail(CSA2_EUNSUPPORTED, "indexer: top_k %d outside [1, %d]", a->top_k, CSA2_MAX_TOPK);
-  if (a->block_keys && a->cand) return fail(CSA2_EINVAL, "indexer: block_keys and cand are exclusive");
+  if ((a->block_keys != nullptr) + (a->cand != nullptr) + (a->cand_blocks != nullptr) > 1)
+    return fail(CSA2_EINVAL, "indexer: block_keys, cand and cand_blocks are exclusive");
   if (a->n_rows > 0 && check_ptrs) {
     if (!a->q || !a->keys || !a->out_idx) return fail(CSA2_EINVAL, "indexer: q, keys and out_idx are required");
     if (!aligned(a->q, 16) || !aligned(a->keys, 16)) return fail(CSA2_EINVAL, "indexer: q/keys not 16-byte aligned");
@@ -100,6 +101,13 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
     p->keep = a->keep_blocks;
     p->items0 = (int32_t)p->NB;
     p->items1 = a->keep_blocks * CSA2_BLOCK_POS;
+  } else if (a->cand_blocks) {
+    if (a->n_cand_blocks < 1 || a->n_cand_blocks > csa2::kMaxItems / CSA2_BLOCK_POS)
+      return fail(CSA2_EINVAL, "indexer: n_cand_blocks %d outside [1, %lld]", a->n_cand_blocks,
+                  (long long)(csa2::kMaxItems / CSA2_BLOCK_POS));
+    if (check_ptrs && !aligned(a->cand_blocks, 4)) return fail(CSA2_EINVAL, "indexer: cand_blocks not 4-byte aligned");
+    p->mode = 3;
+    p->items0 = a->n_cand_blocks * CSA2_BLOCK_POS;
   } else if (a->cand) {
     if (a->n_cand < 1) return fail(CSA2_EINVAL, "indexer: n_cand < 1 with cand set");
     if (check_ptrs && !aligned(a->cand, 4)) return fail(CSA2_EINVAL, "indexer: cand not 4-byte aligned");
@@ -338,6 +346,13 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
     return CSA2_OK;
   };
 
+  if (p.mode == 3) {
+    im0.mode = csa2::kItemsPool;
+    im0.list = a->cand_blocks;
+    im0.list_len = a->n_cand_blocks;
+    return stage(CSA2_SITE_SCORE_POOL, im0, a->keys, a->n_ent, p.stride0, scores0, hist0, a->top_k,
+                 a->out_idx, a->out_score);
+  }
   if (p.mode == 0 || p.mode == 2) {
     im0.mode = p.mode == 0 ? csa2::kItemsFlat : csa2::kItemsCand;
     im0.list = a->cand;

@@ -116,11 +116,19 @@ __global__ __launch_bounds__(256) void block_summary_kernel(const uint8_t* __res
   const int64_t j0 = b * kBlockPos;
   const int cnt = (int)min((int64_t)kBlockPos, n_ent - j0);
   const uint8_t* base = keys + (s * n_ent + j0) * kIdxDim + c4 * 4;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < cnt; ++j) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(base + (int64_t)j * kIdxDim);
+  // all member loads at once (addresses clamped into the block), so the
+  // block costs one memory latency rather than one per member
+  uint32_t w[kBlockPos];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += e4m3_to_f32((w >> (8 * i)) & 0xFFu);
+  for (int j = 0; j < kBlockPos; ++j)
+    w[j] = *reinterpret_cast<const uint32_t*>(base + (int64_t)(j < cnt ? j : 0) * kIdxDim);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kBlockPos; ++j) {
+    if (j < cnt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += e4m3_to_f32((w[j] >> (8 * i)) & 0xFFu);
+    }
   }
   uint32_t out = 0u;
 #pragma unroll

@@ -144,9 +144,18 @@ int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_e
  *   candidate     cand != NULL: select among cand[r][0..n_cand) (distinct
  *                 entry ids; -1 and ids >= n_valid are skipped), e.g. a pool
  *                 kept from an earlier layer.
+ *   block pool    cand_blocks != NULL: select among the positions below
+ *                 n_valid of the blocks cand_blocks[r][0..n_cand_blocks)
+ *                 (block b covers entries 8b..8b+7; -1 skipped) -- the fine
+ *                 stage of the hierarchical mode on a given block list.  With
+ *                 the pool of a Full layer (its out_blocks) this restricts a
+ *                 Reindex layer to that pool [0539edu §3: the candidate pool
+ *                 bounds the indexer's work].  Output is ascending when the
+ *                 list is (out_blocks is); otherwise it follows the list.
  * Supported: 1 <= top_k <= 2048, 1 <= keep_blocks <= 2048, and at most
  * 2^24 items per row in one stage (entries in flat mode, blocks in the
- * coarse stage, candidates in candidate mode).
+ * coarse stage, candidates in candidate mode, 8 per block in block-pool
+ * mode).
  */
 typedef struct {
   int32_t n_rows;           /* R >= 1                                           */
@@ -168,10 +177,12 @@ typedef struct {
   float* out_score;         /* [R][k] their scores, or NULL                     */
   int32_t* out_blocks;      /* [R][keep_blocks] kept blocks (hierarchical mode,
                                ascending, -1 padded), or NULL                   */
+  const int32_t* cand_blocks;/* [R][n_cand_blocks] block ids, or NULL           */
+  int32_t n_cand_blocks;    /* blocks per row when cand_blocks != NULL          */
 } csa2_indexer_args;
 
 /* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error).
- * Reads only the sizes and which of block_keys/cand are set; data pointers
+ * Reads only the sizes and which of block_keys/cand/cand_blocks are set; data pointers
  * may still be NULL.
  *
  * The indexer workspace must be ZERO-FILLED before its first use.  It holds

@@ -308,22 +308,37 @@ def swa_slots(start, length, cap):
 
 
 def layer_group(modes, q_attn, q_idx, w_idx, codes, scales, keys, swa, slots, k,
-                block_keys=None, keep_blocks=2048, n_valid=None, sm_scale=None):
+                block_keys=None, keep_blocks=2048, n_valid=None, sm_scale=None,
+                reindex_in_pool=False):
     """Run one row through a group of layers with modes in {full, reuse,
     reindex}.  Full and Reindex layers select with their own indexer query
     over the shared keys; Reuse layers attend with the last selection.  The
     main KV and index keys are shared by the group; each layer has its own
     query and its own sliding window (swa[L]).  Returns [(idx, O, LSE)] per
-    layer."""
+    layer.
+
+    reindex_in_pool (with block_keys): a Reindex layer selects only among the
+    candidate pool -- the kept blocks' positions -- of the latest Full layer,
+    instead of running its own coarse stage [0539edu §3: the 16384-position
+    pool bounds the indexer's work per query; ai-feeds Method: index reuse
+    across layers]."""
     idx = None
+    pool_blocks = None
     out = []
     for L, mode in enumerate(modes):
         if mode in ("full", "reindex"):
             if block_keys is None:
                 idx = indexer_topk_flat(q_idx[L], w_idx[L], keys, k, n_valid)
+            elif mode == "reindex" and reindex_in_pool:
+                if pool_blocks is None:
+                    raise ValueError("a pool-restricted reindex layer needs an earlier full layer")
+                N = keys.shape[0] if n_valid is None else int(n_valid)
+                idx = indexer_topk_pool(q_idx[L], w_idx[L], keys, pool_positions(pool_blocks, N), k, N)
             else:
-                idx, _ = indexer_topk_hier(q_idx[L], w_idx[L], keys, block_keys, k,
-                                           n_valid, keep_blocks)
+                idx, kept = indexer_topk_hier(q_idx[L], w_idx[L], keys, block_keys, k,
+                                              n_valid, keep_blocks)
+                if mode == "full":
+                    pool_blocks = kept
         elif mode == "reuse":
             if idx is None:
                 raise ValueError("a reuse layer needs an earlier full/reindex layer")

@@ -66,21 +66,25 @@ def _idx_args(**kw):
 def test_indexer_validation_without_gpu():
     L = C.lib()
     ws = ctypes.c_void_p(0x10000)
+    # (fields, status, whether the size query -- which checks no pointers -- fails too)
+    cb = dict(cand_blocks=ctypes.c_void_p(0x6000), n_cand_blocks=4)
     cases = [
-        (dict(top_k=0), 2), (dict(top_k=4096), 2), (dict(q=None), 1),
-        (dict(keys=ctypes.c_void_p(0x2001)), 1),
-        (dict(block_keys=ctypes.c_void_p(0x4000), cand=ctypes.c_void_p(0x5000), n_cand=4), 1),
-        (dict(block_keys=ctypes.c_void_p(0x4000), keep_blocks=0), 2),
-        (dict(cand=ctypes.c_void_p(0x5000), n_cand=0), 1),
-        (dict(n_ent=-1), 1), (dict(n_seq=-1), 1),
+        (dict(top_k=0), 2, True), (dict(top_k=4096), 2, True), (dict(q=None), 1, False),
+        (dict(keys=ctypes.c_void_p(0x2001)), 1, False),
+        (dict(block_keys=ctypes.c_void_p(0x4000), cand=ctypes.c_void_p(0x5000), n_cand=4), 1, True),
+        (dict(block_keys=ctypes.c_void_p(0x4000), keep_blocks=0), 2, True),
+        (dict(cand=ctypes.c_void_p(0x5000), n_cand=0), 1, True),
+        (dict(n_ent=-1), 1, True), (dict(n_seq=-1), 1, True),
+        (dict(cb, cand=ctypes.c_void_p(0x5000), n_cand=4), 1, True),
+        (dict(cb, block_keys=ctypes.c_void_p(0x4000)), 1, True),
+        (dict(cand_blocks=ctypes.c_void_p(0x6000), n_cand_blocks=0), 1, True),
+        (dict(cand_blocks=ctypes.c_void_p(0x6002), n_cand_blocks=4), 1, False),
     ]
-    shape_errors = ("top_k", "keep_blocks", "n_cand", "n_ent", "n_seq")
-    for kw, status in cases:
+    for kw, status, ws_fails in cases:
         a = _idx_args(**kw)
         assert L.csa2_indexer_topk(ctypes.byref(a), ws, 1 << 30, None) == status, kw
         assert C.last_error() != ""
-        if any(k in kw for k in shape_errors) or "block_keys" in kw and "cand" in kw:
-            assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) == 0, kw
+        assert (L.csa2_indexer_topk_workspace(ctypes.byref(a)) == 0) == ws_fails, kw
     # the size query needs no data pointers
     a = _idx_args(q=None, keys=None, out_idx=None)
     assert L.csa2_indexer_topk_workspace(ctypes.byref(a)) > 0
@@ -92,6 +96,11 @@ def test_indexer_validation_without_gpu():
     # hierarchical workspace grows with the kept pool
     ah = _idx_args(block_keys=ctypes.c_void_p(0x4000))
     assert L.csa2_indexer_topk_workspace(ctypes.byref(ah)) > need
+    # block-pool mode sizes its stage by 8 positions per block
+    ab = _idx_args(cand_blocks=None, n_cand_blocks=300)
+    assert L.csa2_indexer_topk_workspace(ctypes.byref(ab)) == need   # no blocks pointer: flat
+    ab.cand_blocks = ctypes.c_void_p(0x6000)
+    assert L.csa2_indexer_topk_workspace(ctypes.byref(ab)) > 0
 
 
 @needs_lib

@@ -22,6 +22,8 @@ the host.
   C5  cache write of 1M tokens at m=2, then a 4096-query prefill chunk at
       the end of the context (256 of its rows, every 16th) with causal
       top-512 + SWA 128
+  C4 with pool-restricted Reindex: the Full layer selects hierarchically and
+      the Reindex layer scores only the Full layer's 16384-position pool
 """
 
 import numpy as np
@@ -374,3 +376,51 @@ def test_c5_cache_write_and_prefill_chunk():
         check_close(go[r], Ox, f"C5 row {r} out")
         check_close(gl[r], lx, f"C5 row {r} lse")
     assert compared >= 2
+
+
+def test_c4_reindex_in_pool():
+    say("C4 with pool-restricted Reindex: batch 64, 262144 entries, Full hierarchical (keep 2048), "
+        "Reindex over the Full layer's pool")
+    seed, cfg, S, N, H, k, keep = 0, 3, 64, 262144, 64, 512, 2048
+    cache = Cache(seed, cfg, S, N, 1)
+    keys = index_keys(seed, cfg, S, N)
+    summ = C.index_block_summary(keys)
+    swa_len = torch.full((S,), 128, dtype=torch.int32, device="cuda")
+    blocks = torch.empty((S, keep), dtype=torch.int32, device="cuda")
+    q1, w1, qa1, swa1 = queries(seed, cfg, S, H, layer=1)
+    q5, w5, qa5, swa5 = queries(seed, cfg, S, H, layer=5)
+    say("  Full layer (hierarchical) and pool-restricted Reindex layer")
+    idx1 = C.indexer_topk(q1, keys, k, head_w=w1, block_keys=summ, keep_blocks=keep, out_blocks=blocks)
+    idx5 = C.indexer_topk(q5, keys, k, head_w=w5, cand_blocks=blocks)
+    out5, lse5 = C.sparse_attn_decode(qa5, cache.codes, cache.scales, idx5, swa=swa5, swa_len=swa_len)
+    torch.cuda.synchronize()
+    gb, gi5, go5, gl5 = host(blocks), host(idx5), host(out5), host(lse5)
+    compared = 0
+    for r in (0, 41):
+        keys_h = host(keys[r])
+        bk = O.block_summary(keys_h)
+        qi = [host(q1[r]), None, None, None, host(q5[r])]
+        wi = [host(w1[r]), None, None, None, host(w5[r])]
+        _, kept = O.indexer_topk_hier(qi[0], wi[0], keys_h, bk, k, N, keep)
+        sb = O.index_scores(qi[0], wi[0], bk)
+        check_topk(gb[r], kept, np.arange(len(bk)), sb, keep, f"row {r} full-layer blocks")
+        if not np.array_equal(gb[r], kept):
+            continue                       # a coarse tie swapped a block: the pools differ legitimately
+        pool = O.pool_positions(kept, N)
+        sc = O.index_scores(qi[4], wi[4], keys_h[pool])
+        ref5 = O.indexer_topk_pool(qi[4], wi[4], keys_h, pool, k, N)
+        check_topk(gi5[r], ref5, pool, sc, k, f"row {r} reindex in pool")
+        if not np.array_equal(gi5[r], ref5):
+            continue
+        codes_o, scales_o, same = cache.oracle_sparse(r, ref5)
+        assert same
+        modes = ["full", "reuse", "reuse", "reuse", "reindex"]
+        qa = [synth.bf16_host_bits(qa1[r])] * 4 + [synth.bf16_host_bits(qa5[r])]
+        sw = [host(swa1[r])] * 4 + [host(swa5[r])]
+        ref = O.layer_group(modes, qa, qi, wi, codes_o, scales_o, keys_h, sw, O.swa_slots(0, 128, 128), k,
+                            block_keys=bk, keep_blocks=keep, reindex_in_pool=True)
+        assert np.array_equal(ref[4][0], ref5)
+        check_close(go5[r], ref[4][1], f"row {r} reindex out")
+        check_close(gl5[r], ref[4][2], f"row {r} reindex lse")
+        compared += 1
+    assert compared >= 1

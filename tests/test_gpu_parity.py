@@ -259,6 +259,25 @@ def test_indexer_flat_long_rows():
     check_flat_rows(case, gi, gsc, 2048)
 
 
+def test_indexer_block_pool():
+    """Block-pool mode: select among the positions of given blocks (ascending
+    lists with -1 holes and blocks past n_valid), ragged rows."""
+    say("indexer block pool: S=2 N=20003 R=3, 300-block lists")
+    case = idx_case(31, 2, 20003, 3, row_seq=np.array([0, 1, 1]), n_valid=np.array([20003, 9001, 20003]))
+    g = np.random.default_rng(8)
+    nb = (20003 + 7) // 8
+    blocks = np.stack([np.sort(g.choice(nb, 300, replace=False)) for _ in range(3)]).astype(np.int32)
+    blocks[:, ::29] = -1
+    gi, gsc = run_indexer(case, 512, cand_blocks=dev(blocks))
+    for r in range(3):
+        s = int(case["row_seq"][r])
+        nv = int(case["n_valid"][r])
+        pool = O.pool_positions(blocks[r], nv)
+        sc = O.index_scores(case["q"][r], case["w"][r], case["keys"][s][pool])
+        ref = O.indexer_topk_pool(case["q"][r], case["w"][r], case["keys"][s], pool, 512, nv)
+        check_topk(gi[r], ref, pool, sc, 512, f"row {r}")
+
+
 def test_indexer_wide_tie_bins():
     """Boundary bins far larger than the workgroup's staging buffer: every
     key equal (one bin holds the whole row) and three distinct keys (three

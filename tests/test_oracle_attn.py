@@ -98,6 +98,37 @@ def test_layer_group_reuse_and_reindex():
     assert np.array_equal(out[3][0], out[2][0]) and not np.array_equal(out[2][0], out[0][0])
 
 
+def test_layer_group_reindex_in_pool():
+    """A Reindex layer restricted to the Full layer's pool: brute force over
+    the pool's positions, and equal to the unrestricted (hierarchical)
+    Reindex when the pool covers every entry."""
+    c, codes, scales = case(N=203, H=4)
+    g = np.random.default_rng(5)
+    keys = c.keys[0]
+    bk = O.block_summary(keys)
+    q1, q2 = c.q_idx[0], synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32))
+    w = g.uniform(0.25, 1.0, 32)
+    modes = ["full", "reuse", "reindex"]
+    L = len(modes)
+    args = dict(q_attn=[c.q[0]] * L, q_idx=[q1, None, q2], w_idx=[w, None, w], codes=codes, scales=scales,
+                keys=keys, swa=[c.swa[0]] * L, slots=O.swa_slots(0, 40, 40), k=16, block_keys=bk)
+    out = O.layer_group(modes, keep_blocks=6, reindex_in_pool=True, **args)
+    # brute force: the Full layer's six best blocks (ties to the lower id),
+    # their positions, then the reindex query's best 16 there
+    sb = [sum(wi * max(0.0, float(np.dot(F.e4m3_decode(q2b), F.e4m3_decode(kb))))
+              for wi, q2b in zip(w, q1)) for kb in bk]
+    blocks = sorted(sorted(range(len(bk)), key=lambda b: (-sb[b], b))[:6])
+    pool = [8 * b + i for b in blocks for i in range(8) if 8 * b + i < len(keys)]
+    sp = {p: sum(wi * max(0.0, float(np.dot(F.e4m3_decode(qr), F.e4m3_decode(keys[p]))))
+                 for wi, qr in zip(w, q2)) for p in pool}
+    want = sorted(sorted(pool, key=lambda p: (-sp[p], p))[:16])
+    assert out[2][0].tolist() == want
+    # restricting to a pool that covers everything changes nothing
+    full = O.layer_group(modes, keep_blocks=26, reindex_in_pool=True, **args)
+    free = O.layer_group(modes, keep_blocks=26, reindex_in_pool=False, **args)
+    assert np.array_equal(full[2][0], free[2][0]) and np.array_equal(full[2][1], free[2][1])
+
+
 def test_prefill_row_view():
     assert O.prefill_row_view(0, 2) == (0, 0, 1)
     assert O.prefill_row_view(1, 2) == (1, 0, 2)
