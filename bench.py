@@ -49,7 +49,22 @@ WORKLOADS = {
                B=32, N=1 << 16, H=64, k=512, keep=0, hier=False, m=2, dist="t3"),
     "c1": dict(desc="single decode query, 4,096 FP4 entries, top-512, 16 heads, SWA 128 fp8",
                B=1, N=4096, H=16, k=512, keep=0, hier=False, m=1, dist="normal"),
+    # layer groups: one query = one token through all the group's layers
+    "c4": dict(desc="layer group, batch 64: 262,144 FP4 entries/seq; Full (flat indexer, top-512) + "
+                    "3 Reuse + Reindex (flat, new indexer queries) + 3 Reuse; 64 heads, SWA 128 fp8, "
+                    "fresh queries and windows per layer",
+               B=64, N=262144, H=64, k=512, keep=0, hier=False, m=1, dist="normal",
+               layers=("full", "reuse", "reuse", "reuse", "reindex", "reuse", "reuse", "reuse")),
+    "c4pool": dict(desc="layer group, batch 64: 262,144 FP4 entries/seq; Full (hierarchical, keep 2048 "
+                        "blocks -> 16384-position pool, top-512) + 3 Reuse + Reindex restricted to the "
+                        "Full layer's pool + 3 Reuse; 64 heads, SWA 128 fp8, fresh queries per layer",
+                   B=64, N=262144, H=64, k=512, keep=2048, hier=True, m=1, dist="normal", pool=True,
+                   layers=("full", "reuse", "reuse", "reuse", "reindex", "reuse", "reuse", "reuse")),
 }
+
+
+def layers_of(w):
+    return w.get("layers", ("full",))
 
 
 class InputSet:
@@ -79,6 +94,20 @@ class InputSet:
         self.q = torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16)
         self.x_new = synth.latent_dev((B, m, 512), g, w["dist"]).to(torch.bfloat16)
         self.z_new = torch.randn((B, m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+        # per-layer queries and windows (layer 0 uses the tensors above)
+        layers = layers_of(w)
+        self.lq, self.lq_idx, self.lswa = [self.q], [self.q_idx], [self.swa]
+        for L in range(1, len(layers)):
+            self.lq_idx.append(synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
+                               if layers[L] == "reindex" else None)
+            self.lq.append(torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16))
+            self.lswa.append(synth.to_e4m3(synth.latent_dev((B, 128, 512), g, w["dist"])))
+        self.pool = w.get("pool", False)
+        self.blocks = torch.empty((B, w["keep"]), dtype=torch.int32, device="cuda") if self.pool else None
+        self.idx2 = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
+        self.ws_idx2 = torch.zeros(max(256, C.indexer_topk_workspace(
+            self.q_idx, self.keys, w["k"], block_keys=None if self.pool else self.summ,
+            keep_blocks=w["keep"] or 2048, cand_blocks=self.blocks)), dtype=torch.uint8, device="cuda")
         self.idx = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
@@ -99,12 +128,26 @@ def step(w, s):
     if w["hier"]:
         b = (N - 1) // 8
         C.index_block_summary(s.keys, summ=s.summ, blk_begin=b, blk_end=b + 1)
-    # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context)
-    C.indexer_topk(s.q_idx, s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
-                   out_idx=s.idx, workspace=s.ws_idx)
-    # a4-a6: gather + dequant + joint sparse/window attention
-    C.sparse_attn_decode(s.q, s.codes, s.scales, s.idx, swa=s.swa, swa_len=s.swa_len, out=s.out,
-                         lse=s.lse, workspace=s.ws_attn)
+    idx = None
+    for L, mode in enumerate(layers_of(w)):
+        # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context); a7:
+        # Reuse layers keep the selection, Reindex layers select anew (within
+        # the Full layer's pool when the workload says so)
+        if mode == "full":
+            C.indexer_topk(s.lq_idx[L], s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
+                           out_idx=s.idx, out_blocks=s.blocks, workspace=s.ws_idx)
+            idx = s.idx
+        elif mode == "reindex":
+            if s.pool:
+                C.indexer_topk(s.lq_idx[L], s.keys, w["k"], cand_blocks=s.blocks, out_idx=s.idx2,
+                               workspace=s.ws_idx2)
+            else:
+                C.indexer_topk(s.lq_idx[L], s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
+                               out_idx=s.idx2, workspace=s.ws_idx2)
+            idx = s.idx2
+        # a4-a6: gather + dequant + joint sparse/window attention
+        C.sparse_attn_decode(s.lq[L], s.codes, s.scales, idx, swa=s.lswa[L], swa_len=s.swa_len, out=s.out,
+                             lse=s.lse, workspace=s.ws_attn)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_coarse_c3_traffic.md")
@@ -204,12 +247,14 @@ def scan_bytes(w):
 
 def cpu_baseline(w, s, seconds):
     """Time the oracle on a bounded sample: decode steps of sequence 0 of the
-    first input set, with fresh seeded queries, until `seconds` elapse."""
+    first input set (every layer of the workload's group), with fresh seeded
+    queries, until `seconds` elapse."""
     from threadpoolctl import threadpool_info
 
     from oracle import csa2 as O
 
-    N, H, k = w["N"], w["H"], w["k"]
+    N, H, k, m = w["N"], w["H"], w["k"], w["m"]
+    layers = layers_of(w)
     keys = s.keys[0].cpu().numpy()
     x0 = s.x0.view(torch.int16).cpu().numpy().view(np.uint16)
     z0 = None if s.z0 is None else s.z0.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -219,21 +264,28 @@ def cpu_baseline(w, s, seconds):
     n = 0
     el = 0.0
     while True:
-        q_idx = synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32))
-        q = torch.from_numpy(g.standard_normal((H, 512)).astype(np.float32)).to(torch.bfloat16)
-        q = q.view(torch.int16).numpy().view(np.uint16)
+        q_idx = [synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32)) for _ in layers]
+        q = [torch.from_numpy(g.standard_normal((H, 512)).astype(np.float32)).to(torch.bfloat16)
+             .view(torch.int16).numpy().view(np.uint16) for _ in layers]
         ts = time.perf_counter()
-        m = w["m"]
         O.kv_compress_quantize(x0[-m:], None if z0 is None else z0[-m:], m)   # a0: the new entry
         if w["hier"]:
             O.block_summary(keys[(N - 1) // 8 * 8:])                   # a1: its block
-            idx, _ = O.indexer_topk_hier(q_idx, None, keys, summ, k, N, w["keep"])
-        else:
-            idx = O.indexer_topk_flat(q_idx, None, keys, k, N)
-        sel = idx[idx >= 0]
-        tok = (sel[:, None] * m + np.arange(m)[None, :]).reshape(-1)
-        codes, scales = O.kv_compress_quantize(x0[tok], None if z0 is None else z0[tok], m)
-        O.sparse_attn(q, codes, scales, np.arange(len(sel)), swa, O.swa_slots(0, 128, 128))
+        idx = kept = None
+        for L, mode in enumerate(layers):
+            if mode == "full" or (mode == "reindex" and not w.get("pool")):
+                if w["hier"]:
+                    idx, kept_l = O.indexer_topk_hier(q_idx[L], None, keys, summ, k, N, w["keep"])
+                    kept = kept_l if mode == "full" else kept
+                else:
+                    idx = O.indexer_topk_flat(q_idx[L], None, keys, k, N)
+            elif mode == "reindex":
+                idx = O.indexer_topk_pool(q_idx[L], None, keys, O.pool_positions(kept, N), k, N)
+            if mode != "reuse":
+                sel = idx[idx >= 0]
+                tok = (sel[:, None] * m + np.arange(m)[None, :]).reshape(-1)
+                codes, scales = O.kv_compress_quantize(x0[tok], None if z0 is None else z0[tok], m)
+            O.sparse_attn(q[L], codes, scales, np.arange(len(sel)), swa, O.swa_slots(0, 128, 128))
         el += time.perf_counter() - ts
         n += 1
         if el >= seconds:
@@ -246,7 +298,8 @@ def cpu_baseline(w, s, seconds):
     except OSError:
         pass
     return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode queries on sequence 0 of the {w['N']}-entry cache "
+            "sample": f"{n} decode queries{f' ({len(layers)}-layer group each)' if len(layers) > 1 else ''} "
+                      f"on sequence 0 of the {w['N']}-entry cache "
                       f"(fresh seeded queries; oracle float64, NumPy/BLAS on {threads} threads"
                       f"{', ' + model if model else ''}; {el:.1f} s)"}
 
@@ -288,6 +341,9 @@ def main():
 
     graphs = None
     if not args.no_graph:
+        for s in sets:                 # every set's eager result, the reference for its graph
+            step(w, s)
+        torch.cuda.synchronize()
         ref = [(s.idx.clone(), s.out.clone()) for s in sets]
         graphs = []
         for s in sets:
@@ -346,6 +402,7 @@ def main():
         "config": {"workload": f"{args.workload}: {w['desc']}", "batch": w["B"],
                    "entries_per_seq": w["N"], "heads": w["H"], "top_k": w["k"],
                    "keep_blocks": w["keep"], "swa_window": 128, "input_sets_rotated": len(sets),
+                   "layers": "/".join(layers_of(w)),
                    "timed": "graph replays" if graphs else "eager launches"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

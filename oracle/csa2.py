@@ -3,7 +3,8 @@
 Steps and where the pages state them:
 
 1. ``pool``            -- the main key compressor folds every m tokens into one
-   entry with context-dependent weights, "not a plain average" [nxbn §4.2];
+   entry with weights that depend on the context rather than a uniform mean
+   [nxbn §4.2];
    m = 2 in the encoder layers, m = 1 in the decoder layers [0539edu §3],
    [daiw table "four factors", row "sequence length"].  Read as a per-channel
    softmax over the m tokens of a group of caller-supplied gate logits; no
@@ -56,6 +57,7 @@ SCALE_GROUP = 16
 IDX_HEADS = 32
 IDX_DIM = 128
 BLOCK_POS = 8
+IDX_FP4_GROUP = 32          # channels per E4M3 scale of an FP4 index key
 
 
 # ---------------------------------------------------------------------------
@@ -92,11 +94,11 @@ def pool(x, z, m):
     return y.astype(np.float32).astype(np.float64)
 
 
-def quantize_fp4(y, chunk=8192):
-    """Quantise entries y [E, 512] (float32 values, given as float64) to packed
+def quantize_fp4(y, chunk=8192, group=SCALE_GROUP):
+    """Quantise entries y [E, C] (float32 values, given as float64) to packed
     FP4 codes and E4M3 scales [0539edu §3, nxbn §3.1].
 
-    Per 16-channel group: amax = max |y|; scale = E4M3(amax / 6) with the
+    Per group of `group` channels (16 for the main KV): amax = max |y|; scale = E4M3(amax / 6) with the
     division done in float32 (6 is the largest E2M1 magnitude); a zero scale
     gives all-zero codes; otherwise each |y| becomes the nearest point of
     {0, .5, 1, 1.5, 2, 3, 4, 6} * scale, an exact tie keeping the even code;
@@ -104,17 +106,17 @@ def quantize_fp4(y, chunk=8192):
     the grid.  (After that clip the distances are exact in float64: the grid
     points have at most 7 significant bits and |y| at most 24.)
 
-    Returns codes uint8 [E, 256] (channel 2j in the low nibble of byte j,
-    channel 2j+1 in the high nibble) and scales uint8 [E, 32].
+    Returns codes uint8 [E, C/2] (channel 2j in the low nibble of byte j,
+    channel 2j+1 in the high nibble) and scales uint8 [E, C/group].
     """
     y = np.asarray(y, dtype=np.float64)
     E, C = y.shape
-    G = C // SCALE_GROUP
+    G = C // group
     packed = np.empty((E, C // 2), dtype=np.uint8)
     scales = np.empty((E, G), dtype=np.uint8)
     even = (np.arange(8) % 2 == 0)
     for e0 in range(0, E, chunk):
-        yg = y[e0:e0 + chunk].reshape(-1, G, SCALE_GROUP)
+        yg = y[e0:e0 + chunk].reshape(-1, G, group)
         amax = np.abs(yg).max(axis=2).astype(np.float32)
         s_code = e4m3_rne_sat((amax / np.float32(6.0)).astype(np.float64))
         s = e4m3_decode(s_code)
@@ -143,11 +145,11 @@ def unpack_fp4(codes):
     return out
 
 
-def dequantize_fp4(codes, scales):
+def dequantize_fp4(codes, scales, group=SCALE_GROUP):
     """FP4 entries back to float64: E2M1(code) * E4M3(scale of its group)."""
     v = e2m1_decode(unpack_fp4(codes))
     s = e4m3_decode(scales)
-    return v * np.repeat(s, SCALE_GROUP, axis=1)
+    return v * np.repeat(s, group, axis=1)
 
 
 def kv_compress_quantize(x_bits, z_bits, m):
@@ -173,7 +175,10 @@ def block_summary(keys):
     computed as an exact sum divided by the member count in float32, then
     rounded to E4M3.  (Any sum of at most 8 E4M3 values is exact in float32:
     it is a multiple of 2**-9 below 2**12, so only the division rounds.)
+    FP4 keys (Fp4Keys) go to block_summary_fp4.
     """
+    if isinstance(keys, Fp4Keys):
+        return block_summary_fp4(keys.codes, keys.scales)
     k = e4m3_decode(keys)
     N, D = k.shape
     nb = (N + BLOCK_POS - 1) // BLOCK_POS
@@ -186,8 +191,76 @@ def block_summary(keys):
 
 
 # ---------------------------------------------------------------------------
+# 4b. FP4 index keys: 128 x E2M1 + one E4M3 scale per 32 channels = 68 B/entry
+# ---------------------------------------------------------------------------
+#
+# [daiw "four generations" table: 890 B/token of global cache; "four factors"
+# table: FP4 main KV with E4M3 scales] -- with 2.5 entries per token and a
+# 288-byte FP4 main entry, 170 B/token = 68 B/entry are left for the index
+# key: 128 FP4 codes (64 B) and 4 B of scale, read here as one E4M3 scale per
+# 32 channels, quantised by the same rule as the main KV.
+
+
+class Fp4Keys:
+    """FP4 index keys (codes [N, 64], scales [N, 4]); indexable like E4M3
+    keys [N, 128], so every indexer function below takes either."""
+
+    def __init__(self, codes, scales):
+        self.codes = np.asarray(codes, dtype=np.uint8)
+        self.scales = np.asarray(scales, dtype=np.uint8)
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], IDX_DIM)
+
+    def __getitem__(self, sel):
+        return Fp4Keys(self.codes[sel], self.scales[sel])
+
+    def decode(self):
+        return index_key_decode_fp4(self.codes, self.scales)
+
+
+def index_key_quantize_fp4(k_bits):
+    """bf16 index keys [N, 128] -> FP4 codes uint8 [N, 64], scales uint8 [N, 4]."""
+    return quantize_fp4(bf16_bits_to_f64(k_bits), group=IDX_FP4_GROUP)
+
+
+def index_key_decode_fp4(codes, scales):
+    """FP4 index keys back to float64 [N, 128]."""
+    return dequantize_fp4(codes, scales, group=IDX_FP4_GROUP)
+
+
+def block_summary_fp4(codes, scales):
+    """Block keys (E4M3 [ceil(N/8), 128]) of FP4 index keys: the mean of the
+    members' decoded values, as their sum divided by the member count in
+    float32, rounded to E4M3.  (The decoded values are multiples of 2**-10
+    below 2**12 in magnitude, so float32 partial sums are exact while below
+    2**14; a block that reaches 2**14 has a mean beyond 448 in magnitude and
+    saturates either way.  The sum is formed in float32 in member order.)"""
+    k = index_key_decode_fp4(codes, scales).astype(np.float32)
+    N, D = k.shape
+    nb = (N + BLOCK_POS - 1) // BLOCK_POS
+    ssum = np.zeros((nb, D), dtype=np.float32)
+    for j in range(BLOCK_POS):
+        rows = np.arange(nb) * BLOCK_POS + j
+        ok = rows < N
+        ssum[ok] = ssum[ok] + k[rows[ok]]
+    count = np.minimum(BLOCK_POS, N - np.arange(nb) * BLOCK_POS).astype(np.float32)
+    return e4m3_rne_sat((ssum / count[:, None]).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
 # 5-7. indexer and top-k
 # ---------------------------------------------------------------------------
+
+
+def index_scores_dec(q, w, kd):
+    """I_t = sum_h w_h * max(0, q_h . k_t), all in float64, for decoded keys
+    kd float [N, 128].  q uint8 E4M3 [32, 128]; w float [32] or None (ones)."""
+    qd = e4m3_decode(q)
+    wd = np.ones(qd.shape[0]) if w is None else np.asarray(w, dtype=np.float64)
+    dots = qd @ np.asarray(kd, dtype=np.float64).T    # [32, N]
+    return (wd[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
 
 
 def index_scores(q, w, keys):
@@ -196,11 +269,14 @@ def index_scores(q, w, keys):
     q uint8 E4M3 [32, 128]; w float [32] or None (all ones); keys uint8 E4M3
     [N, 128].  Returns float64 [N].
     """
-    qd = e4m3_decode(q)
-    kd = e4m3_decode(keys)
-    wd = np.ones(qd.shape[0]) if w is None else np.asarray(w, dtype=np.float64)
-    dots = qd @ kd.T                                  # [32, N]
-    return (wd[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+    if isinstance(keys, Fp4Keys):
+        return index_scores_dec(q, w, keys.decode())
+    return index_scores_dec(q, w, e4m3_decode(keys))
+
+
+def index_scores_fp4(q, w, codes, scales):
+    """index_scores for FP4 index keys (codes [N, 64], scales [N, 4])."""
+    return index_scores_dec(q, w, index_key_decode_fp4(codes, scales))
 
 
 def topk_select(scores, ids, k):
