@@ -47,6 +47,8 @@ class IndexerArgs(ctypes.Structure):
         ("out_blocks", ctypes.c_void_p),
         ("cand_blocks", ctypes.c_void_p),
         ("n_cand_blocks", ctypes.c_int32),
+        ("key_format", ctypes.c_int32),
+        ("key_scales", ctypes.c_void_p),
     ]
 
 
@@ -75,6 +77,7 @@ class AttnArgs(ctypes.Structure):
 EXPORTS = (
     "csa2_abi_version", "csa2_status_string", "csa2_last_error",
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
+    "csa2_index_key_quantize", "csa2_index_block_summary_fp4",
     "csa2_indexer_topk_workspace", "csa2_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
@@ -103,6 +106,10 @@ def lib():
     L.csa2_kv_compress_quantize.argtypes = [vp, vp, i64, i64, i32, i64, vp, vp, i64, vp]
     L.csa2_index_block_summary.restype = i32
     L.csa2_index_block_summary.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+    L.csa2_index_key_quantize.restype = i32
+    L.csa2_index_key_quantize.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
+    L.csa2_index_block_summary_fp4.restype = i32
+    L.csa2_index_block_summary_fp4.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp]
     L.csa2_indexer_topk_workspace.restype = sz
     L.csa2_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
     L.csa2_indexer_topk.restype = i32
@@ -198,8 +205,37 @@ def index_block_summary(keys, summ=None, blk_begin=0, blk_end=None, stream=None)
     return summ
 
 
+def index_key_quantize(k, codes=None, scales=None, n_ent=None, out_seq_stride=0, stream=None):
+    """bf16 index keys [S, T, 128] -> FP4 codes uint8 [S, N, 64] and scales
+    uint8 [S, N, 4] (N = n_ent or T)."""
+    _dev(k, "k")
+    S, T = k.shape[0], k.shape[1]
+    N = T if n_ent is None else n_ent
+    if codes is None:
+        codes = torch.empty((S, N, 64), dtype=torch.uint8, device=k.device)
+    if scales is None:
+        scales = torch.empty((S, N, 4), dtype=torch.uint8, device=k.device)
+    _check(lib().csa2_index_key_quantize(_ptr(k), S, N, T, _ptr(codes), _ptr(scales), out_seq_stride,
+                                         _stream(stream)))
+    return codes, scales
+
+
+def index_block_summary_fp4(codes, scales, summ=None, blk_begin=0, blk_end=None, stream=None):
+    """FP4 index keys [S, N, 64] + [S, N, 4] -> E4M3 block keys [S, ceil(N/8), 128]."""
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    S, N = codes.shape[0], codes.shape[1]
+    nb = (N + 7) // 8
+    if summ is None:
+        summ = torch.empty((S, nb, 128), dtype=torch.uint8, device=codes.device)
+    blk_end = nb if blk_end is None else blk_end
+    _check(lib().csa2_index_block_summary_fp4(_ptr(codes), _ptr(scales), S, N, blk_begin, blk_end, _ptr(summ),
+                                              _stream(stream)))
+    return summ
+
+
 def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
-                    out_idx, out_score, out_blocks, cand_blocks=None):
+                    out_idx, out_score, out_blocks, cand_blocks=None, key_scales=None):
     a = IndexerArgs()
     a.n_rows = q.shape[0]
     a.n_seq = keys.shape[0]
@@ -219,30 +255,34 @@ def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_b
     a.out_blocks = _ptr(out_blocks)
     a.cand_blocks = _ptr(cand_blocks)
     a.n_cand_blocks = 0 if cand_blocks is None else cand_blocks.shape[1]
+    a.key_format = 0 if key_scales is None else 1
+    a.key_scales = _ptr(key_scales)
     return a
 
 
-def indexer_topk_workspace(q, keys, top_k, block_keys=None, keep_blocks=2048, cand=None, cand_blocks=None):
+def indexer_topk_workspace(q, keys, top_k, block_keys=None, keep_blocks=2048, cand=None, cand_blocks=None,
+                           key_scales=None):
     a = _indexer_struct(q, keys, top_k, None, None, None, block_keys, keep_blocks, cand,
-                        None, None, None, cand_blocks)
+                        None, None, None, cand_blocks, key_scales)
     return lib().csa2_indexer_topk_workspace(ctypes.byref(a))
 
 
 def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_keys=None,
                  keep_blocks=2048, cand=None, out_idx=None, out_score=None, out_blocks=None,
-                 workspace=None, stream=None, cand_blocks=None):
-    """q uint8 [R, 32, 128]; keys uint8 [S, N, 128].  Returns out_idx int32
+                 workspace=None, stream=None, cand_blocks=None, key_scales=None):
+    """q uint8 [R, 32, 128]; keys uint8 [S, N, 128] (E4M3), or FP4 codes
+    [S, N, 64] with key_scales uint8 [S, N, 4].  Returns out_idx int32
     [R, top_k] (ascending, -1 padded).  cand_blocks int32 [R, B]: select among
     the positions of these blocks (e.g. a Full layer's out_blocks)."""
     for t, nm in ((q, "q"), (keys, "keys"), (head_w, "head_w"), (row_seq, "row_seq"),
                   (n_valid, "n_valid"), (block_keys, "block_keys"), (cand, "cand"),
-                  (cand_blocks, "cand_blocks")):
+                  (cand_blocks, "cand_blocks"), (key_scales, "key_scales")):
         _dev(t, nm)
     R = q.shape[0]
     if out_idx is None:
         out_idx = torch.empty((R, top_k), dtype=torch.int32, device=q.device)
     a = _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
-                        out_idx, out_score, out_blocks, cand_blocks)
+                        out_idx, out_score, out_blocks, cand_blocks, key_scales)
     L = lib()
     need = L.csa2_indexer_topk_workspace(ctypes.byref(a))
     if workspace is None:

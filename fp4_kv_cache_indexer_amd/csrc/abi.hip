@@ -80,6 +80,11 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
     return fail(CSA2_EUNSUPPORTED, "indexer: top_k %d outside [1, %d]", a->top_k, CSA2_MAX_TOPK);
   if ((a->block_keys != nullptr) + (a->cand != nullptr) + (a->cand_blocks != nullptr) > 1)
     return fail(CSA2_EINVAL, "indexer: block_keys, cand and cand_blocks are exclusive");
+  if (a->key_format != CSA2_KEY_E4M3 && a->key_format != CSA2_KEY_FP4)
+    return fail(CSA2_EUNSUPPORTED, "indexer: key_format %d unknown", a->key_format);
+  if (check_ptrs && a->n_rows > 0 && a->key_format == CSA2_KEY_FP4 &&
+      (!a->key_scales || !aligned(a->key_scales, 4)))
+    return fail(CSA2_EINVAL, "indexer: FP4 keys need 4-byte aligned key_scales");
   if (a->n_rows > 0 && check_ptrs) {
     if (!a->q || !a->keys || !a->out_idx) return fail(CSA2_EINVAL, "indexer: q, keys and out_idx are required");
     if (!aligned(a->q, 16) || !aligned(a->keys, 16)) return fail(CSA2_EINVAL, "indexer: q/keys not 16-byte aligned");
@@ -272,6 +277,44 @@ int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_e
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "index_block_summary launch");
 }
 
+int32_t csa2_index_key_quantize(const void* k_bf16, int64_t n_seq, int64_t n_ent, int64_t k_seq_stride,
+                                uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, void* stream) {
+  g_err.clear();
+  if (n_seq < 0 || n_ent < 0) return fail(CSA2_EINVAL, "index_key_quantize: negative size");
+  if (k_seq_stride == 0) k_seq_stride = n_ent;
+  if (out_seq_stride == 0) out_seq_stride = n_ent;
+  if (k_seq_stride < n_ent || out_seq_stride < n_ent)
+    return fail(CSA2_EINVAL, "index_key_quantize: a sequence stride is below n_ent");
+  if (n_seq == 0 || n_ent == 0) return CSA2_OK;
+  if (!k_bf16 || !codes || !scales) return fail(CSA2_EINVAL, "index_key_quantize: NULL pointer");
+  if (!aligned(k_bf16, 16) || !aligned(codes, 16))
+    return fail(CSA2_EINVAL, "index_key_quantize: keys/codes not 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_KV_QUANT, s, [&] {
+    return csa2::launch_index_key_quantize(k_bf16, n_seq, n_ent, k_seq_stride, codes, scales, out_seq_stride, s);
+  });
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "index_key_quantize launch");
+}
+
+int32_t csa2_index_block_summary_fp4(const uint8_t* codes, const uint8_t* scales, int64_t n_seq,
+                                     int64_t n_ent, int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                     void* stream) {
+  g_err.clear();
+  if (n_seq < 0 || n_ent < 0) return fail(CSA2_EINVAL, "index_block_summary_fp4: negative size");
+  const int64_t nb = (n_ent + CSA2_BLOCK_POS - 1) / CSA2_BLOCK_POS;
+  if (blk_begin < 0 || blk_end < blk_begin || blk_end > nb)
+    return fail(CSA2_EINVAL, "index_block_summary_fp4: block range [%lld, %lld) outside [0, %lld)",
+                (long long)blk_begin, (long long)blk_end, (long long)nb);
+  if (n_seq == 0 || blk_end == blk_begin) return CSA2_OK;
+  if (!codes || !scales || !summ) return fail(CSA2_EINVAL, "index_block_summary_fp4: NULL pointer");
+  if (!aligned(codes, 4) || !aligned(summ, 4)) return fail(CSA2_EINVAL, "index_block_summary_fp4: misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_BLOCK_SUMMARY, s, [&] {
+    return csa2::launch_block_summary_fp4(codes, scales, n_seq, n_ent, blk_begin, blk_end, summ, s);
+  });
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "index_block_summary_fp4 launch");
+}
+
 size_t csa2_indexer_topk_workspace(const csa2_indexer_args* a) {
   IndexerPlan p;
   if (check_indexer(a, &p, false) != CSA2_OK) return 0;
@@ -302,6 +345,8 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   sa.n_seq = a->n_seq;
   sa.q = a->q;
   sa.w = a->head_w;
+  sa.key_fp4 = a->key_format == CSA2_KEY_FP4;
+  sa.key_scales = a->key_scales;
 
   csa2::SelectArgs se{};
   se.n_rows = a->n_rows;

@@ -41,6 +41,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return s ? -mag : mag;
 }
 
+// E2M1 code (sign bit 3, magnitude index 0..7) -> float32, exact.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+  const float mag = m < 4u ? 0.5f * (float)m : (float)(2u << ((m - 4u) >> 1)) * (1.0f + 0.5f * (float)(m & 1u));
+  return (c & 8u) ? -mag : mag;
+}
+
 // Round a finite float32 to E4M3FN: nearest, ties to even, saturate at +-448,
 // zero results encoded as +0.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {

@@ -11,6 +11,12 @@ hipError_t launch_kv_compress_quantize(const void* x, const void* z, int64_t n_s
                                        int32_t m, int64_t x_seq_stride, uint8_t* codes,
                                        uint8_t* scales, int64_t out_seq_stride, hipStream_t stream);
 
+hipError_t launch_index_key_quantize(const void* k, int64_t n_seq, int64_t n_ent, int64_t k_seq_stride,
+                                     uint8_t* codes, uint8_t* scales, int64_t out_seq_stride,
+                                     hipStream_t stream);
+hipError_t launch_block_summary_fp4(const uint8_t* codes, const uint8_t* scales, int64_t n_seq,
+                                    int64_t n_ent, int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                    hipStream_t stream);
 hipError_t launch_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_ent,
                                 int64_t blk_begin, int64_t blk_end, uint8_t* summ,
                                 hipStream_t stream);
@@ -46,6 +52,8 @@ struct ScoreArgs {
   int64_t n_seq;
   const int32_t* row_seq;
   const uint8_t* keys;      // key rows (index keys, or block keys in kItemsBlocks mode)
+  const uint8_t* key_scales;// FP4 index keys: [S][seq_rows][4] E4M3 scales
+  int32_t key_fp4;          // index keys are FP4 (codes in `keys`, 64 B per row)
   int64_t seq_rows;         // key rows per sequence in `keys`
   const uint8_t* q;         // [R][32][128]
   const float* w;           // [R][32] or null

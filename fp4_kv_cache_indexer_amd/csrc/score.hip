@@ -42,6 +42,18 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
   return v;
 }
 
+// 8 FP4 channels (one word, channel 2j in the low nibble of byte j) times
+// their E4M3 scale, as fp16: the unit-scale hardware decode is exact and the
+// product has at most 6 significant bits within [2^-10, 2688], so it is exact.
+__device__ __forceinline__ v8h fp4x8_to_f16(uint32_t w, _Float16 s) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  const v8h v = v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return v * s;
+}
+
 // 8 E4M3 bytes (two words, byte order = element order) widened to fp16.
 __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
   const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w0, 1.0f, false);
@@ -56,7 +68,9 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
 // G > 0: the chunk is exactly G groups per wave and the group loop is fully
 // unrolled (straight-line code lets the compiler keep the next group's loads
 // in flight exactly); G == 0: runtime trip count.
-template <int MODE, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0>
+// KF: key format, 0 = E4M3 (128 B per key), 1 = FP4 (64 B of codes + a
+// 4-byte word of E4M3 scales, one per 32 channels).
+template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0>
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
   __shared__ uint32_t hist[kHistBins];
@@ -72,7 +86,11 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t seq = row_seq_of(a.im, r);
-  const uint8_t* kbase = a.keys + seq * a.seq_rows * kIdxDim + g * 32;
+  // lane (n, g) owns channels 32g .. 32g+31 of key n: 32 E4M3 bytes, or 16
+  // FP4 code bytes and the scale word (byte g)
+  constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
+  const uint8_t* kbase = a.keys + seq * a.seq_rows * kKeyBytes + g * (KF ? 16 : 32);
+  const uint8_t* sbase = KF ? a.key_scales + seq * a.seq_rows * 4 : nullptr;
 
   // MFMA A operands: indexer query rows n and 16+n, bytes [32g, 32g+32), as
   // four fp16 k-slices of 8.  The B operand (keys) uses the same byte split,
@@ -110,7 +128,14 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     for (int u = 0; u < U; ++u) {
       const int64_t item = c0 + (t0 + u) * 16 + n;
       pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
-      kb[u] = load32(kbase + (int64_t)(pos[u] >= 0 ? pos[u] : safe_pos) * kIdxDim);
+      const int64_t p = pos[u] >= 0 ? pos[u] : safe_pos;
+      if (KF) {
+        const uint4 c = *reinterpret_cast<const uint4*>(kbase + p * kKeyBytes);
+        kb[u][0] = c.x; kb[u][1] = c.y; kb[u][2] = c.z; kb[u][3] = c.w;
+        kb[u][4] = *reinterpret_cast<const uint32_t*>(sbase + p * 4);
+      } else {
+        kb[u] = load32(kbase + p * kKeyBytes);
+      }
     }
   };
   auto compute_group = [&](int64_t t0, const v8i* kb) {
@@ -121,9 +146,12 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       for (int u = 0; u < 4; ++u) {
         // D[h][entry] = sum_k q[h][k] * key[entry][k]; lane: entry n, heads 4g+i
         v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        _Float16 ksc = (_Float16)0.0f;
+        if (KF) ksc = (_Float16)e4m3_to_f32(((uint32_t)kb[u4 + u][4] >> (8 * g)) & 0xFFu);   // exact
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const v8h kh = fp8x8_to_f16(kb[u4 + u][2 * v], kb[u4 + u][2 * v + 1]);
+          const v8h kh = KF ? fp4x8_to_f16((uint32_t)kb[u4 + u][v], ksc)
+                            : fp8x8_to_f16(kb[u4 + u][2 * v], kb[u4 + u][2 * v + 1]);
           d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa0[v], kh, d0, 0, 0, 0);
           d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa1[v], kh, d1, 0, 0, 0);
         }
@@ -206,7 +234,7 @@ int score_resident_wgs() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_score_kernel<kItemsBlocks, kScoreDB, kScoreMinW>,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_score_kernel<kItemsBlocks, 0, kScoreDB, kScoreMinW>,
                                                    kScoreThreads, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     (void)hipGetLastError();
@@ -220,12 +248,19 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.im.n_items == 0) return hipSuccess;
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
   const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
-  switch (a.im.mode) {
-    case kItemsFlat: hipLaunchKernelGGL((index_score_kernel<kItemsFlat, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    case kItemsBlocks: hipLaunchKernelGGL((index_score_kernel<kItemsBlocks, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    case kItemsPool: hipLaunchKernelGGL((index_score_kernel<kItemsPool, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((index_score_kernel<kItemsCand, kScoreDB, kScoreMinW>), grid, block, 0, stream, a); break;
+#define CSA2_SCORE(MM, KK) \
+  hipLaunchKernelGGL((index_score_kernel<MM, KK, kScoreDB, kScoreMinW>), grid, block, 0, stream, a)
+  if (a.im.mode == kItemsBlocks) CSA2_SCORE(kItemsBlocks, 0);      // block summaries are E4M3
+  else if (a.key_fp4) {
+    if (a.im.mode == kItemsFlat) CSA2_SCORE(kItemsFlat, 1);
+    else if (a.im.mode == kItemsPool) CSA2_SCORE(kItemsPool, 1);
+    else CSA2_SCORE(kItemsCand, 1);
+  } else {
+    if (a.im.mode == kItemsFlat) CSA2_SCORE(kItemsFlat, 0);
+    else if (a.im.mode == kItemsPool) CSA2_SCORE(kItemsPool, 0);
+    else CSA2_SCORE(kItemsCand, 0);
   }
+#undef CSA2_SCORE
   return hipGetLastError();
 }
 

@@ -125,6 +125,31 @@ int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_e
                                  void* stream);
 
 /*
+ * FP4 index keys [daiw "four generations" table: 890 B/token of global
+ * cache = 2.5 entries/token x (288 B main entry + 68 B index key)]: each
+ * 128-dim key is stored as 128 E2M1 codes (64 B, channel 2j in the low nibble
+ * of byte j) and one E4M3 scale per 32 channels (4 B), quantised by the
+ * main-KV rule (scale = E4M3(amax/6), nearest grid point, ties to the even
+ * code, saturate at 6*scale, no -0).
+ *   k_bf16       : bf16 [n_seq][k_seq_stride][128]; k_seq_stride 0 = n_ent
+ *   codes        : uint8 [n_seq][out_seq_stride][64]   (16-byte aligned)
+ *   scales       : uint8 [n_seq][out_seq_stride][4];   out_seq_stride 0 = n_ent
+ * The indexer reads them with key_format = CSA2_KEY_FP4.
+ */
+int32_t csa2_index_key_quantize(const void* k_bf16, int64_t n_seq, int64_t n_ent, int64_t k_seq_stride,
+                                uint8_t* codes, uint8_t* scales, int64_t out_seq_stride, void* stream);
+
+/*
+ * Block summaries of FP4 index keys: as csa2_index_block_summary, from the
+ * decoded FP4 members (float32 mean, E4M3 rounding; E4M3 block keys).
+ *   codes : uint8 [n_seq][n_ent][64];  scales : uint8 [n_seq][n_ent][4]
+ *   summ  : uint8 [n_seq][ceil(n_ent/8)][128]
+ */
+int32_t csa2_index_block_summary_fp4(const uint8_t* codes, const uint8_t* scales, int64_t n_seq,
+                                     int64_t n_ent, int64_t blk_begin, int64_t blk_end, uint8_t* summ,
+                                     void* stream);
+
+/*
  * Indexer + top-k [0539edu §3, csa2.indexer and its hierarchical block].
  *
  * Row r scores entries of sequence row_seq[r] (r if NULL) that are visible to
@@ -179,7 +204,15 @@ typedef struct {
                                ascending, -1 padded), or NULL                   */
   const int32_t* cand_blocks;/* [R][n_cand_blocks] block ids, or NULL           */
   int32_t n_cand_blocks;    /* blocks per row when cand_blocks != NULL          */
+  int32_t key_format;       /* CSA2_KEY_E4M3 (keys [S][N][128]) or CSA2_KEY_FP4
+                               (keys = codes [S][N][64], key_scales [S][N][4],
+                               see csa2_index_key_quantize); block_keys are
+                               E4M3 in both                                     */
+  const uint8_t* key_scales;/* FP4 keys: [S][N][4] E4M3 scales, else NULL       */
 } csa2_indexer_args;
+
+#define CSA2_KEY_E4M3 0
+#define CSA2_KEY_FP4 1
 
 /* Workspace bytes csa2_indexer_topk needs for these arguments (0 on error).
  * Reads only the sizes and which of block_keys/cand/cand_blocks are set; data pointers

@@ -79,6 +79,9 @@ def test_indexer_validation_without_gpu():
         (dict(cb, block_keys=ctypes.c_void_p(0x4000)), 1, True),
         (dict(cand_blocks=ctypes.c_void_p(0x6000), n_cand_blocks=0), 1, True),
         (dict(cand_blocks=ctypes.c_void_p(0x6002), n_cand_blocks=4), 1, False),
+        (dict(key_format=7), 2, True),
+        (dict(key_format=1), 1, False),                                  # FP4 without scales
+        (dict(key_format=1, key_scales=ctypes.c_void_p(0x7002)), 1, False),
     ]
     for kw, status, ws_fails in cases:
         a = _idx_args(**kw)
@@ -127,3 +130,12 @@ def test_attn_and_cache_write_validation_without_gpu():
     assert L.csa2_kv_compress_quantize(p, None, 0, 16, 2, 0, p, p, 0, None) == 0   # nothing to do
     assert L.csa2_index_block_summary(p, 1, 17, 0, 4, p, None) == 1               # 3 blocks only
     assert L.csa2_index_block_summary(p, 1, 17, 2, 2, p, None) == 0
+    # FP4 index keys: sizes, strides and alignment are checked before any launch
+    assert L.csa2_index_key_quantize(p, -1, 8, 0, p, p, 0, None) == 1
+    assert L.csa2_index_key_quantize(p, 2, 8, 7, p, p, 0, None) == 1              # stride < n_ent
+    assert L.csa2_index_key_quantize(None, 2, 8, 0, p, p, 0, None) == 1
+    assert L.csa2_index_key_quantize(ctypes.c_void_p(0x1008), 2, 8, 0, p, p, 0, None) == 1
+    assert L.csa2_index_key_quantize(None, 0, 8, 0, None, None, 0, None) == 0      # nothing to do
+    assert L.csa2_index_block_summary_fp4(p, p, 1, 17, 0, 4, p, None) == 1         # 3 blocks only
+    assert L.csa2_index_block_summary_fp4(None, p, 1, 17, 0, 3, p, None) == 1
+    assert L.csa2_index_block_summary_fp4(p, p, 1, 17, 1, 1, p, None) == 0

@@ -330,6 +330,120 @@ def test_indexer_workspace_reuse():
 
 
 # ---------------------------------------------------------------------------
+# FP4 index keys (128 E2M1 + one E4M3 scale per 32 channels)
+# ---------------------------------------------------------------------------
+
+
+def fp4_key_case(seed, S, N):
+    """bf16 index keys with edge groups (zero, tiny, huge, mixed), their
+    oracle FP4 encoding (the input both sides score from)."""
+    g = np.random.default_rng(seed)
+    k = (g.standard_normal((S, N, 128)) * np.exp(g.uniform(-2, 2, (S, N, 1)))).astype(np.float32)
+    k[0, 0] = 0.0
+    k[0, 1, :32] = 1e-30
+    k[0, 2, 32:64] = 3.0e38
+    k[0, 3, 96:] = [1e-38] * 16 + [-2e-38] * 16
+    kb = synth.to_bf16_bits(k)
+    enc = [O.index_key_quantize_fp4(kb[s]) for s in range(S)]
+    codes = np.stack([e[0] for e in enc])
+    scales = np.stack([e[1] for e in enc])
+    return kb, codes, scales
+
+
+def test_index_key_quantize():
+    say("index_key_quantize: S=2 N=5003 bf16 keys -> FP4 (bit-exact)")
+    kb, codes, scales = fp4_key_case(41, 2, 5003)
+    gc, gs = C.index_key_quantize(dev(kb))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gc), codes) and np.array_equal(host(gs), scales)
+
+
+@pytest.mark.parametrize("N", [4096, 4093, 8, 5])
+def test_block_summary_fp4(N):
+    say(f"block_summary_fp4 N={N}")
+    _, codes, scales = fp4_key_case(42 + N, 3, N)
+    summ = C.index_block_summary_fp4(dev(codes), dev(scales))
+    torch.cuda.synchronize()
+    gs = host(summ)
+    for s in range(3):
+        assert np.array_equal(gs[s], O.block_summary_fp4(codes[s], scales[s])), s
+
+
+def fp4_idx_case(seed, S, N, R, **kw):
+    case = idx_case(seed, S, N, R, **kw)
+    _, codes, scales = fp4_key_case(seed + 100, S, N)
+    case["codes"], case["kscales"] = codes, scales
+    case["keys"] = None
+    return case
+
+
+def check_fp4_rows(case, gi, gsc, k, pool_of=None):
+    R = case["q"].shape[0]
+    for r in range(R):
+        s = r if case["row_seq"] is None else int(case["row_seq"][r])
+        N = case["codes"].shape[1]
+        nv = N if case["n_valid"] is None else int(case["n_valid"][r])
+        keys = O.Fp4Keys(case["codes"][s], case["kscales"][s])
+        ids = np.arange(nv) if pool_of is None else pool_of(r, nv)
+        sc = O.index_scores(case["q"][r], case["w"][r], keys[ids])
+        ref = O.topk_select(sc, ids, k)
+        check_topk(gi[r], ref, ids, sc, k, f"row {r}")
+        sel = gi[r][gi[r] >= 0]
+        if len(sel):
+            sfull = dict(zip(ids.tolist(), sc.tolist()))
+            want = np.array([sfull[int(x)] for x in sel])
+            err = np.abs(gsc[r][:len(sel)] - want)
+            assert np.all(err <= 2e-6 * np.abs(want) + 1e-5), f"row {r} scores"
+
+
+def run_fp4_indexer(case, k, **kw):
+    R = case["q"].shape[0]
+    out_score = torch.empty((R, k), dtype=torch.float32, device="cuda")
+    args = dict(head_w=dev(case["w"]), key_scales=dev(case["kscales"]), out_score=out_score)
+    if case.get("row_seq") is not None:
+        args["row_seq"] = dev(case["row_seq"].astype(np.int32))
+    if case.get("n_valid") is not None:
+        args["n_valid"] = dev(case["n_valid"].astype(np.int32))
+    args.update(kw)
+    idx = C.indexer_topk(dev(case["q"]), dev(case["codes"]), k, **args)
+    torch.cuda.synchronize()
+    return host(idx), host(out_score)
+
+
+def test_indexer_fp4_keys_flat():
+    say("indexer with FP4 keys, flat: S=3 R=5 ragged, k=512")
+    case = fp4_idx_case(43, 3, 7000, 5, row_seq=np.array([0, 1, 2, 0, 2]),
+                        n_valid=np.array([7000, 300, 6999, 4097, 0]))
+    gi, gsc = run_fp4_indexer(case, 512)
+    check_fp4_rows(case, gi, gsc, 512)
+
+
+def test_indexer_fp4_keys_hierarchical_and_block_pool():
+    say("indexer with FP4 keys: hierarchical (summaries from FP4 keys) and block pool")
+    case = fp4_idx_case(44, 2, 20003, 3, row_seq=np.array([0, 1, 1]), n_valid=np.array([20003, 20003, 9001]))
+    summ = C.index_block_summary_fp4(dev(case["codes"]), dev(case["kscales"]))
+    blocks = torch.empty((3, 300), dtype=torch.int32, device="cuda")
+    gi, gsc = run_fp4_indexer(case, 512, block_keys=summ, keep_blocks=300, out_blocks=blocks)
+    gb = host(blocks)
+    for r in range(3):
+        s, nv = int(case["row_seq"][r]), int(case["n_valid"][r])
+        keys = O.Fp4Keys(case["codes"][s], case["kscales"][s])
+        bk = O.block_summary(keys)
+        ref_idx, ref_blocks = O.indexer_topk_hier(case["q"][r], case["w"][r], keys, bk, 512, nv, 300)
+        nb = (nv + 7) // 8
+        sb = O.index_scores(case["q"][r], case["w"][r], bk[:nb])
+        check_topk(gb[r], ref_blocks, np.arange(nb), sb, 300, f"row {r} blocks")
+        if np.array_equal(gb[r], ref_blocks):
+            pool = O.pool_positions(ref_blocks, nv)
+            sc = O.index_scores(case["q"][r], case["w"][r], keys[pool])
+            check_topk(gi[r], ref_idx, pool, sc, 512, f"row {r} fine")
+    # the Full layer's pool, rescored by a new query over FP4 keys
+    case2 = dict(case, q=idx_case(45, 2, 8, 3)["q"])
+    gi2, gsc2 = run_fp4_indexer(case2, 256, cand_blocks=blocks)
+    check_fp4_rows(case2, gi2, gsc2, 256, pool_of=lambda r, nv: O.pool_positions(gb[r], nv))
+
+
+# ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
 
