@@ -37,6 +37,7 @@ from fp4_kv_cache_indexer_amd import synth  # noqa: E402
 
 METRIC = "decode sparse-attn queries/sec at 1M ctx; indexer HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0     # dense bf16/fp16
 
 WORKLOADS = {
     # the configuration the metric is quoted on
@@ -61,6 +62,10 @@ WORKLOADS = {
                    B=64, N=262144, H=64, k=512, keep=2048, hier=True, m=1, dist="normal", pool=True,
                    layers=("full", "reuse", "reuse", "reuse", "reindex", "reuse", "reuse", "reuse")),
 }
+# the same workloads with FP4 index keys (64 code bytes + 4 E4M3 group scales per entry)
+for _name in ("c3", "c4"):
+    WORKLOADS[_name + "fp4"] = dict(WORKLOADS[_name], key="fp4",
+                                    desc=WORKLOADS[_name]["desc"] + "; FP4 index keys (68 B/entry)")
 
 
 def layers_of(w):
@@ -84,10 +89,22 @@ class InputSet:
                 self.x0 = x[0]                       # kept for the oracle baseline
                 self.z0 = None if z is None else z[0]
             del x, z
-        self.keys = torch.empty((B, N, 128), dtype=torch.uint8, device="cuda")
-        for b in range(B):
-            self.keys[b] = synth.to_e4m3(torch.randn((N, 128), generator=g, device="cuda"))
-        self.summ = C.index_block_summary(self.keys) if w["hier"] else None
+        self.fp4 = w.get("key") == "fp4"
+        if self.fp4:
+            self.keys = torch.empty((B, N, 64), dtype=torch.uint8, device="cuda")
+            self.kscales = torch.empty((B, N, 4), dtype=torch.uint8, device="cuda")
+            for b in range(B):
+                kb = torch.randn((1, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+                C.index_key_quantize(kb, codes=self.keys[b:b + 1], scales=self.kscales[b:b + 1])
+                del kb
+            self.k_new = torch.randn((B, 1, 128), generator=g, device="cuda").to(torch.bfloat16)
+            self.summ = C.index_block_summary_fp4(self.keys, self.kscales) if w["hier"] else None
+        else:
+            self.keys = torch.empty((B, N, 128), dtype=torch.uint8, device="cuda")
+            for b in range(B):
+                self.keys[b] = synth.to_e4m3(torch.randn((N, 128), generator=g, device="cuda"))
+            self.kscales = None
+            self.summ = C.index_block_summary(self.keys) if w["hier"] else None
         self.swa = synth.to_e4m3(synth.latent_dev((B, 128, 512), g, w["dist"]))
         self.swa_len = torch.full((B,), 128, dtype=torch.int32, device="cuda")
         self.q_idx = synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
@@ -107,12 +124,14 @@ class InputSet:
         self.idx2 = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
         self.ws_idx2 = torch.zeros(max(256, C.indexer_topk_workspace(
             self.q_idx, self.keys, w["k"], block_keys=None if self.pool else self.summ,
-            keep_blocks=w["keep"] or 2048, cand_blocks=self.blocks)), dtype=torch.uint8, device="cuda")
+            keep_blocks=w["keep"] or 2048, cand_blocks=self.blocks, key_scales=self.kscales)),
+            dtype=torch.uint8, device="cuda")
         self.idx = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
         self.ws_idx = torch.zeros(max(256, C.indexer_topk_workspace(
-            self.q_idx, self.keys, w["k"], block_keys=self.summ, keep_blocks=w["keep"] or 2048)),
+            self.q_idx, self.keys, w["k"], block_keys=self.summ, keep_blocks=w["keep"] or 2048,
+            key_scales=self.kscales)),
             dtype=torch.uint8, device="cuda")
         need = C.sparse_attn_workspace(self.q, self.idx, swa=self.swa, swa_len=self.swa_len, codes=self.codes)
         self.ws_attn = torch.empty(max(256, need), dtype=torch.uint8, device="cuda")
@@ -124,10 +143,15 @@ def step(w, s):
     # a0: the newest entry (m tokens pooled; m = 1 in the decoder layers)
     C.kv_compress_quantize(s.x_new, w["m"], gate=s.z_new, codes=s.codes[:, N - 1:],
                            scales=s.scales[:, N - 1:], out_seq_stride=N)
+    if s.fp4:                  # ... and its index key, quantized to FP4
+        C.index_key_quantize(s.k_new, codes=s.keys[:, N - 1:], scales=s.kscales[:, N - 1:], out_seq_stride=N)
     # a1: refresh the summary of the block holding that entry
     if w["hier"]:
         b = (N - 1) // 8
-        C.index_block_summary(s.keys, summ=s.summ, blk_begin=b, blk_end=b + 1)
+        if s.fp4:
+            C.index_block_summary_fp4(s.keys, s.kscales, summ=s.summ, blk_begin=b, blk_end=b + 1)
+        else:
+            C.index_block_summary(s.keys, summ=s.summ, blk_begin=b, blk_end=b + 1)
     idx = None
     for L, mode in enumerate(layers_of(w)):
         # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context); a7:
@@ -135,15 +159,15 @@ def step(w, s):
         # the Full layer's pool when the workload says so)
         if mode == "full":
             C.indexer_topk(s.lq_idx[L], s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
-                           out_idx=s.idx, out_blocks=s.blocks, workspace=s.ws_idx)
+                           out_idx=s.idx, out_blocks=s.blocks, workspace=s.ws_idx, key_scales=s.kscales)
             idx = s.idx
         elif mode == "reindex":
             if s.pool:
                 C.indexer_topk(s.lq_idx[L], s.keys, w["k"], cand_blocks=s.blocks, out_idx=s.idx2,
-                               workspace=s.ws_idx2)
+                               workspace=s.ws_idx2, key_scales=s.kscales)
             else:
                 C.indexer_topk(s.lq_idx[L], s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
-                               out_idx=s.idx2, workspace=s.ws_idx2)
+                               out_idx=s.idx2, workspace=s.ws_idx2, key_scales=s.kscales)
             idx = s.idx2
         # a4-a6: gather + dequant + joint sparse/window attention
         C.sparse_attn_decode(s.lq[L], s.codes, s.scales, idx, swa=s.lswa[L], swa_len=s.swa_len, out=s.out,
@@ -239,10 +263,33 @@ def copy_probe(mib):
 
 def scan_bytes(w):
     """Algorithmic HBM bytes of one launch of the dominant kernel (the
-    indexer scan): the key rows it must read plus queries and weights."""
+    indexer scan): the key rows it must read plus queries and weights.  The
+    coarse scan reads E4M3 block keys (128 B); a flat scan reads E4M3 keys or
+    FP4 keys (64 code bytes + 4 scale bytes)."""
     B, N = w["B"], w["N"]
     rows = (N + 7) // 8 if w["hier"] else N
-    return B * (rows * 128 + 32 * 128 + 32 * 4)
+    row_bytes = 68 if (w.get("key") == "fp4" and not w["hier"]) else 128
+    return B * (rows * row_bytes + 32 * 128 + 32 * 4)
+
+
+def attn_flops(w):
+    """Algorithmic flops of one attention launch: QK^T and PV over the
+    selected entries and the window, 2 * 2 * H * (k + 128) * 512 per query."""
+    return w["B"] * 4 * w["H"] * (w["k"] + 128) * 512
+
+
+def stall_calibrate(seconds):
+    """Cycles for torch.cuda._sleep that keep the stream busy for about
+    `seconds` (measured once with events)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 1 << 20
+    torch.cuda._sleep(cyc)
+    e0.record()
+    torch.cuda._sleep(cyc)
+    e1.record()
+    torch.cuda.synchronize()
+    per_s = cyc / (e0.elapsed_time(e1) / 1e3)
+    return max(1, int(per_s * seconds))
 
 
 def cpu_baseline(w, s, seconds):
@@ -256,6 +303,8 @@ def cpu_baseline(w, s, seconds):
     N, H, k, m = w["N"], w["H"], w["k"], w["m"]
     layers = layers_of(w)
     keys = s.keys[0].cpu().numpy()
+    if s.fp4:
+        keys = O.Fp4Keys(keys, s.kscales[0].cpu().numpy())
     x0 = s.x0.view(torch.int16).cpu().numpy().view(np.uint16)
     z0 = None if s.z0 is None else s.z0.view(torch.int16).cpu().numpy().view(np.uint16)
     swa = s.swa[0].cpu().numpy()
@@ -267,8 +316,11 @@ def cpu_baseline(w, s, seconds):
         q_idx = [synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32)) for _ in layers]
         q = [torch.from_numpy(g.standard_normal((H, 512)).astype(np.float32)).to(torch.bfloat16)
              .view(torch.int16).numpy().view(np.uint16) for _ in layers]
+        k_new = synth.to_bf16_bits(g.standard_normal((1, 128)).astype(np.float32)) if s.fp4 else None
         ts = time.perf_counter()
         O.kv_compress_quantize(x0[-m:], None if z0 is None else z0[-m:], m)   # a0: the new entry
+        if s.fp4:
+            O.index_key_quantize_fp4(k_new)                             # ... and its index key
         if w["hier"]:
             O.block_summary(keys[(N - 1) // 8 * 8:])                   # a1: its block
         idx = kept = None
@@ -378,15 +430,30 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {qps:.0f} queries/s",
           file=sys.stderr, flush=True)
 
+    # per-kernel durations from HIP events recorded around one launch site.
+    # Eager steps follow a stall kernel on the same stream, so the launches
+    # are queued before the GPU reaches them and the events see the kernel,
+    # not the host's launch gaps.
+    stall_cycles = stall_calibrate(300e-6)
+
+    def time_site(site):
+        C.kernel_timer_start(site, args.steps * len(layers_of(w)))
+        for i in range(args.steps):
+            torch.cuda._sleep(stall_cycles)
+            step(w, sets[i % len(sets)])
+        n_l, tot_ms = C.kernel_timer_stop()
+        return n_l, tot_ms / max(1, n_l) / 1e3
+
     # dominant kernel: the indexer scan (coarse stage when hierarchical)
     site = "score_coarse" if w["hier"] else "score_flat"
-    C.kernel_timer_start(site, args.steps)
-    for i in range(args.steps):
-        step(w, sets[i % len(sets)])
-    n_l, tot_ms = C.kernel_timer_stop()
-    avg_s = tot_ms / max(1, n_l) / 1e3
+    n_l, avg_s = time_site(site)
     achieved = scan_bytes(w) / avg_s / 1e9
     print(f"[bench] {site}: {n_l} launches, avg {avg_s * 1e6:.2f} us, {achieved:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+    # the attention contraction against the bf16 MFMA peak
+    n_a, avg_a = time_site("attn")
+    attn_tf = attn_flops(w) / avg_a / 1e12
+    print(f"[bench] attn: {n_a} launches, avg {avg_a * 1e6:.2f} us, {attn_tf:.1f} TFLOP/s algorithmic",
           file=sys.stderr, flush=True)
 
     if args.copy_probe_mib > 0:
@@ -408,6 +475,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"index_score_kernel ({site})", "avg_us": round(avg_s * 1e6, 3),
                      "bytes_per_launch": scan_bytes(w)},
+        "roofline_attn": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
+                          "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                          "kernel": "sparse_attn_kernel", "avg_us": round(avg_a * 1e6, 3),
+                          "flops_per_launch": attn_flops(w)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

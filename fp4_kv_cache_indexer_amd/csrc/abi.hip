@@ -476,8 +476,10 @@ int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
     return fail(CSA2_EINVAL, "kernel_timer_start: max_launches %d outside [1, 1e6]", max_launches);
   const size_t need = 2 * (size_t)max_launches;
   while (g_timer.ev.size() < need) {
+    // timing only: no system-scope fence around the kernel being measured
+    // (callers synchronise through their own stream or device calls)
     hipEvent_t ev;
-    hipError_t e = hipEventCreate(&ev);
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
     if (e != hipSuccess) return hip_fail(e, "kernel_timer_start: hipEventCreate");
     g_timer.ev.push_back(ev);
   }

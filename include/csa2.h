@@ -281,7 +281,9 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
  * csa2_kernel_timer_start(site, max_launches) arms a timer on one launch
  * site: each of the next `max_launches` launches made from that site is
  * bracketed by two HIP events recorded on the stream the kernel is launched
- * on.  csa2_kernel_timer_stop() waits for those events, returns how many
+ * on (created with hipEventDisableSystemFence: they order nothing beyond the
+ * stream and only measure).  csa2_kernel_timer_stop() waits for those events,
+ * returns how many
  * launches were timed and their summed duration in milliseconds, and
  * disarms the timer.  One timer per process; arm it outside HIP graph
  * capture.  Sites:
