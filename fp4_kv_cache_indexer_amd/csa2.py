@@ -52,6 +52,30 @@ class IndexerArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_rows", ctypes.c_int32),
+        ("n_seq", ctypes.c_int64),
+        ("row_seq", ctypes.c_void_p),
+        ("pos", ctypes.c_void_p),
+        ("m", ctypes.c_int32),
+        ("x_bf16", ctypes.c_void_p),
+        ("gate_bf16", ctypes.c_void_p),
+        ("pend_x", ctypes.c_void_p),
+        ("pend_gate", ctypes.c_void_p),
+        ("n_ent", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("key_bf16", ctypes.c_void_p),
+        ("key_format", ctypes.c_int32),
+        ("keys", ctypes.c_void_p),
+        ("key_scales", ctypes.c_void_p),
+        ("block_keys", ctypes.c_void_p),
+        ("swa", ctypes.c_void_p),
+        ("swa_cap", ctypes.c_int32),
+    ]
+
+
 class AttnArgs(ctypes.Structure):
     _fields_ = [
         ("n_rows", ctypes.c_int32),
@@ -77,14 +101,16 @@ class AttnArgs(ctypes.Structure):
 EXPORTS = (
     "csa2_abi_version", "csa2_status_string", "csa2_last_error",
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
-    "csa2_index_key_quantize", "csa2_index_block_summary_fp4",
+    "csa2_index_key_quantize", "csa2_index_block_summary_fp4", "csa2_decode_append",
     "csa2_indexer_topk_workspace", "csa2_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
 )
 
+KEY_E4M3, KEY_FP4 = 0, 1          # index-key formats (CSA2_KEY_*)
+
 SITES = dict(kv_quant=1, block_summary=2, score_flat=3, score_coarse=4, score_pool=5,
-             score_cand=6, select=7, attn=8, attn_combine=9, filter=10)
+             score_cand=6, select=7, attn=8, attn_combine=9, filter=10, append=11)
 
 
 def lib():
@@ -110,6 +136,8 @@ def lib():
     L.csa2_index_key_quantize.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
     L.csa2_index_block_summary_fp4.restype = i32
     L.csa2_index_block_summary_fp4.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp]
+    L.csa2_decode_append.restype = i32
+    L.csa2_decode_append.argtypes = [ctypes.POINTER(AppendArgs), vp]
     L.csa2_indexer_topk_workspace.restype = sz
     L.csa2_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
     L.csa2_indexer_topk.restype = i32
@@ -234,6 +262,42 @@ def index_block_summary_fp4(codes, scales, summ=None, blk_begin=0, blk_end=None,
     return summ
 
 
+def decode_append(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None, pend_gate=None,
+                  key_scales=None, block_keys=None, swa=None, row_seq=None, stream=None):
+    """Append one token per row (x: bf16 [R, 512], pos: int64 [R]) to the
+    caches of sequences row_seq (identity when None): window ring slot
+    pos % swa_cap, the pending group for m > 1, and when a group completes
+    entry pos // m (codes/scales), its index key (key: bf16 [R, 128]; E4M3
+    keys [S, N, 128] or FP4 keys [S, N, 64] with key_scales [S, N, 4]) and
+    the summary of its block (block_keys [S, ceil(N/8), 128])."""
+    for name, t in (("x", x), ("pos", pos), ("codes", codes), ("scales", scales), ("key", key),
+                    ("keys", keys), ("gate", gate), ("pend_x", pend_x), ("pend_gate", pend_gate),
+                    ("key_scales", key_scales), ("block_keys", block_keys), ("swa", swa),
+                    ("row_seq", row_seq)):
+        _dev(t, name)
+    a = AppendArgs()
+    a.n_rows = x.shape[0]
+    a.n_seq = codes.shape[0]
+    a.row_seq = _ptr(row_seq)
+    a.pos = _ptr(pos)
+    a.m = m
+    a.x_bf16 = _ptr(x)
+    a.gate_bf16 = _ptr(gate)
+    a.pend_x = _ptr(pend_x)
+    a.pend_gate = _ptr(pend_gate)
+    a.n_ent = codes.shape[1]
+    a.codes = _ptr(codes)
+    a.scales = _ptr(scales)
+    a.key_bf16 = _ptr(key)
+    a.key_format = KEY_FP4 if key_scales is not None else KEY_E4M3
+    a.keys = _ptr(keys)
+    a.key_scales = _ptr(key_scales)
+    a.block_keys = _ptr(block_keys)
+    a.swa = _ptr(swa)
+    a.swa_cap = 0 if swa is None else swa.shape[1]
+    _check(lib().csa2_decode_append(ctypes.byref(a), _stream(stream)))
+
+
 def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
                     out_idx, out_score, out_blocks, cand_blocks=None, key_scales=None):
     a = IndexerArgs()
@@ -255,7 +319,7 @@ def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_b
     a.out_blocks = _ptr(out_blocks)
     a.cand_blocks = _ptr(cand_blocks)
     a.n_cand_blocks = 0 if cand_blocks is None else cand_blocks.shape[1]
-    a.key_format = 0 if key_scales is None else 1
+    a.key_format = KEY_E4M3 if key_scales is None else KEY_FP4
     a.key_scales = _ptr(key_scales)
     return a
 

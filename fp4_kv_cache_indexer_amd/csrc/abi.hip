@@ -258,6 +258,52 @@ int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "kv_compress_quantize launch");
 }
 
+int32_t csa2_decode_append(const csa2_append_args* a, void* stream) {
+  g_err.clear();
+  if (!a) return fail(CSA2_EINVAL, "decode_append: NULL args");
+  if (a->m != 1 && a->m != 2 && a->m != 4) return fail(CSA2_EUNSUPPORTED, "decode_append: m=%d not in {1,2,4}", a->m);
+  if (a->key_format != CSA2_KEY_E4M3 && a->key_format != CSA2_KEY_FP4)
+    return fail(CSA2_EUNSUPPORTED, "decode_append: key_format %d unknown", a->key_format);
+  if (a->n_rows < 0 || a->n_seq < 0 || a->n_ent < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
+  if (a->n_rows == 0) return CSA2_OK;
+  if (!a->pos || !a->x_bf16 || !a->codes || !a->scales || !a->key_bf16 || !a->keys)
+    return fail(CSA2_EINVAL, "decode_append: pos, x, codes, scales, key and keys are required");
+  if (a->m > 1 && !a->pend_x) return fail(CSA2_EINVAL, "decode_append: m > 1 needs pend_x");
+  if (a->m > 1 && a->gate_bf16 && !a->pend_gate) return fail(CSA2_EINVAL, "decode_append: a gate needs pend_gate");
+  if (a->key_format == CSA2_KEY_FP4 && !a->key_scales) return fail(CSA2_EINVAL, "decode_append: FP4 keys need key_scales");
+  if (a->swa && a->swa_cap < 1) return fail(CSA2_EINVAL, "decode_append: swa_cap %d < 1", a->swa_cap);
+  if (!aligned(a->x_bf16, 16) || (a->gate_bf16 && !aligned(a->gate_bf16, 16)) ||
+      (a->pend_x && !aligned(a->pend_x, 16)) || (a->pend_gate && !aligned(a->pend_gate, 16)) ||
+      !aligned(a->key_bf16, 8) || !aligned(a->pos, 8) || (a->row_seq && !aligned(a->row_seq, 4)))
+    return fail(CSA2_EINVAL, "decode_append: x/gate/pending/key/pos misaligned");
+  if (!aligned(a->codes, 8) || !aligned(a->keys, 8) || (a->block_keys && !aligned(a->block_keys, 4)) ||
+      (a->swa && !aligned(a->swa, 4)))
+    return fail(CSA2_EINVAL, "decode_append: codes/keys/block_keys/swa misaligned");
+  csa2::AppendArgs k;
+  k.n_rows = a->n_rows;
+  k.n_seq = a->n_seq;
+  k.row_seq = a->row_seq;
+  k.pos = a->pos;
+  k.m = a->m;
+  k.x = static_cast<const uint16_t*>(a->x_bf16);
+  k.gate = a->m > 1 ? static_cast<const uint16_t*>(a->gate_bf16) : nullptr;
+  k.pend_x = static_cast<uint16_t*>(a->pend_x);
+  k.pend_gate = static_cast<uint16_t*>(a->pend_gate);
+  k.n_ent = a->n_ent;
+  k.codes = a->codes;
+  k.scales = a->scales;
+  k.key = static_cast<const uint16_t*>(a->key_bf16);
+  k.key_fp4 = a->key_format == CSA2_KEY_FP4;
+  k.keys = a->keys;
+  k.key_scales = a->key_scales;
+  k.block_keys = a->block_keys;
+  k.swa = a->swa;
+  k.swa_cap = a->swa ? a->swa_cap : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "decode_append launch");
+}
+
 int32_t csa2_index_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_ent,
                                  int64_t blk_begin, int64_t blk_end, uint8_t* summ,
                                  void* stream) {
@@ -470,7 +516,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
   g_err.clear();
-  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_FILTER)
+  if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_APPEND)
     return fail(CSA2_EINVAL, "kernel_timer_start: unknown site %d", site);
   if (max_launches < 1 || max_launches > 1000000)
     return fail(CSA2_EINVAL, "kernel_timer_start: max_launches %d outside [1, 1e6]", max_launches);

@@ -109,6 +109,32 @@ struct AttnArgs {
   float* part_ml;           // [n_split][R][H][2]
 };
 
+// One new token per row: window ring, pending group or a completed entry
+// with its index key and block summary.
+struct AppendArgs {
+  int32_t n_rows;
+  int64_t n_seq;
+  const int32_t* row_seq;
+  const int64_t* pos;
+  int32_t m;
+  const uint16_t* x;
+  const uint16_t* gate;
+  uint16_t* pend_x;
+  uint16_t* pend_gate;
+  int64_t n_ent;
+  uint8_t* codes;
+  uint8_t* scales;
+  const uint16_t* key;
+  bool key_fp4;
+  uint8_t* keys;
+  uint8_t* key_scales;
+  uint8_t* block_keys;
+  uint8_t* swa;
+  int32_t swa_cap;
+};
+
+hipError_t launch_decode_append(const AppendArgs& a, hipStream_t stream);
+
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 

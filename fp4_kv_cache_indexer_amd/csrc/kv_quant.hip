@@ -34,28 +34,21 @@ __device__ __forceinline__ void load_bf16x16(const uint16_t* p, float* v) {
   }
 }
 
-// One thread = one (sequence, entry, 16-channel group).
+// Pool the m tokens of one group over 16 channels (xs[j], zs[j]: token j's
+// channels) and quantise them: returns the E4M3 scale byte, the 16 E2M1
+// codes in lo (channels 0-7) and hi (8-15).
 template <int M, bool GATE>
-__global__ __launch_bounds__(256) void kv_compress_quantize_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ z, int64_t n_seq, int64_t n_ent,
-    int64_t x_seq_stride, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    int64_t out_seq_stride) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= n_seq * n_ent * 32) return;
-  const int g = (int)(gid & 31);
-  const int64_t ent = gid >> 5;
-  const int64_t s = ent / n_ent, e = ent - s * n_ent;
-  const int64_t tok0 = s * x_seq_stride + e * M;
-
+__device__ __forceinline__ uint32_t pool_quantize16(const uint16_t* const* xs, const uint16_t* const* zs,
+                                                   uint32_t& lo, uint32_t& hi) {
   float y[16];
   if (M == 1) {
-    load_bf16x16(x + tok0 * kD + g * 16, y);
+    load_bf16x16(xs[0], y);
   } else if (!GATE) {
     float acc[16], t[16];
-    load_bf16x16(x + tok0 * kD + g * 16, acc);
+    load_bf16x16(xs[0], acc);
 #pragma unroll
     for (int j = 1; j < M; ++j) {
-      load_bf16x16(x + (tok0 + j) * kD + g * 16, t);
+      load_bf16x16(xs[j], t);
 #pragma unroll
       for (int c = 0; c < 16; ++c) acc[c] += t[c];
     }
@@ -65,8 +58,8 @@ __global__ __launch_bounds__(256) void kv_compress_quantize_kernel(
     float xv[M][16], zv[M][16];
 #pragma unroll
     for (int j = 0; j < M; ++j) {
-      load_bf16x16(x + (tok0 + j) * kD + g * 16, xv[j]);
-      load_bf16x16(z + (tok0 + j) * kD + g * 16, zv[j]);
+      load_bf16x16(xs[j], xv[j]);
+      load_bf16x16(zs[j], zv[j]);
     }
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -90,12 +83,36 @@ __global__ __launch_bounds__(256) void kv_compress_quantize_kernel(
   const uint32_t sc = f32_to_e4m3(__fdiv_rn(amax, 6.0f));
   const float sv = e4m3_to_f32(sc);
 
-  uint32_t lo = 0u, hi = 0u;
+  lo = 0u;
+  hi = 0u;
 #pragma unroll
   for (int c = 0; c < 8; ++c) lo |= e2m1_code(y[c], sv) << (4 * c);
 #pragma unroll
   for (int c = 0; c < 8; ++c) hi |= e2m1_code(y[8 + c], sv) << (4 * c);
+  return sc;
+}
 
+// One thread = one (sequence, entry, 16-channel group).
+template <int M, bool GATE>
+__global__ __launch_bounds__(256) void kv_compress_quantize_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ z, int64_t n_seq, int64_t n_ent,
+    int64_t x_seq_stride, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    int64_t out_seq_stride) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_seq * n_ent * 32) return;
+  const int g = (int)(gid & 31);
+  const int64_t ent = gid >> 5;
+  const int64_t s = ent / n_ent, e = ent - s * n_ent;
+  const int64_t tok0 = s * x_seq_stride + e * M;
+  const uint16_t* xs[M];
+  const uint16_t* zs[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    xs[j] = x + (tok0 + j) * kD + g * 16;
+    zs[j] = GATE ? z + (tok0 + j) * kD + g * 16 : nullptr;
+  }
+  uint32_t lo, hi;
+  const uint32_t sc = pool_quantize16<M, GATE>(xs, zs, lo, hi);
   const int64_t oe = s * out_seq_stride + e;
   *reinterpret_cast<uint2*>(codes + oe * 256 + g * 8) = make_uint2(lo, hi);
   scales[oe * 32 + g] = (uint8_t)sc;
@@ -214,6 +231,156 @@ __global__ __launch_bounds__(256) void block_summary_fp4_kernel(const uint8_t* _
 #pragma unroll
   for (int i = 0; i < 4; ++i) out |= f32_to_e4m3(__fdiv_rn(acc[i], (float)cnt)) << (8 * i);
   *reinterpret_cast<uint32_t*>(summ + (s * nb_total + b) * kIdxDim + c4 * 4) = out;
+}
+
+// ---------------------------------------------------------------------------
+// Decode-time append: one launch per generated token and cache [0539edu §3:
+// m = 2 in the encoder, 1 in the decoder; 128-token FP8 window].
+// ---------------------------------------------------------------------------
+
+// One workgroup of 128 threads per row (one new token of one sequence):
+//   * every thread: 4 channels of the token into the E4M3 window ring;
+//   * an open group (pos % m < m - 1): the token (and its gate logits) wait
+//     in the pending buffer;
+//   * a completed group: threads 0-31 pool + quantise one 16-channel group of
+//     entry pos / m each, quantise 4 channels of its index key each (FP4:
+//     the 32-channel group maximum over 8 neighbouring lanes) and refresh
+//     4 channels of the block summary, taking the new member from their own
+//     registers and the older members from the cache.
+template <int M, bool GATE, int KF>
+__global__ __launch_bounds__(128) void decode_append_kernel(AppendArgs a) {
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t s = a.row_seq ? a.row_seq[r] : r;
+  const int64_t p = a.pos[r];
+  if (s < 0 || s >= a.n_seq || p < 0 || p / M >= a.n_ent) return;
+  const uint16_t* x = a.x + (int64_t)r * kD;
+  const uint16_t* z = GATE ? a.gate + (int64_t)r * kD : nullptr;
+
+  if (a.swa) {
+    const uint2 w = *reinterpret_cast<const uint2*>(x + 4 * t);
+    uint32_t b = 0u;
+    b |= f32_to_e4m3(bf16_to_f32(w.x & 0xFFFFu));
+    b |= f32_to_e4m3(bf16_to_f32(w.x >> 16)) << 8;
+    b |= f32_to_e4m3(bf16_to_f32(w.y & 0xFFFFu)) << 16;
+    b |= f32_to_e4m3(bf16_to_f32(w.y >> 16)) << 24;
+    const int64_t slot = p % a.swa_cap;
+    *reinterpret_cast<uint32_t*>(a.swa + (s * a.swa_cap + slot) * kD + 4 * t) = b;
+  }
+  const int j = (int)(p % M);
+  const int64_t e = p / M;     // the entry this token belongs to
+  if (j < M - 1) {
+    const int64_t pr = (s * (M - 1) + j) * kD + 4 * t;
+    *reinterpret_cast<uint2*>(a.pend_x + pr) = *reinterpret_cast<const uint2*>(x + 4 * t);
+    if (GATE) *reinterpret_cast<uint2*>(a.pend_gate + pr) = *reinterpret_cast<const uint2*>(z + 4 * t);
+    return;
+  }
+  if (t >= 32) return;
+
+  // ---- the entry: 16-channel group t
+  {
+    const uint16_t* xs[M];
+    const uint16_t* zs[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const bool cur = i == M - 1;
+      const int64_t pr = (s * (M - 1) + i) * kD + 16 * t;
+      xs[i] = cur ? x + 16 * t : a.pend_x + pr;
+      zs[i] = GATE ? (cur ? z + 16 * t : a.pend_gate + pr) : nullptr;
+    }
+    uint32_t lo, hi;
+    const uint32_t sc = pool_quantize16<M, GATE>(xs, zs, lo, hi);
+    const int64_t oe = s * a.n_ent + e;
+    *reinterpret_cast<uint2*>(a.codes + oe * 256 + t * 8) = make_uint2(lo, hi);
+    a.scales[oe * 32 + t] = (uint8_t)sc;
+  }
+
+  // ---- its index key: channels 4t .. 4t+3
+  const uint16_t* kb = a.key + (int64_t)r * kIdxDim + 4 * t;
+  const uint2 kw = *reinterpret_cast<const uint2*>(kb);
+  float kv[4] = {bf16_to_f32(kw.x & 0xFFFFu), bf16_to_f32(kw.x >> 16), bf16_to_f32(kw.y & 0xFFFFu),
+                 bf16_to_f32(kw.y >> 16)};
+  const int64_t oe = s * a.n_ent + e;
+  uint32_t new_key;      // E4M3: 4 bytes; FP4: 4 codes (16 bits) | scale << 16
+  if (KF == 0) {
+    new_key = f32_to_e4m3(kv[0]) | (f32_to_e4m3(kv[1]) << 8) | (f32_to_e4m3(kv[2]) << 16) |
+              (f32_to_e4m3(kv[3]) << 24);
+    *reinterpret_cast<uint32_t*>(a.keys + oe * kIdxDim + 4 * t) = new_key;
+  } else {
+    float amax = fmaxf(fmaxf(fabsf(kv[0]), fabsf(kv[1])), fmaxf(fabsf(kv[2]), fabsf(kv[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));        // lanes 8g .. 8g+7: group g's 32 channels
+    const uint32_t sc = f32_to_e4m3(__fdiv_rn(amax, 6.0f));
+    const float sv = e4m3_to_f32(sc);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c |= e2m1_code(kv[i], sv) << (4 * i);
+    *reinterpret_cast<uint16_t*>(a.keys + oe * 64 + 2 * t) = (uint16_t)c;
+    if ((t & 7) == 0) a.key_scales[oe * 4 + t / 8] = (uint8_t)sc;
+    new_key = c | (sc << 16);
+  }
+
+  // ---- the summary of the entry's block over the entries written so far
+  if (!a.block_keys) return;
+  const int64_t b = e / kBlockPos;
+  const int64_t j0 = b * kBlockPos;
+  const int cnt = (int)(e - j0) + 1;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (KF == 0) {
+    const uint8_t* base = a.keys + (s * a.n_ent + j0) * kIdxDim + 4 * t;
+    uint32_t w[kBlockPos];
+#pragma unroll
+    for (int i = 0; i < kBlockPos; ++i)
+      w[i] = i < cnt - 1 ? *reinterpret_cast<const uint32_t*>(base + (int64_t)i * kIdxDim) : new_key;
+#pragma unroll
+    for (int i = 0; i < kBlockPos; ++i) {
+      if (i < cnt) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += e4m3_to_f32((w[i] >> (8 * c)) & 0xFFu);
+      }
+    }
+  } else {
+    const uint8_t* cb = a.keys + (s * a.n_ent + j0) * 64 + 2 * t;
+    const uint8_t* sb = a.key_scales + (s * a.n_ent + j0) * 4 + t / 8;
+    uint32_t cw[kBlockPos], sw[kBlockPos];
+#pragma unroll
+    for (int i = 0; i < kBlockPos; ++i) {
+      const bool old = i < cnt - 1;
+      cw[i] = old ? *reinterpret_cast<const uint16_t*>(cb + (int64_t)i * 64) : (new_key & 0xFFFFu);
+      sw[i] = old ? sb[(int64_t)i * 4] : (new_key >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kBlockPos; ++i) {
+      if (i < cnt) {
+        const float sv = e4m3_to_f32(sw[i]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += e2m1_to_f32((cw[i] >> (4 * c)) & 0xFu) * sv;
+      }
+    }
+  }
+  uint32_t out = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) out |= f32_to_e4m3(__fdiv_rn(acc[c], (float)cnt)) << (8 * c);
+  const int64_t nb = (a.n_ent + kBlockPos - 1) / kBlockPos;
+  *reinterpret_cast<uint32_t*>(a.block_keys + (s * nb + b) * kIdxDim + 4 * t) = out;
+}
+
+hipError_t launch_decode_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.n_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.n_rows), block(128);
+  const bool gate = a.gate != nullptr;
+  const int kf = a.key_fp4 ? 1 : 0;
+#define CSA2_AP(MM, GG, KK) hipLaunchKernelGGL((decode_append_kernel<MM, GG, KK>), grid, block, 0, stream, a)
+#define CSA2_AP_K(MM, GG) do { if (kf) CSA2_AP(MM, GG, 1); else CSA2_AP(MM, GG, 0); } while (0)
+  if (a.m == 1) CSA2_AP_K(1, false);
+  else if (a.m == 2 && gate) CSA2_AP_K(2, true);
+  else if (a.m == 2) CSA2_AP_K(2, false);
+  else if (gate) CSA2_AP_K(4, true);
+  else CSA2_AP_K(4, false);
+#undef CSA2_AP_K
+#undef CSA2_AP
+  return hipGetLastError();
 }
 
 hipError_t launch_index_key_quantize(const void* k, int64_t n_seq, int64_t n_ent, int64_t k_seq_stride,

@@ -150,6 +150,70 @@ int32_t csa2_index_block_summary_fp4(const uint8_t* codes, const uint8_t* scales
                                      void* stream);
 
 /*
+ * Decode-time append: one generated token per row, written into a sequence's
+ * caches in one launch [0539edu §3: compression_ratio 2 in the encoder and
+ * 1 in the decoder, swa_window_size 128, FP8 window; nxbn §4.2 pooling].
+ * For row r, sequence s = row_seq[r] (identity when NULL), position p = pos[r]:
+ *   * window ring (when swa != NULL): swa[s][p % swa_cap] = E4M3 of the token
+ *     (round to nearest even, saturating), as the prefill window reads it;
+ *   * p % m < m-1: the group is still open; the token (and its gate logits)
+ *     go to pend_x[s][p % m] (pend_gate[s][p % m]);
+ *   * p % m == m-1: entry e = p / m completes from pend_x[s][0..m-2] and the
+ *     token, pooled and quantised exactly as csa2_kv_compress_quantize
+ *     (codes/scales[s][e]); its index key key_bf16[r] is stored as E4M3
+ *     (round to nearest even, saturating) or FP4 (as csa2_index_key_quantize)
+ *     in keys/key_scales[s][e]; with block_keys != NULL the summary of block
+ *     e/8 is recomputed over its entries written so far, [8*(e/8), e], as
+ *     csa2_index_block_summary(_fp4) with n_ent = e + 1.
+ * Rows whose sequence is outside [0, n_seq), whose position is negative or
+ * whose entry would be at or past n_ent are skipped.  Two rows of one
+ * sequence in one call race.  The pending buffers are the caller's but their
+ * contents are the library's (bf16 tokens); keep them per cache.
+ *   n_rows              : rows (tokens) in this call
+ *   n_seq               : sequences in the caches
+ *   row_seq, pos        : device int32 [R] (nullable), int64 [R]
+ *   m                   : 1, 2 or 4
+ *   x_bf16, gate_bf16   : bf16 [R][512]; gate nullable (equal weights)
+ *   pend_x, pend_gate   : bf16 [n_seq][m-1][512]; pend_x required for m > 1,
+ *                         pend_gate when gate_bf16 is given
+ *   n_ent               : entries per sequence in codes/scales/keys
+ *   codes, scales       : [n_seq][n_ent][256], [n_seq][n_ent][32]
+ *   key_bf16            : bf16 [R][128]: the index key of the entry the row
+ *                         completes (read only then)
+ *   key_format          : CSA2_KEY_E4M3 (keys [n_seq][n_ent][128]) or
+ *                         CSA2_KEY_FP4 (keys [n_seq][n_ent][64] codes,
+ *                         key_scales [n_seq][n_ent][4])
+ *   block_keys          : nullable, [n_seq][ceil(n_ent/8)][128] E4M3
+ *   swa, swa_cap        : nullable, [n_seq][swa_cap][512] E4M3 ring
+ * Alignment: x, gate, pending buffers 16 bytes; codes, keys 8; swa 4.
+ * Status: EUNSUPPORTED for m or key_format outside the sets above, EINVAL
+ * for missing or misaligned buffers and negative sizes.
+ */
+typedef struct {
+  int32_t n_rows;
+  int64_t n_seq;
+  const int32_t* row_seq;
+  const int64_t* pos;
+  int32_t m;
+  const void* x_bf16;
+  const void* gate_bf16;
+  void* pend_x;
+  void* pend_gate;
+  int64_t n_ent;
+  uint8_t* codes;
+  uint8_t* scales;
+  const void* key_bf16;
+  int32_t key_format;
+  uint8_t* keys;
+  uint8_t* key_scales;
+  uint8_t* block_keys;
+  uint8_t* swa;
+  int32_t swa_cap;
+} csa2_append_args;
+
+int32_t csa2_decode_append(const csa2_append_args* args, void* stream);
+
+/*
  * Indexer + top-k [0539edu §3, csa2.indexer and its hierarchical block].
  *
  * Row r scores entries of sequence row_seq[r] (r if NULL) that are visible to
@@ -298,6 +362,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
 #define CSA2_SITE_ATTN 8           /* sparse + window attention                 */
 #define CSA2_SITE_ATTN_COMBINE 9   /* merge of the attention key splits         */
 #define CSA2_SITE_FILTER 10        /* top-k candidate filter (every stage)      */
+#define CSA2_SITE_APPEND 11        /* decode-time append                        */
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches);
 int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);

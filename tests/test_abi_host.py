@@ -139,3 +139,31 @@ def test_attn_and_cache_write_validation_without_gpu():
     assert L.csa2_index_block_summary_fp4(p, p, 1, 17, 0, 4, p, None) == 1         # 3 blocks only
     assert L.csa2_index_block_summary_fp4(None, p, 1, 17, 0, 3, p, None) == 1
     assert L.csa2_index_block_summary_fp4(p, p, 1, 17, 1, 1, p, None) == 0
+
+
+@needs_lib
+def test_decode_append_validation_without_gpu():
+    L = C.lib()
+    p = ctypes.c_void_p(0x1000)
+
+    def args(**kw):
+        a = C.AppendArgs()
+        a.n_rows, a.n_seq, a.m, a.n_ent = 2, 2, 1, 64
+        a.pos, a.x_bf16, a.codes, a.scales, a.key_bf16, a.keys = p, p, p, p, p, p
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    cases = [
+        (dict(m=3), 2), (dict(key_format=5), 2), (dict(n_rows=-1), 1), (dict(pos=None), 1),
+        (dict(keys=None), 1), (dict(m=2), 1),                          # m > 1 needs pend_x
+        (dict(m=2, pend_x=p, gate_bf16=p), 1),                          # a gate needs pend_gate
+        (dict(key_format=1), 1),                                        # FP4 keys need key_scales
+        (dict(swa=p, swa_cap=0), 1), (dict(x_bf16=ctypes.c_void_p(0x1008)), 1),
+        (dict(codes=ctypes.c_void_p(0x1004)), 1),
+    ]
+    for kw, status in cases:
+        a = args(**kw)
+        assert L.csa2_decode_append(ctypes.byref(a), None) == status, kw
+        assert C.last_error() != ""
+    assert L.csa2_decode_append(ctypes.byref(args(n_rows=0, pos=None)), None) == 0   # nothing to do
