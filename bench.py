@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fp4_kv_cache_indexer_amd import csa2 as C  # noqa: E402
+from fp4_kv_cache_indexer_amd import schedule as SCH  # noqa: E402
 from fp4_kv_cache_indexer_amd import synth  # noqa: E402
 
 METRIC = "decode sparse-attn queries/sec at 1M ctx; indexer HBM GB/s vs peak"
@@ -68,6 +69,18 @@ for _name in ("c3", "c4"):
                                     desc=WORKLOADS[_name]["desc"] + "; FP4 index keys (68 B/entry)")
 
 
+# the full 40-layer decode step of the CSA2 schedule
+WORKLOADS["sched40"] = dict(
+    desc="40-layer CSA2 decode step at 1M context, batch 8: 2 window-only layers; 3 encoder groups "
+         "(Full + 5 Reuse) on m=2 caches of 524,288 FP4 entries; 5 decoder groups on one m=1 cache of "
+         "1,048,576 FP4 entries (Full + 3 Reuse, then Reindex within the Full layer's 16384-position pool "
+         "+ 3 Reuse); hierarchical indexers keep 2048 blocks; per token: append to all four caches and "
+         "all 40 windows; 64 heads, top-512, 128-token FP8 windows",
+    B=8, T=1 << 20, H=64, k=512, keep=2048, sched=True, N=1 << 20, hier=True, m=1)
+WORKLOADS["sched40fp4"] = dict(WORKLOADS["sched40"], key="fp4",
+                               desc=WORKLOADS["sched40"]["desc"] + "; FP4 index keys (the 890 B/token layout)")
+
+
 def layers_of(w):
     return w.get("layers", ("full",))
 
@@ -97,7 +110,6 @@ class InputSet:
                 kb = torch.randn((1, N, 128), generator=g, device="cuda").to(torch.bfloat16)
                 C.index_key_quantize(kb, codes=self.keys[b:b + 1], scales=self.kscales[b:b + 1])
                 del kb
-            self.k_new = torch.randn((B, 1, 128), generator=g, device="cuda").to(torch.bfloat16)
             self.summ = C.index_block_summary_fp4(self.keys, self.kscales) if w["hier"] else None
         else:
             self.keys = torch.empty((B, N, 128), dtype=torch.uint8, device="cuda")
@@ -105,20 +117,35 @@ class InputSet:
                 self.keys[b] = synth.to_e4m3(torch.randn((N, 128), generator=g, device="cuda"))
             self.kscales = None
             self.summ = C.index_block_summary(self.keys) if w["hier"] else None
-        self.swa = synth.to_e4m3(synth.latent_dev((B, 128, 512), g, w["dist"]))
+        layers = layers_of(w)
+        nl = len(layers)
+        # every layer's window ring, one tensor [layers, B, 128, 512]
+        self.rings = synth.to_e4m3(synth.latent_dev((nl * B, 128, 512), g, w["dist"])).view(nl, B, 128, 512)
+        self.swa = self.rings[0]
         self.swa_len = torch.full((B,), 128, dtype=torch.int32, device="cuda")
         self.q_idx = synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
         self.q = torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16)
-        self.x_new = synth.latent_dev((B, m, 512), g, w["dist"]).to(torch.bfloat16)
-        self.z_new = torch.randn((B, m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+        # the new token: its latent (and gate logits), its index key, its
+        # position (sets alternate the parity, so m=2 caches alternately
+        # complete the last entry and hold a pending token)
+        self.x_tok = synth.latent_dev((B, 512), g, w["dist"]).to(torch.bfloat16)
+        self.z_tok = torch.randn((B, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+        self.k_tok = torch.randn((B, 128), generator=g, device="cuda").to(torch.bfloat16)
+        self.pos = torch.full((B,), N * m - 1 - (set_id % 2 if m > 1 else 0), dtype=torch.int64, device="cuda")
+        self.pend_x = torch.zeros((B, m - 1, 512), dtype=torch.bfloat16, device="cuda") if m > 1 else None
+        self.pend_z = torch.zeros((B, m - 1, 512), dtype=torch.bfloat16, device="cuda") if m > 1 else None
+        # the other layers' windows take their own new tokens
+        self.ring_rows = torch.tensor([li * B + b for li in range(1, nl) for b in range(B)], dtype=torch.int32,
+                                      device="cuda")
+        self.ring_pos = torch.full(((nl - 1) * B,), N * m - 1, dtype=torch.int64, device="cuda")
+        self.ring_x = synth.latent_dev(((nl - 1) * B, 512), g, w["dist"]).to(torch.bfloat16) if nl > 1 else None
         # per-layer queries and windows (layer 0 uses the tensors above)
-        layers = layers_of(w)
         self.lq, self.lq_idx, self.lswa = [self.q], [self.q_idx], [self.swa]
-        for L in range(1, len(layers)):
+        for L in range(1, nl):
             self.lq_idx.append(synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
                                if layers[L] == "reindex" else None)
             self.lq.append(torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16))
-            self.lswa.append(synth.to_e4m3(synth.latent_dev((B, 128, 512), g, w["dist"])))
+            self.lswa.append(self.rings[L])
         self.pool = w.get("pool", False)
         self.blocks = torch.empty((B, w["keep"]), dtype=torch.int32, device="cuda") if self.pool else None
         self.idx2 = torch.empty((B, w["k"]), dtype=torch.int32, device="cuda")
@@ -139,19 +166,14 @@ class InputSet:
 
 def step(w, s):
     """One decode step for the whole batch (all hot-path rows)."""
-    N = w["N"]
-    # a0: the newest entry (m tokens pooled; m = 1 in the decoder layers)
-    C.kv_compress_quantize(s.x_new, w["m"], gate=s.z_new, codes=s.codes[:, N - 1:],
-                           scales=s.scales[:, N - 1:], out_seq_stride=N)
-    if s.fp4:                  # ... and its index key, quantized to FP4
-        C.index_key_quantize(s.k_new, codes=s.keys[:, N - 1:], scales=s.kscales[:, N - 1:], out_seq_stride=N)
-    # a1: refresh the summary of the block holding that entry
-    if w["hier"]:
-        b = (N - 1) // 8
-        if s.fp4:
-            C.index_block_summary_fp4(s.keys, s.kscales, summ=s.summ, blk_begin=b, blk_end=b + 1)
-        else:
-            C.index_block_summary(s.keys, summ=s.summ, blk_begin=b, blk_end=b + 1)
+    # a0-a1: the new token -- the window of layer 0, the last entry (m tokens
+    # pooled; m = 1 in the decoder layers) with its index key and the summary
+    # of its block -- and the windows of the group's other layers
+    C.decode_append(s.x_tok, s.pos, s.codes, s.scales, s.k_tok, s.keys, m=w["m"], gate=s.z_tok,
+                    pend_x=s.pend_x, pend_gate=s.pend_z, key_scales=s.kscales, block_keys=s.summ,
+                    swa=s.rings[0])
+    if s.ring_x is not None:
+        C.window_append(s.ring_x, s.ring_pos, s.rings.view(-1, 128, 512), row_seq=s.ring_rows)
     idx = None
     for L, mode in enumerate(layers_of(w)):
         # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context); a7:
@@ -172,6 +194,149 @@ def step(w, s):
         # a4-a6: gather + dequant + joint sparse/window attention
         C.sparse_attn_decode(s.lq[L], s.codes, s.scales, idx, swa=s.lswa[L], swa_len=s.swa_len, out=s.out,
                              lse=s.lse, workspace=s.ws_attn)
+
+
+class SchedSet:
+    """One batch of the 40-layer schedule's caches, windows and per-layer
+    queries, all device-resident.  Sets alternate the new token's position
+    parity so the m=2 caches alternately complete an entry and hold a
+    pending token."""
+
+    def __init__(self, w, set_id, seed=0):
+        B, T, H, k = w["B"], w["T"], w["H"], w["k"]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1_000_003 * seed + 7919 * set_id + 29)
+        self.layers = SCH.csa2_layers()
+        self.fp4 = w.get("key") == "fp4"
+        bf = dict(dtype=torch.bfloat16, device="cuda")
+        u8 = dict(dtype=torch.uint8, device="cuda")
+        self.caches = []
+        for m in SCH.cache_ratios(self.layers):
+            N = T // m
+            c = dict(m=m, N=N, hier=N > 8 * w["keep"])
+            c["codes"] = torch.empty((B, N, 256), **u8)
+            c["scales"] = torch.empty((B, N, 32), **u8)
+            c["keys"] = torch.empty((B, N, 64 if self.fp4 else 128), **u8)
+            c["kscales"] = torch.empty((B, N, 4), **u8) if self.fp4 else None
+            for b in range(B):
+                x = synth.latent_dev((1, N * m, 512), g, "normal").to(torch.bfloat16)
+                z = torch.randn((1, N * m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+                C.kv_compress_quantize(x, m, gate=z, codes=c["codes"][b:b + 1], scales=c["scales"][b:b + 1])
+                del x, z
+                kb = torch.randn((1, N, 128), generator=g, device="cuda")
+                if self.fp4:
+                    C.index_key_quantize(kb.to(torch.bfloat16), codes=c["keys"][b:b + 1],
+                                         scales=c["kscales"][b:b + 1])
+                else:
+                    c["keys"][b] = synth.to_e4m3(kb[0])
+                del kb
+            c["summ"] = ((C.index_block_summary_fp4(c["keys"], c["kscales"]) if self.fp4
+                          else C.index_block_summary(c["keys"])) if c["hier"] else None)
+            c["pend_x"] = torch.zeros((B, m - 1, 512), **bf) if m > 1 else None
+            c["pend_z"] = torch.zeros((B, m - 1, 512), **bf) if m > 1 else None
+            c["x_new"] = synth.latent_dev((B, 512), g, "normal").to(torch.bfloat16)
+            c["z_new"] = torch.randn((B, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
+            c["k_new"] = torch.randn((B, 128), generator=g, device="cuda").to(torch.bfloat16)
+            self.caches.append(c)
+        L = len(self.layers)
+        self.rings = synth.to_e4m3(synth.latent_dev((L * B, SCH.WINDOW, 512), g, "normal")).view(L, B, SCH.WINDOW, 512)
+        self.swa_len = torch.full((B,), SCH.WINDOW, dtype=torch.int32, device="cuda")
+        p = T - 1 - (set_id % 2)
+        self.pos = torch.full((B,), p, dtype=torch.int64, device="cuda")
+        self.full_layer = {ly.cache: ly.index for ly in self.layers if ly.mode == "full"}
+        ring_layers = [ly.index for ly in self.layers if ly.index not in self.full_layer.values()]
+        self.ring_rows = torch.tensor([li * B + b for li in ring_layers for b in range(B)], dtype=torch.int32,
+                                      device="cuda")
+        self.ring_pos = torch.full((len(ring_layers) * B,), p, dtype=torch.int64, device="cuda")
+        self.ring_x = synth.latent_dev((len(ring_layers) * B, 512), g, "normal").to(torch.bfloat16)
+        self.q = [torch.randn((B, H, 512), generator=g, device="cuda").to(torch.bfloat16) for _ in self.layers]
+        self.q_idx = {ly.index: synth.to_e4m3(torch.randn((B, 32, 128), generator=g, device="cuda"))
+                      for ly in self.layers if ly.mode in ("full", "reindex")}
+        groups = sorted({ly.group for ly in self.layers if ly.group >= 0})
+        self.gidx = {gr: torch.empty((B, k), dtype=torch.int32, device="cuda") for gr in groups}
+        dec = self.caches[3]
+        self.blocks = torch.empty((B, w["keep"]), dtype=torch.int32, device="cuda") if dec["hier"] else None
+        self.ws_idx = {}
+        for ci, c in enumerate(self.caches):
+            self.ws_idx[ci] = torch.zeros(max(256, C.indexer_topk_workspace(
+                self.q_idx[self.full_layer[ci]], c["keys"], k, block_keys=c["summ"], keep_blocks=w["keep"],
+                key_scales=c["kscales"])), **u8)
+        self.ws_pool = torch.zeros(max(256, C.indexer_topk_workspace(
+            self.q_idx[self.full_layer[3]], dec["keys"], k, cand_blocks=self.blocks, key_scales=dec["kscales"])),
+            **u8)
+        self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        idx0 = self.gidx[groups[0]]
+        need = max(C.sparse_attn_workspace(self.q[0], idx0, swa=self.rings[0], swa_len=self.swa_len,
+                                           codes=self.caches[0]["codes"]),
+                   C.sparse_attn_workspace(self.q[0], None, swa=self.rings[0], swa_len=self.swa_len))
+        self.ws_attn = torch.empty(max(256, need), **u8)
+        self.idx = self.gidx[groups[-1]]       # compared across graph replays
+
+
+def step_sched(w, s):
+    """One token through all 40 layers: appends, then every layer's selection
+    (Full / Reindex) and attention."""
+    for ci, c in enumerate(s.caches):
+        C.decode_append(c["x_new"], s.pos, c["codes"], c["scales"], c["k_new"], c["keys"], m=c["m"],
+                        gate=c["z_new"], pend_x=c["pend_x"], pend_gate=c["pend_z"], key_scales=c["kscales"],
+                        block_keys=c["summ"], swa=s.rings[s.full_layer[ci]])
+    C.window_append(s.ring_x, s.ring_pos, s.rings.view(-1, SCH.WINDOW, 512), row_seq=s.ring_rows)
+    dec = s.caches[3]
+    for ly in s.layers:
+        if ly.mode == "swa_only":
+            C.sparse_attn_decode(s.q[ly.index], None, None, None, swa=s.rings[ly.index], swa_len=s.swa_len,
+                                 out=s.out, lse=s.lse, workspace=s.ws_attn)
+            continue
+        c = s.caches[ly.cache]
+        idx = s.gidx[ly.group]
+        if ly.mode == "full":
+            C.indexer_topk(s.q_idx[ly.index], c["keys"], w["k"], block_keys=c["summ"], keep_blocks=w["keep"],
+                           out_idx=idx, out_blocks=s.blocks if ly.cache == 3 else None, workspace=s.ws_idx[ly.cache],
+                           key_scales=c["kscales"])
+        elif ly.mode == "reindex":
+            if s.blocks is not None:
+                C.indexer_topk(s.q_idx[ly.index], dec["keys"], w["k"], cand_blocks=s.blocks, out_idx=idx,
+                               workspace=s.ws_pool, key_scales=dec["kscales"])
+            else:
+                C.indexer_topk(s.q_idx[ly.index], dec["keys"], w["k"], out_idx=idx, workspace=s.ws_idx[3],
+                               key_scales=dec["kscales"])
+        C.sparse_attn_decode(s.q[ly.index], c["codes"], c["scales"], idx, swa=s.rings[ly.index],
+                             swa_len=s.swa_len, out=s.out, lse=s.lse, workspace=s.ws_attn)
+
+
+def sched_work(T, B=1, H=64, k=512, keep=2048, window=SCH.WINDOW, fp4=False):
+    """Algorithmic work of one token of the 40-layer schedule at context T:
+    indexer and attention flops (raw and weighted as the pages weigh
+    operations: BF16 1, FP8 0.5, FP4 0.25 -- indexer products take their
+    FP8 queries' weight, attention runs on bf16 operands), coarse-scan bytes
+    and the coarse-scan launches."""
+    layers = SCH.csa2_layers()
+    ratios = SCH.cache_ratios(layers)
+    idx_fl = attn_fl = 0
+    coarse_bytes = 0
+    coarse_launches = 0
+    key_b = 68 if fp4 else 128
+    for ly in layers:
+        w_eff = min(window, T)
+        if ly.mode == "swa_only":
+            attn_fl += 4 * H * w_eff * 512
+            continue
+        N = T // ratios[ly.cache]
+        nb = (N + 7) // 8
+        if ly.mode == "full":
+            if nb > keep:
+                idx_fl += (nb + min(N, keep * 8)) * 8192
+                coarse_bytes += nb * 128 + 32 * 128 + 32 * 4
+                coarse_launches += 1
+            else:
+                idx_fl += N * 8192
+        elif ly.mode == "reindex":
+            idx_fl += min(N, keep * 8) * 8192
+        attn_fl += 4 * H * (min(k, N) + w_eff) * 512
+    return dict(idx_flops=B * idx_fl, attn_flops=B * attn_fl,
+                weighted=B * (0.5 * idx_fl + 1.0 * attn_fl),
+                coarse_bytes=B * coarse_bytes, coarse_launches=coarse_launches, key_bytes=key_b)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_score_coarse_c3_traffic.md")
@@ -266,6 +431,9 @@ def scan_bytes(w):
     indexer scan): the key rows it must read plus queries and weights.  The
     coarse scan reads E4M3 block keys (128 B); a flat scan reads E4M3 keys or
     FP4 keys (64 code bytes + 4 scale bytes)."""
+    if w.get("sched"):
+        sw = sched_work(w["T"], w["B"], w["H"], w["k"], w["keep"], fp4=w.get("key") == "fp4")
+        return sw["coarse_bytes"] // max(1, sw["coarse_launches"])      # per coarse launch
     B, N = w["B"], w["N"]
     rows = (N + 7) // 8 if w["hier"] else N
     row_bytes = 68 if (w.get("key") == "fp4" and not w["hier"]) else 128
@@ -275,6 +443,8 @@ def scan_bytes(w):
 def attn_flops(w):
     """Algorithmic flops of one attention launch: QK^T and PV over the
     selected entries and the window, 2 * 2 * H * (k + 128) * 512 per query."""
+    if w.get("sched"):
+        return sched_work(w["T"], w["B"], w["H"], w["k"], w["keep"])["attn_flops"] // len(SCH.csa2_layers())
     return w["B"] * 4 * w["H"] * (w["k"] + 128) * 512
 
 
@@ -356,6 +526,127 @@ def cpu_baseline(w, s, seconds):
                       f"{', ' + model if model else ''}; {el:.1f} s)"}
 
 
+def cpu_baseline_sched(w, seconds):
+    """Time the oracle on a bounded sample of the 40-layer step: one
+    sequence, seeded host inputs of the workload's shapes (index keys and
+    summaries of every cache built once, untimed), fresh queries per token;
+    per token the append of every cache (pooling, quantisation, index key,
+    block summary) and every layer's selection and attention, the attended
+    entries quantised from seeded tokens by the oracle."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import csa2 as O
+
+    T, H, k, keep = w["T"], w["H"], w["k"], w["keep"]
+    fp4 = w.get("key") == "fp4"
+    layers = SCH.csa2_layers()
+    ratios = SCH.cache_ratios(layers)
+    g = np.random.default_rng(1)
+    caches = []
+    for m in ratios:
+        N = T // m
+        kb = synth.to_bf16_bits(g.standard_normal((N, 128)).astype(np.float32))
+        keys = O.Fp4Keys(*O.index_key_quantize_fp4(kb)) if fp4 else synth.to_e4m3(F64(kb))
+        summ = O.block_summary(keys) if (N + 7) // 8 > keep else None
+        caches.append(dict(m=m, N=N, keys=keys, summ=summ))
+    swa = synth.to_e4m3(g.standard_normal((SCH.WINDOW, 512)).astype(np.float32))
+    slots = O.swa_slots(0, SCH.WINDOW, SCH.WINDOW)
+
+    def bf16(shape):
+        return synth.to_bf16_bits(g.standard_normal(shape).astype(np.float32))
+
+    n, el = 0, 0.0
+    while el < seconds:
+        q = [bf16((H, 512)) for _ in layers]
+        q_idx = {ly.index: synth.to_e4m3(g.standard_normal((32, 128)).astype(np.float32))
+                 for ly in layers if ly.mode in ("full", "reindex")}
+        toks = {ci: bf16((c["m"], 512)) for ci, c in enumerate(caches)}
+        gates = {ci: bf16((c["m"], 512)) for ci, c in enumerate(caches)}
+        knew = bf16((1, 128))
+        sel_tok = bf16((k, 512))                        # the attended entries' tokens (m = 1 view)
+        ts = time.perf_counter()
+        for ci, c in enumerate(caches):                 # appends
+            O.kv_compress_quantize(toks[ci], gates[ci] if c["m"] > 1 else None, c["m"])
+            kq = O.Fp4Keys(*O.index_key_quantize_fp4(knew)) if fp4 else synth.to_e4m3(F64(knew))
+            blk = c["keys"][(c["N"] - 1) // 8 * 8:]
+            O.block_summary(blk)
+            del kq
+        sel, pool = {}, None
+        for ly in layers:
+            if ly.mode == "swa_only":
+                O.sparse_attn(q[ly.index], np.zeros((0, 256), np.uint8), np.zeros((0, 32), np.uint8),
+                              np.zeros(0, np.int64), swa, slots)
+                continue
+            c = caches[ly.cache]
+            if ly.mode == "full":
+                if c["summ"] is not None:
+                    idx, kept = O.indexer_topk_hier(q_idx[ly.index], None, c["keys"], c["summ"], k, c["N"], keep)
+                    if ly.cache == 3:
+                        pool = O.pool_positions(kept, c["N"])
+                else:
+                    idx = O.indexer_topk_flat(q_idx[ly.index], None, c["keys"], k, c["N"])
+                sel[ly.group] = idx
+            elif ly.mode == "reindex":
+                if pool is not None:
+                    sel[ly.group] = O.indexer_topk_pool(q_idx[ly.index], None, c["keys"], pool, k, c["N"])
+                else:
+                    sel[ly.group] = O.indexer_topk_flat(q_idx[ly.index], None, c["keys"], k, c["N"])
+            if ly.mode in ("full", "reindex"):
+                ne = int((sel[ly.group] >= 0).sum())
+                codes, scales = O.kv_compress_quantize(sel_tok[:ne], None, 1)
+            O.sparse_attn(q[ly.index], codes, scales, np.arange(ne), swa, slots)
+        el += time.perf_counter() - ts
+        n += 1
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} tokens of one sequence through the 40-layer step at {T} tokens of context "
+                      f"(seeded host inputs; oracle float64, NumPy/BLAS on {threads} threads; {el:.1f} s)"}
+
+
+def F64(bits):
+    """bf16 bits -> float32 values (exact) for the E4M3 rounding of synth."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def sweep(args, w0):
+    """The 40-layer step across contexts: time per token step next to the
+    schedule's algorithmic work per token."""
+    print("| context tokens | us/step (batch %d) | tokens/s | indexer GFLOP/token | attention GFLOP/token "
+          "| weighted GFLOP/token | global KV bytes/token |" % w0["B"])
+    print("|---:|---:|---:|---:|---:|---:|---:|")
+    base = None
+    for T in (4096, 16384, 65536, 262144, 1 << 20):
+        w = dict(w0, T=T, N=T)
+        sets = [SchedSet(w, i) for i in range(2)]
+        for i in range(3):
+            step_sched(w, sets[i % 2])
+        torch.cuda.synchronize()
+        graphs = []
+        for st in sets:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                step_sched(w, st)
+            graphs.append(gph)
+        for i in range(4):
+            graphs[i % 2].replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            graphs[i % 2].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        sw = sched_work(T, 1, w["H"], w["k"], w["keep"], fp4=w.get("key") == "fp4")
+        base = base or sw["weighted"]
+        kvb = SCH.global_bytes_per_token(SCH.csa2_layers(), 288, sw["key_bytes"])
+        print(f"| {T} | {us:.1f} | {w['B'] * 1e6 / us:.0f} | {sw['idx_flops'] / 1e9:.3f} | "
+              f"{sw['attn_flops'] / 1e9:.3f} | {sw['weighted'] / 1e9:.3f} ({sw['weighted'] / base:.2f}x) | {kvb:g} |",
+              flush=True)
+        del sets, graphs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +659,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a copy kernel of this size (for scaling rocprofv3 HBM counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="40-layer step across contexts 4K..1M (workload sched40 or sched40fp4); prints a table")
     ap.add_argument("--prof-summary", metavar="DIR",
                     help="print markdown summaries of the rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
@@ -381,27 +674,33 @@ def main():
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     C.lib()
+    if args.sweep:
+        if not w.get("sched"):
+            sys.exit("bench.py: --sweep runs the 40-layer schedule (--workload sched40 or sched40fp4)")
+        sweep(args, w)
+        return
     print(f"[bench] workload {args.workload}: {w['desc']}", file=sys.stderr, flush=True)
     t = time.perf_counter()
-    sets = [InputSet(w, i) for i in range(args.sets)]
+    make_set, step_fn = (SchedSet, step_sched) if w.get("sched") else (InputSet, step)
+    sets = [make_set(w, i) for i in range(args.sets)]
     torch.cuda.synchronize()
     print(f"[bench] {args.sets} input sets ready in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
 
     for i in range(max(1, args.warmup)):
-        step(w, sets[i % len(sets)])
+        step_fn(w, sets[i % len(sets)])
     torch.cuda.synchronize()
 
     graphs = None
     if not args.no_graph:
         for s in sets:                 # every set's eager result, the reference for its graph
-            step(w, s)
+            step_fn(w, s)
         torch.cuda.synchronize()
         ref = [(s.idx.clone(), s.out.clone()) for s in sets]
         graphs = []
         for s in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(w, s)
+                step_fn(w, s)
             graphs.append(g)
         # every replay must reproduce the eager step exactly
         for _ in range(2):
@@ -421,7 +720,7 @@ def main():
         if graphs:
             graphs[i % len(graphs)].replay()
         else:
-            step(w, sets[i % len(sets)])
+            step_fn(w, sets[i % len(sets)])
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
@@ -437,10 +736,10 @@ def main():
     stall_cycles = stall_calibrate(300e-6)
 
     def time_site(site):
-        C.kernel_timer_start(site, args.steps * len(layers_of(w)))
+        C.kernel_timer_start(site, args.steps * (len(SCH.csa2_layers()) if w.get("sched") else len(layers_of(w))))
         for i in range(args.steps):
             torch.cuda._sleep(stall_cycles)
-            step(w, sets[i % len(sets)])
+            step_fn(w, sets[i % len(sets)])
         n_l, tot_ms = C.kernel_timer_stop()
         return n_l, tot_ms / max(1, n_l) / 1e3
 
@@ -469,7 +768,7 @@ def main():
         "config": {"workload": f"{args.workload}: {w['desc']}", "batch": w["B"],
                    "entries_per_seq": w["N"], "heads": w["H"], "top_k": w["k"],
                    "keep_blocks": w["keep"], "swa_window": 128, "input_sets_rotated": len(sets),
-                   "layers": "/".join(layers_of(w)),
+                   "layers": ("40-layer CSA2 schedule" if w.get("sched") else "/".join(layers_of(w))),
                    "timed": "graph replays" if graphs else "eager launches"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -482,7 +781,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
+        res["cpu_baseline"] = (cpu_baseline_sched(w, args.cpu_seconds) if w.get("sched")
+                               else cpu_baseline(w, sets[0], args.cpu_seconds))
     print(json.dumps(res), flush=True)
 
 

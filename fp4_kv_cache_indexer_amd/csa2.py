@@ -298,6 +298,24 @@ def decode_append(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None,
     _check(lib().csa2_decode_append(ctypes.byref(a), _stream(stream)))
 
 
+def window_append(x, pos, swa, row_seq=None, stream=None):
+    """Write one token per row (x: bf16 [R, 512]) into window rings only
+    (swa: uint8 [S, cap, 512], slot pos % cap of sequence row_seq[r]), for
+    layers without a global cache of their own."""
+    for name, t in (("x", x), ("pos", pos), ("swa", swa), ("row_seq", row_seq)):
+        _dev(t, name)
+    a = AppendArgs()
+    a.n_rows = x.shape[0]
+    a.n_seq = swa.shape[0]
+    a.row_seq = _ptr(row_seq)
+    a.pos = _ptr(pos)
+    a.m = 1
+    a.x_bf16 = _ptr(x)
+    a.swa = _ptr(swa)
+    a.swa_cap = swa.shape[1]
+    _check(lib().csa2_decode_append(ctypes.byref(a), _stream(stream)))
+
+
 def _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
                     out_idx, out_score, out_blocks, cand_blocks=None, key_scales=None):
     a = IndexerArgs()

@@ -261,13 +261,34 @@ int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int
 int32_t csa2_decode_append(const csa2_append_args* a, void* stream) {
   g_err.clear();
   if (!a) return fail(CSA2_EINVAL, "decode_append: NULL args");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!a->codes) {                // window-only rows
+    if (a->n_rows < 0 || a->n_seq < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
+    if (a->n_rows == 0) return CSA2_OK;
+    if (!a->swa || a->swa_cap < 1 || !a->pos || !a->x_bf16)
+      return fail(CSA2_EINVAL, "decode_append: window-only rows need swa, swa_cap >= 1, pos and x");
+    if (!aligned(a->x_bf16, 16) || !aligned(a->pos, 8) || !aligned(a->swa, 4) ||
+        (a->row_seq && !aligned(a->row_seq, 4)))
+      return fail(CSA2_EINVAL, "decode_append: x/pos/swa/row_seq misaligned");
+    csa2::AppendArgs k{};
+    k.n_rows = a->n_rows;
+    k.n_seq = a->n_seq;
+    k.row_seq = a->row_seq;
+    k.pos = a->pos;
+    k.m = 1;
+    k.x = static_cast<const uint16_t*>(a->x_bf16);
+    k.swa = a->swa;
+    k.swa_cap = a->swa_cap;
+    hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
+    return e == hipSuccess ? CSA2_OK : hip_fail(e, "decode_append launch");
+  }
   if (a->m != 1 && a->m != 2 && a->m != 4) return fail(CSA2_EUNSUPPORTED, "decode_append: m=%d not in {1,2,4}", a->m);
   if (a->key_format != CSA2_KEY_E4M3 && a->key_format != CSA2_KEY_FP4)
     return fail(CSA2_EUNSUPPORTED, "decode_append: key_format %d unknown", a->key_format);
   if (a->n_rows < 0 || a->n_seq < 0 || a->n_ent < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
   if (a->n_rows == 0) return CSA2_OK;
-  if (!a->pos || !a->x_bf16 || !a->codes || !a->scales || !a->key_bf16 || !a->keys)
-    return fail(CSA2_EINVAL, "decode_append: pos, x, codes, scales, key and keys are required");
+  if (!a->pos || !a->x_bf16 || !a->scales || !a->key_bf16 || !a->keys)
+    return fail(CSA2_EINVAL, "decode_append: pos, x, scales, key and keys are required with codes");
   if (a->m > 1 && !a->pend_x) return fail(CSA2_EINVAL, "decode_append: m > 1 needs pend_x");
   if (a->m > 1 && a->gate_bf16 && !a->pend_gate) return fail(CSA2_EINVAL, "decode_append: a gate needs pend_gate");
   if (a->key_format == CSA2_KEY_FP4 && !a->key_scales) return fail(CSA2_EINVAL, "decode_append: FP4 keys need key_scales");
@@ -299,7 +320,6 @@ int32_t csa2_decode_append(const csa2_append_args* a, void* stream) {
   k.block_keys = a->block_keys;
   k.swa = a->swa;
   k.swa_cap = a->swa ? a->swa_cap : 1;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "decode_append launch");
 }

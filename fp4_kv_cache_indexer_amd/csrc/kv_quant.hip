@@ -253,7 +253,7 @@ __global__ __launch_bounds__(128) void decode_append_kernel(AppendArgs a) {
   const int t = threadIdx.x;
   const int64_t s = a.row_seq ? a.row_seq[r] : r;
   const int64_t p = a.pos[r];
-  if (s < 0 || s >= a.n_seq || p < 0 || p / M >= a.n_ent) return;
+  if (s < 0 || s >= a.n_seq || p < 0 || (a.codes && p / M >= a.n_ent)) return;
   const uint16_t* x = a.x + (int64_t)r * kD;
   const uint16_t* z = GATE ? a.gate + (int64_t)r * kD : nullptr;
 
@@ -267,6 +267,7 @@ __global__ __launch_bounds__(128) void decode_append_kernel(AppendArgs a) {
     const int64_t slot = p % a.swa_cap;
     *reinterpret_cast<uint32_t*>(a.swa + (s * a.swa_cap + slot) * kD + 4 * t) = b;
   }
+  if (!a.codes) return;          // a layer with a window only
   const int j = (int)(p % M);
   const int64_t e = p / M;     // the entry this token belongs to
   if (j < M - 1) {

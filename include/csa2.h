@@ -165,6 +165,8 @@ int32_t csa2_index_block_summary_fp4(const uint8_t* codes, const uint8_t* scales
  *     in keys/key_scales[s][e]; with block_keys != NULL the summary of block
  *     e/8 is recomputed over its entries written so far, [8*(e/8), e], as
  *     csa2_index_block_summary(_fp4) with n_ent = e + 1.
+ * With codes == NULL the call only writes windows (layers with no global
+ * cache of their own): swa, swa_cap, pos and x are used, the rest ignored.
  * Rows whose sequence is outside [0, n_seq), whose position is negative or
  * whose entry would be at or past n_ent are skipped.  Two rows of one
  * sequence in one call race.  The pending buffers are the caller's but their

@@ -157,6 +157,7 @@ def test_decode_append_validation_without_gpu():
     cases = [
         (dict(m=3), 2), (dict(key_format=5), 2), (dict(n_rows=-1), 1), (dict(pos=None), 1),
         (dict(keys=None), 1), (dict(m=2), 1),                          # m > 1 needs pend_x
+        (dict(codes=None), 1),                                          # window-only rows need swa
         (dict(m=2, pend_x=p, gate_bf16=p), 1),                          # a gate needs pend_gate
         (dict(key_format=1), 1),                                        # FP4 keys need key_scales
         (dict(swa=p, swa_cap=0), 1), (dict(x_bf16=ctypes.c_void_p(0x1008)), 1),
@@ -167,3 +168,5 @@ def test_decode_append_validation_without_gpu():
         assert L.csa2_decode_append(ctypes.byref(a), None) == status, kw
         assert C.last_error() != ""
     assert L.csa2_decode_append(ctypes.byref(args(n_rows=0, pos=None)), None) == 0   # nothing to do
+    w = args(codes=None, swa=ctypes.c_void_p(0x2002), swa_cap=128)
+    assert L.csa2_decode_append(ctypes.byref(w), None) == 1                          # swa misaligned

@@ -166,3 +166,21 @@ def test_decode_append_staggered_rows_and_skips():
         sub.codes, sub.scales, sub.keys, sub.kscales = c.codes[s:s + 1], c.scales[s:s + 1], c.keys[s:s + 1], None
         sub.summ, sub.swa, sub.pend_x, sub.m = c.summ[s:s + 1], c.swa[s:s + 1], c.pend_x[s:s + 1], m
         assert check_against_bulk(sub, x[s:s + 1], z[s:s + 1], k[s:s + 1], T, m, False, True, f"seq {s}") <= 1
+
+
+def test_window_append_many_rings():
+    """Window-only rows (layers without a cache of their own) write slot
+    pos % cap of their ring and nothing else."""
+    L, S, cap, T = 5, 3, 8, 19
+    x, _, _ = token_stream(9, L * S, T, False)
+    ring = torch.zeros((L * S, cap, 512), dtype=torch.uint8, device="cuda")
+    order = np.random.default_rng(3).permutation(L * S)
+    for p in range(T):
+        C.window_append(dev(x[order, p]).view(torch.bfloat16), dev(np.full(L * S, p, np.int64)), ring,
+                        row_seq=dev(order.astype(np.int32)))
+    torch.cuda.synchronize()
+    got = host(ring)
+    for r in range(L * S):
+        for slot in range(cap):
+            last = max(p for p in range(T) if p % cap == slot)
+            assert np.array_equal(got[r, slot], e4m3_of_bf16(x[r, last])), (r, slot)
