@@ -42,7 +42,7 @@ void timer_mark(int32_t site, hipStream_t s, bool end) {
   if (g_timer.site != site) return;
   const size_t i = 2 * (size_t)g_timer.used + (end ? 1 : 0);
   if (i >= g_timer.ev.size()) return;
-  hipEventRecord(g_timer.ev[i], s);
+  (void)hipEventRecord(g_timer.ev[i], s);   // a failed record shows up when the timer is read
   if (end) ++g_timer.used;
 }
 
@@ -54,6 +54,11 @@ hipError_t timed(int32_t site, hipStream_t s, F f) {
   timer_mark(site, s, true);
   return e;
 }
+
+// Fewest keys one attention workgroup takes when a row is split.
+#ifndef CSA2_MIN_SPLIT_KEYS
+#define CSA2_MIN_SPLIT_KEYS 64
+#endif
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -188,7 +193,7 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   const int64_t hg = (a->n_heads + 63) / 64;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-  const int64_t max_split = (nk + 63) / 64;        // at least 64 keys per split
+  const int64_t max_split = (nk + CSA2_MIN_SPLIT_KEYS - 1) / CSA2_MIN_SPLIT_KEYS;   // keys per split at least
   if (ns > max_split) ns = max_split;
   const int64_t min_split = (nk + 1023) / 1024;    // at most 1024 selected ids staged per split
   if (ns < min_split) ns = min_split;

@@ -240,21 +240,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
   }
   const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  const RowThreshold th = row_threshold<kSelThreads>(gh, a.k, sh.wsum, sh.pair);
-  const int bstar = th.bstar, c_above = th.c_above;
-  const uint32_t kk = th.kk;
   const int64_t crow0 = (int64_t)r * a.n_chunks * kFiltChunk;
   const uint32_t* cnt = a.cand_count + (int64_t)r * a.n_chunks;
+  // the chunks' candidate counts and the histogram are independent: both
+  // loads fly together
+  constexpr int kCpt = kMaxChunks / kSelThreads;
+  int cc[kCpt];
+#pragma unroll
+  for (int i = 0; i < kCpt; ++i) {
+    const int ch = kCpt * tid + i;
+    cc[i] = (int)cnt[min(ch, nch - 1)];
+  }
+  uint32_t hv[kHistBins / kSelThreads];
+  hist_load<kSelThreads>(gh, hv);
+  const RowThreshold th = hist_threshold<kSelThreads>(hv, a.k, sh.wsum, sh.pair);
+  const int bstar = th.bstar, c_above = th.c_above;
+  const uint32_t kk = th.kk;
 
   // flattened candidate offsets: chunk ch holds [coff[ch], coff[ch + 1])
   int n_cand;
   {
-    constexpr int kCpt = kMaxChunks / kSelThreads;
-    int cc[kCpt], loc = 0;
+    int loc = 0;
 #pragma unroll
     for (int i = 0; i < kCpt; ++i) {
       const int ch = kCpt * tid + i;
-      cc[i] = ch < nch ? (int)cnt[ch] : 0;
+      cc[i] = ch < nch ? cc[i] : 0;
       loc += cc[i];
     }
     int base = block_excl_scan<kSelThreads>(loc, sh.wsum, n_cand);
