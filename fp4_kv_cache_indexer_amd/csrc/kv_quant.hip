@@ -257,6 +257,28 @@ __global__ __launch_bounds__(128) void decode_append_kernel(AppendArgs a) {
   const uint16_t* x = a.x + (int64_t)r * kD;
   const uint16_t* z = GATE ? a.gate + (int64_t)r * kD : nullptr;
 
+  // The block summary's older members [8*(e/8), e) are not written by this
+  // launch: load them first, beside the token (clamped addresses, masked
+  // later), so the row costs one memory latency rather than two.
+  const int64_t e_ = p / M;
+  const int64_t j0 = (e_ / kBlockPos) * kBlockPos;
+  const int cnt = (int)(e_ - j0) + 1;            // members including the new entry
+  uint32_t old_w[kBlockPos - 1], old_s[kBlockPos - 1];
+  const bool summarise = a.codes && a.block_keys && (int)(p % M) == M - 1 && t < 32;
+  if (summarise) {                                // uniform within each wave
+#pragma unroll
+    for (int i = 0; i < kBlockPos - 1; ++i) {
+      const int64_t m = j0 + max(0, min(i, cnt - 2));
+      if (KF == 0) {
+        old_w[i] = *reinterpret_cast<const uint32_t*>(a.keys + (s * a.n_ent + m) * kIdxDim + 4 * t);
+        old_s[i] = 0u;
+      } else {
+        old_w[i] = *reinterpret_cast<const uint16_t*>(a.keys + (s * a.n_ent + m) * 64 + 2 * t);
+        old_s[i] = a.key_scales[(s * a.n_ent + m) * 4 + t / 8];
+      }
+    }
+  }
+
   if (a.swa) {
     const uint2 w = *reinterpret_cast<const uint2*>(x + 4 * t);
     uint32_t b = 0u;
@@ -322,41 +344,23 @@ __global__ __launch_bounds__(128) void decode_append_kernel(AppendArgs a) {
     new_key = c | (sc << 16);
   }
 
-  // ---- the summary of the entry's block over the entries written so far
-  if (!a.block_keys) return;
+  // ---- the summary of the entry's block over the entries written so far:
+  // the members loaded at the start, then the new one, in member order
+  if (!summarise) return;
   const int64_t b = e / kBlockPos;
-  const int64_t j0 = b * kBlockPos;
-  const int cnt = (int)(e - j0) + 1;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (KF == 0) {
-    const uint8_t* base = a.keys + (s * a.n_ent + j0) * kIdxDim + 4 * t;
-    uint32_t w[kBlockPos];
 #pragma unroll
-    for (int i = 0; i < kBlockPos; ++i)
-      w[i] = i < cnt - 1 ? *reinterpret_cast<const uint32_t*>(base + (int64_t)i * kIdxDim) : new_key;
-#pragma unroll
-    for (int i = 0; i < kBlockPos; ++i) {
-      if (i < cnt) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += e4m3_to_f32((w[i] >> (8 * c)) & 0xFFu);
-      }
-    }
-  } else {
-    const uint8_t* cb = a.keys + (s * a.n_ent + j0) * 64 + 2 * t;
-    const uint8_t* sb = a.key_scales + (s * a.n_ent + j0) * 4 + t / 8;
-    uint32_t cw[kBlockPos], sw[kBlockPos];
-#pragma unroll
-    for (int i = 0; i < kBlockPos; ++i) {
+  for (int i = 0; i < kBlockPos; ++i) {
+    if (i < cnt) {
       const bool old = i < cnt - 1;
-      cw[i] = old ? *reinterpret_cast<const uint16_t*>(cb + (int64_t)i * 64) : (new_key & 0xFFFFu);
-      sw[i] = old ? sb[(int64_t)i * 4] : (new_key >> 16);
-    }
+      const uint32_t w = old ? old_w[min(i, kBlockPos - 2)] : (KF == 0 ? new_key : (new_key & 0xFFFFu));
+      if (KF == 0) {
 #pragma unroll
-    for (int i = 0; i < kBlockPos; ++i) {
-      if (i < cnt) {
-        const float sv = e4m3_to_f32(sw[i]);
+        for (int c = 0; c < 4; ++c) acc[c] += e4m3_to_f32((w >> (8 * c)) & 0xFFu);
+      } else {
+        const float sv = e4m3_to_f32(old ? old_s[min(i, kBlockPos - 2)] : (new_key >> 16));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] += e2m1_to_f32((cw[i] >> (4 * c)) & 0xFu) * sv;
+        for (int c = 0; c < 4; ++c) acc[c] += e2m1_to_f32((w >> (4 * c)) & 0xFu) * sv;
       }
     }
   }
