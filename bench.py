@@ -217,7 +217,7 @@ class SchedSet:
             c["codes"] = torch.empty((B, N, 256), **u8)
             c["scales"] = torch.empty((B, N, 32), **u8)
             c["keys"] = torch.empty((B, N, 64 if self.fp4 else 128), **u8)
-            c["kscales"] = torch.empty((B, N, 4), **u8) if self.fp4 else None
+            c["key_scales"] = torch.empty((B, N, 4), **u8) if self.fp4 else None
             for b in range(B):
                 x = synth.latent_dev((1, N * m, 512), g, "normal").to(torch.bfloat16)
                 z = torch.randn((1, N * m, 512), generator=g, device="cuda").to(torch.bfloat16) if m > 1 else None
@@ -226,11 +226,11 @@ class SchedSet:
                 kb = torch.randn((1, N, 128), generator=g, device="cuda")
                 if self.fp4:
                     C.index_key_quantize(kb.to(torch.bfloat16), codes=c["keys"][b:b + 1],
-                                         scales=c["kscales"][b:b + 1])
+                                         scales=c["key_scales"][b:b + 1])
                 else:
                     c["keys"][b] = synth.to_e4m3(kb[0])
                 del kb
-            c["summ"] = ((C.index_block_summary_fp4(c["keys"], c["kscales"]) if self.fp4
+            c["summ"] = ((C.index_block_summary_fp4(c["keys"], c["key_scales"]) if self.fp4
                           else C.index_block_summary(c["keys"])) if c["hier"] else None)
             c["pend_x"] = torch.zeros((B, m - 1, 512), **bf) if m > 1 else None
             c["pend_z"] = torch.zeros((B, m - 1, 512), **bf) if m > 1 else None
@@ -255,14 +255,17 @@ class SchedSet:
         groups = sorted({ly.group for ly in self.layers if ly.group >= 0})
         self.gidx = {gr: torch.empty((B, k), dtype=torch.int32, device="cuda") for gr in groups}
         dec = self.caches[3]
-        self.blocks = torch.empty((B, w["keep"]), dtype=torch.int32, device="cuda") if dec["hier"] else None
+        # kept blocks of every hierarchical Full layer (the decoder's is its Reindex layers' pool)
+        self.blocks_by_cache = {ci: torch.empty((B, w["keep"]), dtype=torch.int32, device="cuda")
+                                for ci, c in enumerate(self.caches) if c["hier"]}
+        self.blocks = self.blocks_by_cache.get(3)
         self.ws_idx = {}
         for ci, c in enumerate(self.caches):
             self.ws_idx[ci] = torch.zeros(max(256, C.indexer_topk_workspace(
                 self.q_idx[self.full_layer[ci]], c["keys"], k, block_keys=c["summ"], keep_blocks=w["keep"],
-                key_scales=c["kscales"])), **u8)
+                key_scales=c["key_scales"])), **u8)
         self.ws_pool = torch.zeros(max(256, C.indexer_topk_workspace(
-            self.q_idx[self.full_layer[3]], dec["keys"], k, cand_blocks=self.blocks, key_scales=dec["kscales"])),
+            self.q_idx[self.full_layer[3]], dec["keys"], k, cand_blocks=self.blocks, key_scales=dec["key_scales"])),
             **u8)
         self.out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
@@ -279,30 +282,13 @@ def step_sched(w, s):
     (Full / Reindex) and attention."""
     for ci, c in enumerate(s.caches):
         C.decode_append(c["x_new"], s.pos, c["codes"], c["scales"], c["k_new"], c["keys"], m=c["m"],
-                        gate=c["z_new"], pend_x=c["pend_x"], pend_gate=c["pend_z"], key_scales=c["kscales"],
+                        gate=c["z_new"], pend_x=c["pend_x"], pend_gate=c["pend_z"], key_scales=c["key_scales"],
                         block_keys=c["summ"], swa=s.rings[s.full_layer[ci]])
     C.window_append(s.ring_x, s.ring_pos, s.rings.view(-1, SCH.WINDOW, 512), row_seq=s.ring_rows)
-    dec = s.caches[3]
-    for ly in s.layers:
-        if ly.mode == "swa_only":
-            C.sparse_attn_decode(s.q[ly.index], None, None, None, swa=s.rings[ly.index], swa_len=s.swa_len,
-                                 out=s.out, lse=s.lse, workspace=s.ws_attn)
-            continue
-        c = s.caches[ly.cache]
-        idx = s.gidx[ly.group]
-        if ly.mode == "full":
-            C.indexer_topk(s.q_idx[ly.index], c["keys"], w["k"], block_keys=c["summ"], keep_blocks=w["keep"],
-                           out_idx=idx, out_blocks=s.blocks if ly.cache == 3 else None, workspace=s.ws_idx[ly.cache],
-                           key_scales=c["kscales"])
-        elif ly.mode == "reindex":
-            if s.blocks is not None:
-                C.indexer_topk(s.q_idx[ly.index], dec["keys"], w["k"], cand_blocks=s.blocks, out_idx=idx,
-                               workspace=s.ws_pool, key_scales=dec["kscales"])
-            else:
-                C.indexer_topk(s.q_idx[ly.index], dec["keys"], w["k"], out_idx=idx, workspace=s.ws_idx[3],
-                               key_scales=dec["kscales"])
-        C.sparse_attn_decode(s.q[ly.index], c["codes"], c["scales"], idx, swa=s.rings[ly.index],
-                             swa_len=s.swa_len, out=s.out, lse=s.lse, workspace=s.ws_attn)
+    SCH.decode_layers(s.layers, s.caches, s.rings, s.swa_len, s.q, s.q_idx, w["k"], w["keep"],
+                      out=[s.out] * len(s.layers), lse=[s.lse] * len(s.layers), sel=s.gidx,
+                      blocks=s.blocks_by_cache, ws_idx=s.ws_idx, ws_pool={3: s.ws_pool},
+                      ws_attn=s.ws_attn)
 
 
 def sched_work(T, B=1, H=64, k=512, keep=2048, window=SCH.WINDOW, fp4=False):
