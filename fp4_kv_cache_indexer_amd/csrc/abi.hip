@@ -55,6 +55,11 @@ hipError_t timed(int32_t site, hipStream_t s, F f) {
   return e;
 }
 
+// Attention workgroups that run at once (one per CU of MI355X).
+#ifndef CSA2_RESIDENT_ATTN_WGS
+#define CSA2_RESIDENT_ATTN_WGS 256
+#endif
+
 // Fewest keys one attention workgroup takes when a row is split.
 #ifndef CSA2_MIN_SPLIT_KEYS
 #define CSA2_MIN_SPLIT_KEYS 64
@@ -163,7 +168,7 @@ int32_t score_chunk(int64_t n_items, int64_t rows) {
 // ---- attention plan --------------------------------------------------------
 
 struct AttnPlan {
-  int32_t n_split, keys_per_split;
+  int32_t n_split, keys_per_split, heads_per_wg;
   size_t off_o, off_ml, total;
 };
 
@@ -190,10 +195,20 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
     if (a->lse && !aligned(a->lse, 4)) return fail(CSA2_EINVAL, "attn: lse misaligned");
   }
   const int64_t nk = (int64_t)a->top_k + (has_swa ? a->swa_cap : 0);
-  const int64_t hg = (a->n_heads + 63) / 64;
+  const int64_t max_split = (nk + CSA2_MIN_SPLIT_KEYS - 1) / CSA2_MIN_SPLIT_KEYS;   // keys per split at least
+  // Very few rows: one 16-head group per workgroup, so a workgroup's chain
+  // of dependent steps is short (one score wave, light PV per wave), as long
+  // as every such workgroup (one per CU: their LDS) runs at once at the
+  // full key split; each of them gathers the row's keys (mostly from L2).
+  // Otherwise up to 64 heads per workgroup share one gather and
+  // dequantisation (measured: 8 rows x 64 heads run 19.9 us this way and
+  // 25.6 us as 320 16-head workgroups).
+  const int64_t wg16 = (int64_t)a->n_rows * ((a->n_heads + 15) / 16);
+  p->heads_per_wg = (wg16 * max_split <= CSA2_RESIDENT_ATTN_WGS) ? 16 : 64;
+  const int64_t hg = (a->n_heads + p->heads_per_wg - 1) / p->heads_per_wg;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-  const int64_t max_split = (nk + CSA2_MIN_SPLIT_KEYS - 1) / CSA2_MIN_SPLIT_KEYS;   // keys per split at least
+  if (p->heads_per_wg == 16) ns = max_split;        // shortest chains
   if (ns > max_split) ns = max_split;
   const int64_t min_split = (nk + 1023) / 1024;    // at most 1024 selected ids staged per split
   if (ns < min_split) ns = min_split;
@@ -529,6 +544,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
   k.out = a->out;
   k.lse = a->lse;
   k.n_split = p.n_split;
+  k.heads_per_wg = p.heads_per_wg;
   k.keys_per_split = p.keys_per_split;
   k.part_o = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_o) : nullptr;
   k.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ml) : nullptr;

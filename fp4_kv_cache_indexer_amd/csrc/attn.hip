@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.n_heads;
-  const int hbase = blockIdx.z * kHeadsPerWG;
-  const int HG = min(kHeadsPerWG, H - hbase) / 16;          // head groups here: 1, 2 or 4
+  const int hbase = blockIdx.z * a.heads_per_wg;
+  const int HG = min(a.heads_per_wg, H - hbase) / 16;       // head groups here: 1, 2 or 4
   const bool qk_wave = wave < HG;
   // PV: waves per head group, head group and first channel tile of this wave
   const int wph = kAttnWaves / HG;
@@ -405,7 +405,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)sizeof(AttnShared));
   if (attr != hipSuccess) return attr;
-  const int hblocks = (a.n_heads + kHeadsPerWG - 1) / kHeadsPerWG;
+  const int hblocks = (a.n_heads + a.heads_per_wg - 1) / a.heads_per_wg;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hblocks),
                      dim3(kAttnThreads), sizeof(AttnShared), stream, a);
   return hipGetLastError();

@@ -103,6 +103,7 @@ struct AttnArgs {
   float sm_scale_log2;      // sm_scale * log2(e)
   float* out;
   float* lse;
+  int32_t heads_per_wg;     // heads one workgroup owns: 16 or 64
   int32_t n_split;          // key splits per row
   int32_t keys_per_split;   // multiple of the key chunk
   float* part_o;            // [n_split][R][H][512] when n_split > 1
