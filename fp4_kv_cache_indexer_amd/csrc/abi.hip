@@ -55,9 +55,9 @@ hipError_t timed(int32_t site, hipStream_t s, F f) {
   return e;
 }
 
-// Attention workgroups that run at once (one per CU of MI355X).
+// 16-head attention workgroups that run at once (two per CU of MI355X).
 #ifndef CSA2_RESIDENT_ATTN_WGS
-#define CSA2_RESIDENT_ATTN_WGS 256
+#define CSA2_RESIDENT_ATTN_WGS 512
 #endif
 
 // Fewest keys one attention workgroup takes when a row is split.
@@ -196,13 +196,11 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   }
   const int64_t nk = (int64_t)a->top_k + (has_swa ? a->swa_cap : 0);
   const int64_t max_split = (nk + CSA2_MIN_SPLIT_KEYS - 1) / CSA2_MIN_SPLIT_KEYS;   // keys per split at least
-  // Very few rows: one 16-head group per workgroup, so a workgroup's chain
-  // of dependent steps is short (one score wave, light PV per wave), as long
-  // as every such workgroup (one per CU: their LDS) runs at once at the
-  // full key split; each of them gathers the row's keys (mostly from L2).
-  // Otherwise up to 64 heads per workgroup share one gather and
-  // dequantisation (measured: 8 rows x 64 heads run 19.9 us this way and
-  // 25.6 us as 320 16-head workgroups).
+  // Few rows: one 16-head group per workgroup (the narrow kernel: a short
+  // chain of dependent steps, two workgroups per CU), as long as every such
+  // workgroup of the full key split runs at once; each of them gathers the
+  // row's keys (mostly from L2).  Otherwise up to 64 heads per workgroup
+  // share one gather and dequantisation.
   const int64_t wg16 = (int64_t)a->n_rows * ((a->n_heads + 15) / 16);
   p->heads_per_wg = (wg16 * max_split <= CSA2_RESIDENT_ATTN_WGS) ? 16 : 64;
   const int64_t hg = (a->n_heads + p->heads_per_wg - 1) / p->heads_per_wg;

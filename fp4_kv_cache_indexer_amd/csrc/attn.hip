@@ -17,6 +17,7 @@
 // and the output tiles.  Rows with few keys per workgroup are split over
 // several workgroups whose (O, max, sum) partials are merged by
 // attn_combine_kernel.
+#include "attn_dev.h"
 #include "csa2_dev.h"
 #include "csa2_launch.h"
 
@@ -34,13 +35,14 @@ __device__ __forceinline__ int kt_off(int c, int byte) {
   return c * kKtStride + ((((byte >> 4) ^ (c >> 3)) & 3) << 4) + (byte & 15);
 }
 
-constexpr int kMaxKeysPerSplit = 1024;          // selected ids staged in LDS per workgroup
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kHeadsPerWG = 64;                 // up to 4 head groups of 16 per workgroup
-constexpr int kMaxPvTiles = (kD / 16) * (kHeadsPerWG / 16) / kAttnWaves;   // 16 channel tiles
 constexpr int kPsLo = kKeyChunk * 2;            // offset of P's low fp16 terms in a head row
 constexpr int kPsStride = kKeyChunk * 4 + 16;   // bytes per head row of P (hi + lo fp16 + pad)
+
+constexpr int kHeadsPerWG = 64;                 // up to 4 head groups of 16 per workgroup
+constexpr int kMaxPvTiles = (kD / 16) * (kHeadsPerWG / 16) / kAttnWaves;   // 16 channel tiles
+constexpr int kMaxKeysPerSplit = 1024;          // selected ids staged in LDS per workgroup
 
 struct AttnShared {
   uint8_t kr[kKeyChunk * kKrStride];
@@ -52,34 +54,7 @@ struct AttnShared {
   int32_t sidx[kMaxKeysPerSplit];
 };
 
-typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-
-// 8 FP4 channels (one word, channel 2j in the low nibble of byte j) times the
-// group scale, as float32.  The hardware decode is exact for a unit scale;
-// the product with an E4M3 scale has at most 6 significant bits, so it is
-// exact in float32, bf16 and fp16 alike.
-__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float sv, float* f) {
-  v2f t;
-  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); f[0] = t[0] * sv; f[1] = t[1] * sv;
-  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); f[2] = t[0] * sv; f[3] = t[1] * sv;
-  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); f[4] = t[0] * sv; f[5] = t[1] * sv;
-  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); f[6] = t[0] * sv; f[7] = t[1] * sv;
-}
-
-// 8 E4M3 bytes (two words) as float32 (exact).
-__device__ __forceinline__ void fp8x8_to_f32(uint32_t w0, uint32_t w1, float* f) {
-  v2f t;
-  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false); f[0] = t[0]; f[1] = t[1];
-  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);  f[2] = t[0]; f[3] = t[1];
-  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false); f[4] = t[0]; f[5] = t[1];
-  t = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);  f[6] = t[0]; f[7] = t[1];
-}
-
-// Two exactly representable floats as a bf16 pair (their top halves).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
 
 // Two floats as an fp16 pair; exact inputs pass unchanged.
 __device__ __forceinline__ uint32_t pack_f16_exact(float lo, float hi) {
@@ -116,8 +91,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int H = a.n_heads;
-  const int hbase = blockIdx.z * a.heads_per_wg;
-  const int HG = min(a.heads_per_wg, H - hbase) / 16;       // head groups here: 1, 2 or 4
+  const int hbase = blockIdx.z * kHeadsPerWG;
+  const int HG = min(kHeadsPerWG, H - hbase) / 16;          // head groups here: 1, 2 or 4
   const bool qk_wave = wave < HG;
   // PV: waves per head group, head group and first channel tile of this wave
   const int wph = kAttnWaves / HG;
@@ -401,11 +376,12 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
+  if (a.heads_per_wg == 16) return launch_sparse_attn_narrow(a, stream);
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_attn_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)sizeof(AttnShared));
   if (attr != hipSuccess) return attr;
-  const int hblocks = (a.n_heads + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int hblocks = (a.n_heads + kHeadsPerWG - 1) / kHeadsPerWG;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hblocks),
                      dim3(kAttnThreads), sizeof(AttnShared), stream, a);
   return hipGetLastError();
