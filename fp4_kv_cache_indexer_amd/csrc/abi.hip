@@ -55,10 +55,16 @@ hipError_t timed(int32_t site, hipStream_t s, F f) {
   return e;
 }
 
-// 16-head attention workgroups that run at once (two per CU of MI355X).
+// 16-head attention workgroups that run at once (two per CU of MI355X), and
+// the most keys one of them takes.
 #ifndef CSA2_RESIDENT_ATTN_WGS
 #define CSA2_RESIDENT_ATTN_WGS 512
 #endif
+// (measured with the combine: 32 rows x 64 heads in 5-chunk narrow splits
+// 27.6 + 7.9 us against 24.2 + 10.1 us wide; 64 rows in 10-chunk splits
+// 40.5 + 10.6 against 32.6 + 11.7; 8 rows in 2-chunk splits 14.3 + 5.7
+// against 19.9 + 5.6)
+#define CSA2_NARROW_MAX_SPLIT_KEYS 128
 
 // Fewest keys one attention workgroup takes when a row is split.
 #ifndef CSA2_MIN_SPLIT_KEYS
@@ -202,11 +208,12 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   // row's keys (mostly from L2).  Otherwise up to 64 heads per workgroup
   // share one gather and dequantisation.
   const int64_t wg16 = (int64_t)a->n_rows * ((a->n_heads + 15) / 16);
-  p->heads_per_wg = (wg16 * max_split <= CSA2_RESIDENT_ATTN_WGS) ? 16 : 64;
+  const int64_t ns16 = wg16 > 0 ? std::min(max_split, (int64_t)CSA2_RESIDENT_ATTN_WGS / wg16) : 0;
+  p->heads_per_wg = (ns16 >= 1 && (nk + ns16 - 1) / ns16 <= CSA2_NARROW_MAX_SPLIT_KEYS) ? 16 : 64;
   const int64_t hg = (a->n_heads + p->heads_per_wg - 1) / p->heads_per_wg;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-  if (p->heads_per_wg == 16) ns = max_split;        // shortest chains
+  if (p->heads_per_wg == 16) ns = ns16;             // as many splits as run at once
   if (ns > max_split) ns = max_split;
   const int64_t min_split = (nk + 1023) / 1024;    // at most 1024 selected ids staged per split
   if (ns < min_split) ns = min_split;

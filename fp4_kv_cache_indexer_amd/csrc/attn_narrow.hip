@@ -4,8 +4,8 @@
 //
 // Same mathematics as sparse_attn_kernel (attn.hip), shaped for latency when
 // the rows alone cannot fill the GPU: a row's heads are spread over 16-head
-// workgroups and its keys over 64-key splits, and each workgroup needs only
-// ~51 KB of LDS and 128 registers per lane, so two share a CU.  Per chunk of
+// workgroups and its keys over splits, and each workgroup needs only ~53 KB
+// of LDS and 128 registers per lane, so two share a CU.  Per chunk of
 // 32 keys:
 //   * all 512 threads gather the selected FP4 entries (256 code + 32 E4M3
 //     scale bytes each) or FP8 window tokens and dequantise them exactly into
@@ -33,7 +33,7 @@ constexpr int kHeads = 16;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTilesPerWave = (kD / 16) / kWaves;   // 4 output channel tiles per wave
-constexpr int kMaxSplitKeys = 64;              // keys of one workgroup (the plan's split)
+constexpr int kMaxSplitKeys = 512;             // keys of one workgroup at most
 constexpr float kSlack = 8.0f;                 // log2 growth of the max tolerated before rescaling
 
 struct NarrowShared {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
 
   // stage the split's selected ids and the group's Q; all loads fly together
   const int nst = max(0, min(k0 + a.keys_per_split, a.top_k) - k0);
-  if (tid < nst) sh.sidx[tid] = idxr[k0 + tid];
+  for (int i = tid; i < nst; i += kThreads) sh.sidx[i] = idxr[k0 + i];
 #pragma unroll
   for (int i = 0; i < kHeads * kRow / 16 / kThreads; ++i) {
     const int u = i * kThreads + tid;              // 16-byte unit: head u/64, segment u%64
