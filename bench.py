@@ -642,6 +642,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sites", action="store_true",
+                    help="also print the event-timed average duration of every launch site")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a copy kernel of this size (for scaling rocprofv3 HBM counters)")
@@ -740,6 +742,12 @@ def main():
     attn_tf = attn_flops(w) / avg_a / 1e12
     print(f"[bench] attn: {n_a} launches, avg {avg_a * 1e6:.2f} us, {attn_tf:.1f} TFLOP/s algorithmic",
           file=sys.stderr, flush=True)
+
+    if args.sites:
+        for name in C.SITES:
+            n_x, avg_x = time_site(name)
+            if n_x:
+                print(f"[bench] site {name}: {n_x} launches, avg {avg_x * 1e6:.2f} us", file=sys.stderr, flush=True)
 
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)

@@ -482,117 +482,145 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
 constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kRowCap = 12288;                 // candidates held in LDS
-constexpr int kRowU = 2;                       // float4 loads per thread per round
-constexpr int kRowSub = kRowThreads * 4;       // items per sub-round
-constexpr int kRowRound = kRowSub * kRowU;     // items per round (one barrier)
+constexpr int kRowU = 4;                        // float4 loads per thread per round
+constexpr int kRowSub = kRowThreads * 4;        // items per sub-round (one float4 per thread)
+constexpr int kRowRound = kRowSub * kRowU;      // items per round (one barrier)
 
 struct RowShared {
   uint64_t cbuf[kRowCap];
   int32_t sel_pos[kMaxTopK];
   float sel_score[kMaxTopK];
-  int wtot[2][kRowU][kRowWaves];
+  int wtot[2][kRowWaves][kRowU];
   int wsum[kRowWaves];
   uint32_t hist[256];
   int pair[3];
   int digit, above, dcount;
 };
 
+// One round's raw loads for one thread: items base + u*kRowSub + 4 tid + j
+// (u, j < 4; the loads of a wave are contiguous) and, in pool mode, the id of
+// the block each float4 belongs to.
+struct RowRound {
+  float4 v[kRowU];
+  int32_t blk[kRowU];
+};
+
 // Raw loads of one round (addresses clamped into the row; masking happens in
-// row_compact), unconditional so that nothing waits on them before use.  In
-// pool mode each thread's 4 items of a sub-round share one block, whose id
-// comes with them (other modes load a discarded word of the score row).
+// row_compact), unconditional so that nothing waits on them before use.
+// Other modes than pool load a discarded word of the score row as block ids.
 __device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float* srow, int64_t base,
-                                         float4 (&v)[kRowU], int32_t (&blk)[kRowU]) {
+                                         RowRound& R) {
   const bool pool = a.im.mode == kItemsPool;
   const int32_t* lrow = pool ? a.im.list + (int64_t)r * a.im.list_len : reinterpret_cast<const int32_t*>(srow);
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
-    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * threadIdx.x;
-    v[u] = *reinterpret_cast<const float4*>(srow + (i0 < a.row_stride ? i0 : 0));
-    blk[u] = lrow[pool && (i0 >> 3) < a.im.list_len ? (i0 >> 3) : 0];
+    const int64_t iu = base + (int64_t)u * kRowSub + 4 * threadIdx.x;
+    R.v[u] = *reinterpret_cast<const float4*>(srow + (iu < a.row_stride ? iu : 0));
+    R.blk[u] = lrow[pool && (iu >> 3) < a.im.list_len ? (iu >> 3) : 0];
   }
 }
 
-// Appends the round's items in bin b* or above to cbuf in item order: wave
-// offsets from ballots, round offsets from the per-wave totals in LDS.
+// Smallest score whose composite key lies in bin b* or above, as a float:
+// for non-NaN x, x >= it exactly when order_key(x) >= b* << (32 - kHistBits)
+// (the float order is the key order, and -0 and +0 share a key and compare
+// equal).  NaN, the mark of items a row cannot see, compares false.  Bins
+// below that of -inf hold only NaN patterns, so their threshold is -inf;
+// bins above that of +inf hold none but NaN, whose threshold keeps nothing.
+__device__ __forceinline__ float bin_floor(int bstar) {
+  if (bstar < 0) return -INFINITY;                           // every visible item is kept
+  const uint32_t k0 = (uint32_t)bstar << (32 - kHistBits);
+  const float f = order_key_inv(k0);
+  return (f != f && k0 < 0x80000000u) ? -INFINITY : f;
+}
+
+// Appends the round's items at or above the threshold to cbuf in item order.
+// Within a sub-round u an item's slot counts the kept items of lower lanes
+// (ballots of the bits of each lane's count) and of lower waves (per-wave
+// totals in LDS, one lane per (u, wave) summed by a row scan).
 __device__ __forceinline__ int row_compact(const SelectArgs& a, int r, int64_t nv, int64_t n_row, int64_t base,
-                                           int bstar,
-                                           const float4 (&v)[kRowU], const int32_t (&blk)[kRowU], uint64_t* cbuf,
-                                           int cap, int written, int parity, RowShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t ok[kRowU][4];
-  int fl[kRowU], off[kRowU];
-  const float nan = __uint_as_float(0x7FC00000u);
+                                           float thr, const RowRound& R, uint64_t* cbuf, int cap, int written,
+                                           int parity, RowShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // items of the row from this thread's first one on (clamped to 32 bits)
+  int rem = (int)max((int64_t)0, min(n_row - base - 4 * tid, (int64_t)kRowRound));
+  asm volatile("" : "+v"(rem));                // 32-bit compares below, not 64-bit ones
+  uint32_t fl[kRowU];
+  int below[kRowU], wt[kRowU];
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
-    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * tid;
-    const float x[4] = {i0 + 0 < n_row ? v[u].x : nan, i0 + 1 < n_row ? v[u].y : nan,
-                        i0 + 2 < n_row ? v[u].z : nan, i0 + 3 < n_row ? v[u].w : nan};
+    const float x[4] = {R.v[u].x, R.v[u].y, R.v[u].z, R.v[u].w};
     fl[u] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[u][j] = order_key(x[j]);
-      const bool keep = (x[j] == x[j]) && (int)(ok[u][j] >> (32 - kHistBits)) >= bstar;
-      fl[u] |= (int)keep << j;
-    }
-    int o = 0, t = 0;
+    for (int j = 0; j < 4; ++j) fl[u] |= (uint32_t)(x[j] >= thr && u * kRowSub + j < rem) << j;
+    const int c = __popc(fl[u]);
+    below[u] = 0;
+    wt[u] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint64_t b = __ballot((fl[u] >> j) & 1);
-      o += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-      t += __popcll(b);
+    for (int b = 0; b < 3; ++b) {
+      const uint64_t m = __ballot((c >> b) & 1);
+      below[u] += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+      wt[u] += __popcll(m) << b;
     }
-    off[u] = o;
-    if (lane == 0) sh.wtot[parity][u][wave] = t;
   }
+  if (lane == 0) *reinterpret_cast<int4*>(sh.wtot[parity][wave]) = make_int4(wt[0], wt[1], wt[2], wt[3]);
   lds_barrier();                               // the next round's loads stay in flight
+  // lane (u = lane / 16, w = lane % 16) holds wave w's count of sub-round u;
+  // an inclusive scan over each row of 16 lanes gives the waves' prefixes
+  int sc = sh.wtot[parity][lane & 15][lane >> 4];
+  sc += __builtin_amdgcn_update_dpp(0, sc, 0x111, 0xF, 0xF, true);   // row_shr:1
+  sc += __builtin_amdgcn_update_dpp(0, sc, 0x112, 0xF, 0xF, true);   // row_shr:2
+  sc += __builtin_amdgcn_update_dpp(0, sc, 0x114, 0xF, 0xF, true);   // row_shr:4
+  sc += __builtin_amdgcn_update_dpp(0, sc, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int64_t i0 = base + 4 * tid;
+  int start = written;
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
-    int pre = 0, tot = 0;
+    const int incl = __builtin_amdgcn_readlane(sc, 16 * u + wave);   // waves <= this one
+    const int tot = __builtin_amdgcn_readlane(sc, 16 * u + 15);
+    int slot = start + incl - wt[u] + below[u];
+    const int64_t iu = i0 + (int64_t)u * kRowSub;
+    if (a.im.mode == kItemsPool) {                             // uniform
+      const int64_t pb = (int64_t)R.blk[u] * kBlockPos + (iu & 7);
 #pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      const int t = sh.wtot[parity][u][w];
-      pre += w < wave ? t : 0;
-      tot += t;
+      for (int j = 0; j < 4; ++j)
+        if ((fl[u] >> j) & 1) {
+          const float xj = j == 0 ? R.v[u].x : j == 1 ? R.v[u].y : j == 2 ? R.v[u].z : R.v[u].w;
+          if (slot < cap) cbuf[slot] = comp_key(order_key(xj), pb + j);
+          ++slot;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((fl[u] >> j) & 1) {
+          const float xj = j == 0 ? R.v[u].x : j == 1 ? R.v[u].y : j == 2 ? R.v[u].z : R.v[u].w;
+          const int64_t pos = a.im.mode == kItemsCand ? item_pos(a.im, r, iu + j, nv) : iu + j;
+          if (slot < cap) cbuf[slot] = comp_key(order_key(xj), pos);
+          ++slot;
+        }
     }
-    int slot = written + pre + off[u];
-    const int64_t i0 = base + (int64_t)u * kRowSub + 4 * tid;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((fl[u] >> j) & 1) {
-        // kept items are visible ones: pool positions come from the block id
-        const int64_t pos = a.im.mode == kItemsPool   ? (int64_t)blk[u] * kBlockPos + ((i0 + j) & 7)
-                            : a.im.mode == kItemsCand ? item_pos(a.im, r, i0 + j, nv)
-                                                      : i0 + j;
-        if (slot < cap) cbuf[slot] = comp_key(ok[u][j], pos);
-        ++slot;
-      }
-    written += tot;
+    start += tot;
   }
-  return written;
+  return start;
 }
 
 // Collect, select and write one row with the candidates in cbuf (LDS or
 // global).  Returns the number of ids written to the output (<= k).
 __device__ __forceinline__ int row_select(const SelectArgs& a, int r, int64_t nv, int64_t n_row,
-                                          const RowThreshold& th, float4 (&va)[kRowU], int32_t (&ba)[kRowU],
-                                          uint64_t* cbuf, int cap,
+                                          const RowThreshold& th, RowRound& A, uint64_t* cbuf, int cap,
                                           RowShared& sh, int32_t* oi, float* os, bool sort) {
   const int tid = threadIdx.x;
   const float* srow = a.scores + (int64_t)r * a.row_stride;
 
-  // 1. candidates in item order, loads one round ahead (va holds round 0)
+  // 1. candidates in item order (A holds round 0, loaded before the threshold
+  // search; a row longer than one round waits for each further round)
+  const float thr = bin_floor(th.bstar);
   int written = 0, parity = 0;
-  float4 vb[kRowU];
-  int32_t bb[kRowU];
-  for (int64_t base = 0; base < n_row; base += 2 * kRowRound) {
-    row_load(a, r, srow, base + kRowRound, vb, bb);
-    written = row_compact(a, r, nv, n_row, base, th.bstar, va, ba, cbuf, cap, written, parity, sh);
+  for (int64_t base = 0;; base += kRowRound) {
+    written = row_compact(a, r, nv, n_row, base, thr, A, cbuf, cap, written, parity, sh);
     parity ^= 1;
     if (base + kRowRound >= n_row) break;
-    row_load(a, r, srow, base + 2 * kRowRound, va, ba);
-    written = row_compact(a, r, nv, n_row, base + kRowRound, th.bstar, vb, bb, cbuf, cap, written, parity, sh);
-    parity ^= 1;
+    row_load(a, r, srow, base + kRowRound, A);
   }
   __syncthreads();
   const int n_cand = min(written, cap);        // equal to th.n_cand: the histogram counted these items
@@ -667,14 +695,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
   if (n_row > 0) {                                             // uniform
     uint32_t hv[kHistBins / kRowThreads];
     hist_load<kRowThreads>(gh, hv);
-    float4 va[kRowU];                                          // the first round's scores fly
-    int32_t ba[kRowU];                                         // during the threshold search
-    row_load(a, r, a.scores + (int64_t)r * a.row_stride, 0, va, ba);
+    RowRound A;                                                // the first round's scores fly
+    row_load(a, r, a.scores + (int64_t)r * a.row_stride, 0, A);   // during the threshold search
     const RowThreshold th = hist_threshold<kRowThreads>(hv, a.k, sh.wsum, sh.pair);
     if (th.n_cand <= kRowCap)
-      nsel = row_select(a, r, nv, n_row, th, va, ba, sh.cbuf, kRowCap, sh, oi, os, sort);
+      nsel = row_select(a, r, nv, n_row, th, A, sh.cbuf, kRowCap, sh, oi, os, sort);
     else
-      nsel = row_select(a, r, nv, n_row, th, va, ba, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
+      nsel = row_select(a, r, nv, n_row, th, A, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
                         a.n_chunks * kFiltChunk, sh, oi, os, sort);
   }
   if (sort) {                                                  // candidate lists come in any order
