@@ -161,12 +161,13 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
 
 int32_t score_chunk(int64_t n_items, int64_t rows) {
   // one full round of resident workgroups: as many chunks as fit on the
-  // device at once (no tail round), in multiples of 256 items
-  // (4 waves x 4 tiles x 16)
+  // device at once (no tail round), in whole 16-item tiles, so that every
+  // slot gets a chunk and no compute unit takes a third more work than
+  // another (a wave's last group of tiles may be partial)
   const int64_t slots = csa2::score_resident_wgs();
   const int64_t per_row_wgs = rows >= slots ? 1 : slots / rows;
   int64_t c = (n_items + per_row_wgs - 1) / per_row_wgs;
-  c = (c + 255) / 256 * 256;
+  c = (c + 15) / 16 * 16;
   if (c < 256) c = 256;
   return (int32_t)c;
 }

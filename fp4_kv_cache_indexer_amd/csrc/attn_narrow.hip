@@ -41,7 +41,8 @@ struct NarrowShared {
   uint8_t q[kHeads * kRow];                    // Q of the group, swizzled rows
   uint4 p[kHeads * 4][2];                      // per (head, lane group): P hi, P lo
   float alpha[kHeads];
-  float lsum[kHeads];
+  float mx[2][kHeads];                         // the two key halves' chunk maxima
+  float lsum[2][kHeads];                       // the two key halves' weight sums
   int32_t kvalid[kChunk];
   int32_t sidx[kMaxSplitKeys];
 };
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
     const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)r * H + hbase + h) * kD + seg * 8);
     *reinterpret_cast<uint4*>(sh.q + h * kRow + ((seg ^ tile_sw(h)) << 4)) = v;
   }
-  float m_run = -INFINITY, l_run = 0.0f;            // wave 0: head n
+  float m_run = -INFINITY, l_run = 0.0f;            // waves 0, 1: head n, own key half
   v4f acc[kTilesPerWave];
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -170,35 +171,43 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
     if (kc + kChunk < k1) issue(kc + kChunk, G);
     lds_barrier();
 
-    // ---- wave 0: scores, softmax, P
-    if (wave == 0) {
+    // ---- waves 0 and 1: scores of keys 16w..16w+15, softmax, P.  Both keep
+    // the same reference max (from both halves' maxima, exchanged in LDS)
+    // and each sums the weights of its own keys.
+    float s[4];
+    if (wave < 2) {
       int qk_b = qk_base;
       asm volatile("" : "+v"(qk_b));
-      v4f st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
+      const int toff = wave * 16 * kRow;
+      // two accumulators (even and odd channel steps) halve the dependent
+      // MFMA chain
+      v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const int off = (qk_b ^ ((ks & 3) << 6)) + (ks >> 2) * 256;
-        const v8bf qb = *reinterpret_cast<const v8bf*>(sh.q + off);
-        const v8bf ka0 = *reinterpret_cast<const v8bf*>(sh.tile + off);
-        const v8bf ka1 = *reinterpret_cast<const v8bf*>(sh.tile + off + 16 * kRow);
-        st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb, st0, 0, 0, 0);
-        st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb, st1, 0, 0, 0);
-        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bounded read-ahead
+      for (int ks = 0; ks < kD / 32; ks += 2) {
+        const int off0 = (qk_b ^ ((ks & 3) << 6)) + (ks >> 2) * 256;
+        const int off1 = (qk_b ^ (((ks + 1) & 3) << 6)) + ((ks + 1) >> 2) * 256;
+        const v8bf qa = *reinterpret_cast<const v8bf*>(sh.q + off0);
+        const v8bf ka = *reinterpret_cast<const v8bf*>(sh.tile + off0 + toff);
+        const v8bf qb = *reinterpret_cast<const v8bf*>(sh.q + off1);
+        const v8bf kb = *reinterpret_cast<const v8bf*>(sh.tile + off1 + toff);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qa, sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, sb, 0, 0, 0);
+        if ((ks & 7) == 6) __builtin_amdgcn_sched_barrier(0);   // bounded read-ahead
       }
-      const int4 v0 = *reinterpret_cast<const int4*>(&sh.kvalid[4 * g]);
-      const int4 v1 = *reinterpret_cast<const int4*>(&sh.kvalid[16 + 4 * g]);
-      const int vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      float s[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = vv[i] ? st0[i] * a.sm_scale_log2 : -INFINITY;
-        s[4 + i] = vv[4 + i] ? st1[i] * a.sm_scale_log2 : -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, s[j]);
+      const v4f st = sa + sb;
+      const int4 vv = *reinterpret_cast<const int4*>(&sh.kvalid[16 * wave + 4 * g]);
+      s[0] = vv.x ? st[0] * a.sm_scale_log2 : -INFINITY;
+      s[1] = vv.y ? st[1] * a.sm_scale_log2 : -INFINITY;
+      s[2] = vv.z ? st[2] * a.sm_scale_log2 : -INFINITY;
+      s[3] = vv.w ? st[3] * a.sm_scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (g == 0) sh.mx[wave][n] = mx;
+    }
+    lds_barrier();
+    if (wave < 2) {
+      const float mx = fmaxf(sh.mx[0][n], sh.mx[1][n]);
       // the reference max moves only when the chunk's max exceeds it by more
       // than the slack (weights stay below 2^slack); only then are the
       // accumulators rescaled
@@ -206,12 +215,13 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
       const float m_new = move ? mx : m_run;
       const float alpha = (move && m_run != -INFINITY) ? exp2f(m_run - m_new) : 1.0f;
       m_run = m_new;
-      uint32_t ph[4], pl[4];
+      uint32_t ph[2], pl[2];
       float psum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float p0 = (s[j] == -INFINITY) ? 0.0f : exp2f(s[j] - m_new);
-        const float p1 = (s[j + 1] == -INFINITY) ? 0.0f : exp2f(s[j + 1] - m_new);
+      for (int j = 0; j < 4; j += 2) {
+        // the hardware exp2 (weights below 2^-126 may flush to zero)
+        const float p0 = (s[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[j] - m_new);
+        const float p1 = (s[j + 1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[j + 1] - m_new);
         const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
         const float hf0 = __uint_as_float(h0 << 16), hf1 = __uint_as_float(h1 << 16);
         const uint32_t l0 = bf16_rne(p0 - hf0), l1 = bf16_rne(p1 - hf1);
@@ -223,9 +233,10 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
-      sh.p[n * 4 + g][0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-      sh.p[n * 4 + g][1] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-      if (g == 0) sh.alpha[n] = alpha;
+      // k-slots 0-3 (keys 4g..4g+3) from wave 0, 4-7 (16+4g..) from wave 1
+      reinterpret_cast<uint2*>(&sh.p[n * 4 + g][0])[wave] = make_uint2(ph[0], ph[1]);
+      reinterpret_cast<uint2*>(&sh.p[n * 4 + g][1])[wave] = make_uint2(pl[0], pl[1]);
+      if (wave == 0 && g == 0) sh.alpha[n] = alpha;
     }
     lds_barrier();
 
@@ -259,21 +270,21 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
     lds_barrier();                 // the tile is free for the next chunk
   }
 
-  // ---- finish: wave 0 hands the sums to the others
+  // ---- finish: waves 0 and 1 hand their sums to the others
   const int64_t rh = (int64_t)r * H + hbase + n;
+  if (wave < 2 && g == 0) sh.lsum[wave][n] = l_run;
+  lds_barrier();
+  const float l = sh.lsum[0][n] + sh.lsum[1][n];
   if (wave == 0 && g == 0) {
-    sh.lsum[n] = l_run;
     if (a.n_split == 1) {
-      if (a.lse) a.lse[rh] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+      if (a.lse) a.lse[rh] = l > 0.0f ? (m_run + log2f(l)) * 0.69314718055994531f : -INFINITY;
     } else {
       const int64_t base = (int64_t)split * a.n_rows * H + rh;
       a.part_ml[base * 2] = m_run;
-      a.part_ml[base * 2 + 1] = l_run;
+      a.part_ml[base * 2 + 1] = l;
     }
   }
-  lds_barrier();
   if (a.n_split == 1) {
-    const float l = sh.lsum[n];
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float* orow = a.out + rh * kD + 4 * g;
 #pragma unroll

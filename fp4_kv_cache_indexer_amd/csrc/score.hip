@@ -21,14 +21,20 @@ namespace csa2 {
 // score kernel
 // ---------------------------------------------------------------------------
 
+#ifndef CSA2_SCORE_TILES
+#define CSA2_SCORE_TILES 4
+#endif
+#ifndef CSA2_SCORE_MINW
+#define CSA2_SCORE_MINW 2
+#endif
 constexpr int kScoreThreads = 256;
 constexpr int kScoreWaves = kScoreThreads / 64;
-constexpr int kTilesPerIter = 4;   // 16-item tiles per group
+constexpr int kTilesPerIter = CSA2_SCORE_TILES;   // 16-item tiles per group
 // Chosen by measurement on the 8 x 131072-block coarse scan: double-buffered
 // groups of 4 tiles, register budget for 2 waves per SIMD (28.7 us vs
 // 29.8-37 us for the single-buffered, larger-group and tighter-budget forms).
 constexpr bool kScoreDB = true;
-constexpr int kScoreMinW = 2;
+constexpr int kScoreMinW = CSA2_SCORE_MINW;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -81,8 +87,6 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   if (c0 >= n_row) return;                       // uniform for the workgroup
   const int64_t c1 = min(c0 + (int64_t)a.chunk, n_row);
 
-  for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) hist[b] = 0u;
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t seq = row_seq_of(a.im, r);
@@ -96,17 +100,12 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // four fp16 k-slices of 8.  The B operand (keys) uses the same byte split,
   // so each lane's query bytes meet the same key bytes and the four MFMAs
   // together form the full 128-term dot product.
+  // The query and weight loads are issued first, then the first key group's,
+  // and only then is the query converted (waiting for its own loads alone),
+  // so the key stream starts without waiting a memory round trip.
   const uint8_t* qr = a.q + (int64_t)r * kIdxHeads * kIdxDim + g * 32;
-  v8h qa0[4], qa1[4];
-  {
-    const v8i q0 = load32(qr + n * kIdxDim);
-    const v8i q1 = load32(qr + (16 + n) * kIdxDim);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      qa0[u] = fp8x8_to_f16(q0[2 * u], q0[2 * u + 1]);
-      qa1[u] = fp8x8_to_f16(q1[2 * u], q1[2 * u + 1]);
-    }
-  }
+  const v8i q0 = load32(qr + n * kIdxDim);
+  const v8i q1 = load32(qr + (16 + n) * kIdxDim);
   float w0[4], w1[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -114,7 +113,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     w1[i] = a.w ? a.w[r * kIdxHeads + 16 + 4 * g + i] : 1.0f;
   }
   float* srow = a.scores + (int64_t)r * a.row_stride;
-  __syncthreads();
+  v8h qa0[4], qa1[4];                            // converted after the first key loads
 
   // A wave works on groups of U tiles of 16 items (U a multiple of 4).
   // Loads are unconditional (an invisible item reads a visible row and its
@@ -187,9 +186,20 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   v8i kA[U], kB[U];
   int32_t pA[U], pB[U];
   int64_t t0 = (int64_t)wave * U;
+  // Group loads are unconditional (tiles past the chunk read a visible key
+  // and are discarded): a load on one side of a branch makes the compiler's
+  // later waits cover it, which would serialise the double buffer.
+  if (G > 0 || DB) load_group(t0, kA, pA);
+  __builtin_amdgcn_sched_barrier(0);             // the key loads go out first
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    qa0[u] = fp8x8_to_f16(q0[2 * u], q0[2 * u + 1]);
+    qa1[u] = fp8x8_to_f16(q1[2 * u], q1[2 * u + 1]);
+  }
+  for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) hist[b] = 0u;
+  lds_barrier();                                 // the key loads stay in flight
   if (G > 0) {
     // straight-line: load group i+1 before computing group i
-    load_group(t0, kA, pA);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int64_t ti = t0 + i * gstride;
@@ -201,15 +211,14 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       if (i & 1) compute_group(ti, kB); else compute_group(ti, kA);
     }
   } else if (DB) {
-    if (t0 < ntiles) load_group(t0, kA, pA);
+    // two groups per trip and no exit between them (a group past the chunk
+    // is computed and discarded): one loop shape keeps the waits exact
     for (; t0 < ntiles; t0 += 2 * gstride) {
       const int64_t t1 = t0 + gstride;
-      if (t1 < ntiles) load_group(t1, kB, pB);
+      load_group(t1, kB, pB);
       __builtin_amdgcn_sched_barrier(0);
       compute_group(t0, kA);
-      if (t1 >= ntiles) break;
-      const int64_t t2 = t1 + gstride;
-      if (t2 < ntiles) load_group(t2, kA, pA);
+      load_group(t1 + gstride, kA, pA);
       __builtin_amdgcn_sched_barrier(0);
       compute_group(t1, kB);
     }
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       compute_group(t0, kA);
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t* ghist = a.hist + (int64_t)r * kHistBins;
   for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
     const uint32_t c = hist[b];
