@@ -10,16 +10,19 @@
 //   * all 512 threads gather the selected FP4 entries (256 code + 32 E4M3
 //     scale bytes each) or FP8 window tokens and dequantise them exactly into
 //     one key-major bf16 tile (swizzled rows);
-//   * wave 0 computes S^T[t][h] = sum_c K[t][c] Q[h][c] (Q staged in LDS,
-//     v_mfma_f32_16x16x32_bf16) and the online softmax in float32, and hands
-//     P to the other waves as hi + lo bf16 terms (about 16 significant bits)
-//     with the rescale factor;
+//   * waves 0 and 1 compute S^T[t][h] = sum_c K[t][c] Q[h][c] for keys
+//     16w..16w+15 (Q staged in LDS, v_mfma_f32_16x16x32_bf16), exchange
+//     their chunk maxima through LDS so both keep the same reference max,
+//     run the online softmax in float32 and hand P to the other waves as
+//     hi + lo bf16 terms (about 16 significant bits) with the rescale factor;
+//     each sums the weights of its own keys;
 //   * all 8 waves accumulate O^T[c][h] += sum_t K[t][c] P[h][t] for 4 channel
 //     tiles each, reading K^T from the tile with the LDS transpose read.
-// The score tile leaves head n and keys {4g..4g+3, 16+4g..16+4g+3} in lane
-// (n, g), exactly the k-slot order of the PV operand the transpose read
-// builds, so lane (n, g) of every wave reads the 32 bytes lane (n, g) of
-// wave 0 wrote.  Split partials are merged by attn_combine_kernel.
+// The score tiles leave head n and keys {4g..4g+3} (wave 0) and
+// {16+4g..16+4g+3} (wave 1) in lane (n, g), exactly the k-slot order of the
+// PV operand the transpose read builds, so lane (n, g) of every wave reads
+// the 32 bytes lanes (n, g) of waves 0 and 1 wrote.  Split partials are
+// merged by attn_combine_kernel.
 #include "attn_dev.h"
 #include "csa2_launch.h"
 
