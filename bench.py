@@ -770,7 +770,7 @@ def main():
                      "bytes_per_launch": scan_bytes(w)},
         "roofline_attn": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
                           "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                          "kernel": "sparse_attn_kernel", "avg_us": round(avg_a * 1e6, 3),
+                          "kernel": "sparse attention (launch site attn: the narrow kernel at few rows, the wide one otherwise)", "avg_us": round(avg_a * 1e6, 3),
                           "flops_per_launch": attn_flops(w)},
         "cpu_baseline": None,
     }
