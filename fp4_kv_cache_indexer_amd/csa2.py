@@ -95,6 +95,7 @@ class AttnArgs(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
+        ("swa_max", ctypes.c_int32),
     ]
 
 
@@ -374,7 +375,8 @@ def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_
     return out_idx
 
 
-def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse):
+def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse,
+                 swa_max=0):
     a = AttnArgs()
     a.n_rows = q.shape[0]
     a.n_heads = q.shape[1]
@@ -397,20 +399,22 @@ def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_sca
     a.sm_scale = float(sm_scale)
     a.out = _ptr(out)
     a.lse = _ptr(lse)
+    a.swa_max = int(swa_max)
     return a
 
 
-def sparse_attn_workspace(q, idx, swa=None, swa_len=None, codes=None):
-    a = _attn_struct(q, codes, None, idx, swa, None, swa_len, None, 0.0, None, None)
+def sparse_attn_workspace(q, idx, swa=None, swa_len=None, codes=None, swa_max=0):
+    a = _attn_struct(q, codes, None, idx, swa, None, swa_len, None, 0.0, None, None, swa_max)
     return lib().csa2_sparse_attn_workspace(ctypes.byref(a))
 
 
 def sparse_attn_decode(q, codes, scales, idx, swa=None, swa_start=None, swa_len=None,
                        row_seq=None, sm_scale=0.0, out=None, lse=None, workspace=None,
-                       stream=None):
+                       stream=None, swa_max=0):
     """q bf16 [R, H, 512]; codes/scales [S, N, 256]/[S, N, 32]; idx int32
-    [R, k]; swa uint8 [S, cap, 512].  Returns (out float32 [R, H, 512],
-    lse float32 [R, H])."""
+    [R, k]; swa uint8 [S, cap, 512].  swa_max: bound on every swa_len (0 =
+    cap), e.g. 128 for prefill rows over one shared run of window tokens.
+    Returns (out float32 [R, H, 512], lse float32 [R, H])."""
     for t, nm in ((q, "q"), (codes, "codes"), (scales, "scales"), (idx, "idx"), (swa, "swa"),
                   (swa_start, "swa_start"), (swa_len, "swa_len"), (row_seq, "row_seq")):
         _dev(t, nm)
@@ -419,7 +423,8 @@ def sparse_attn_decode(q, codes, scales, idx, swa=None, swa_start=None, swa_len=
         out = torch.empty((R, H, LATENT_DIM), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((R, H), dtype=torch.float32, device=q.device)
-    a = _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse)
+    a = _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_scale, out, lse,
+                     swa_max)
     L = lib()
     need = L.csa2_sparse_attn_workspace(ctypes.byref(a))
     if workspace is None and need:

@@ -191,6 +191,8 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   const bool has_swa = a->swa_len != nullptr;
   if (has_swa && (a->swa_cap < 1 || a->swa_cap > 65536))
     return fail(CSA2_EINVAL, "attn: swa_cap %d outside [1, 65536] with swa_len set", a->swa_cap);
+  if (has_swa && (a->swa_max < 0 || a->swa_max > a->swa_cap))
+    return fail(CSA2_EINVAL, "attn: swa_max %d outside [0, swa_cap %d]", a->swa_max, a->swa_cap);
   if (a->n_rows > 0 && check_ptrs) {
     if (!a->q_bf16 || !a->out) return fail(CSA2_EINVAL, "attn: q_bf16 and out are required");
     if (!aligned(a->q_bf16, 16) || !aligned(a->out, 16)) return fail(CSA2_EINVAL, "attn: q/out not 16-byte aligned");
@@ -201,7 +203,7 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
     if (has_swa && (!a->swa || !aligned(a->swa, 16))) return fail(CSA2_EINVAL, "attn: swa missing or misaligned");
     if (a->lse && !aligned(a->lse, 4)) return fail(CSA2_EINVAL, "attn: lse misaligned");
   }
-  const int64_t nk = (int64_t)a->top_k + (has_swa ? a->swa_cap : 0);
+  const int64_t nk = (int64_t)a->top_k + (has_swa ? (a->swa_max > 0 ? a->swa_max : a->swa_cap) : 0);
   const int64_t max_split = (nk + CSA2_MIN_SPLIT_KEYS - 1) / CSA2_MIN_SPLIT_KEYS;   // keys per split at least
   // Few rows: one 16-head group per workgroup (the narrow kernel: a short
   // chain of dependent steps, two workgroups per CU), as long as every such
@@ -543,6 +545,7 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
   k.top_k = a->top_k;
   k.swa = a->swa_len ? a->swa : nullptr;
   k.swa_cap = a->swa_len ? a->swa_cap : 0;
+  k.swa_max = a->swa_len ? (a->swa_max > 0 ? a->swa_max : a->swa_cap) : 0;
   k.swa_start = a->swa_start;
   k.swa_len = a->swa_len;
   const float sm = a->sm_scale > 0.0f ? a->sm_scale : 0.044194173824159216f;   // 1/sqrt(512)

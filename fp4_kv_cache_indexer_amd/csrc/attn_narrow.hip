@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;
   int swl = (a.swa_len && seq_ok) ? a.swa_len[r] : 0;
-  swl = max(0, min(swl, a.swa_cap));
+  swl = max(0, min(swl, a.swa_max));
   int swst = a.swa_start ? a.swa_start[r] : 0;
   if (a.swa_cap > 0) { swst %= a.swa_cap; if (swst < 0) swst += a.swa_cap; }
   const int nk = nsel + swl;

@@ -98,6 +98,7 @@ struct AttnArgs {
   int32_t top_k;
   const uint8_t* swa;
   int32_t swa_cap;
+  int32_t swa_max;          // window lengths are clamped to this (<= swa_cap)
   const int32_t* swa_start;
   const int32_t* swa_len;
   float sm_scale_log2;      // sm_scale * log2(e)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -304,7 +304,7 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
  * Keys = values = the latent: for row r the key set is the dequantised FP4
  * entries idx[r][0..top_k) of sequence row_seq[r] (entries < 0 skipped)
  * followed by the SWA tokens in slots (swa_start[r] + j) mod swa_cap,
- * j < swa_len[r].  For every head h:
+ * j < min(swa_len[r], swa_max).  For every head h:
  *   s_t = sm_scale * q[r][h] . K_t,   out[r][h] = sum_t softmax(s)_t K_t,
  *   lse[r][h] = log(sum_t exp(s_t))   (natural log)
  * one softmax over all keys, float32 accumulation.  With no key the output
@@ -312,6 +312,11 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
  *   q_bf16 : bf16 [R][H][512];  out : float32 [R][H][512];  lse : [R][H] or NULL
  *   H in {16, 32, 64, 128};  sm_scale <= 0 selects 1/sqrt(512).
  *   swa may be NULL when every swa_len is 0 (swa_len NULL = no window).
+ *   swa_max bounds the window of every row: the key splits are planned for
+ *   top_k + swa_max keys per row (0 selects swa_cap).  A caller whose window
+ *   buffer is larger than any one row's window (prefill rows reading one
+ *   shared run of tokens, each its own 128) passes the window length here;
+ *   without it every row is planned for swa_cap keys.
  */
 typedef struct {
   int32_t n_rows;           /* R                                                */
@@ -332,6 +337,8 @@ typedef struct {
   float sm_scale;           /* softmax scale, <= 0 -> 1/sqrt(512)               */
   float* out;               /* [R][H][512] float32                              */
   float* lse;               /* [R][H] float32, or NULL                          */
+  int32_t swa_max;          /* largest swa_len used, 0..swa_cap (0 = swa_cap);
+                               longer windows are clamped to it                 */
 } csa2_attn_args;
 
 /* Workspace bytes csa2_sparse_attn_decode needs (0 on error or if none).

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_version_and_status_strings():
     L = C.lib()
-    assert C.abi_version() == 1
+    assert C.abi_version() == 2
     assert C.status_string(0) == "ok"
     assert C.status_string(3) == "workspace too small"
     assert L.csa2_last_error() is not None
@@ -123,6 +123,16 @@ def test_attn_and_cache_write_validation_without_gpu():
     need = L.csa2_sparse_attn_workspace(ctypes.byref(a))
     assert need > 0                                                         # one row -> key splits
     assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 3
+    # swa_max bounds every window: outside [0, swa_cap] is rejected; with many
+    # rows over one long shared window buffer it alone keeps each row in one
+    # split (no partials to merge, so no workspace)
+    for bad in (-1, 129):
+        a.swa_max = bad
+        assert L.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == 1
+    a.n_rows, a.swa_cap, a.swa_max = 4096, 4223, 0
+    assert L.csa2_sparse_attn_workspace(ctypes.byref(a)) > 0
+    a.swa_max = 128
+    assert L.csa2_sparse_attn_workspace(ctypes.byref(a)) == 0
     p = ctypes.c_void_p(0x1000)
     assert L.csa2_kv_compress_quantize(p, None, 1, 16, 3, 0, p, p, 0, None) == 2
     assert L.csa2_kv_compress_quantize(p, None, 1, 16, 2, 8, p, p, 0, None) == 1

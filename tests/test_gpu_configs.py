@@ -328,7 +328,7 @@ def test_c4_layer_group_batch64():
 
 
 def test_c5_cache_write_and_prefill_chunk():
-    say("C5: cache write of 1M tokens at m=2 (gated), prefill chunk of 4096 queries (every 16th row)")
+    say("C5: cache write of 1M tokens at m=2 (gated), prefill chunk of 4096 queries")
     seed, cfg, T, m, H, k = 0, 4, 1 << 20, 2, 64, 512
     cache = Cache(seed, cfg, 1, T, m, gate=True)
     N = cache.N
@@ -338,7 +338,7 @@ def test_c5_cache_write_and_prefill_chunk():
     assert cache.codes.shape[-1] + cache.scales.shape[-1] == A.fp4_entry_bytes(D)
     keys = index_keys(seed, cfg, 1, N)
     chunk = 4096
-    pos = np.arange(T - chunk, T)[::16]                      # 256 rows of the chunk
+    pos = np.arange(T - chunk, T)                            # every row of the chunk
     R = len(pos)
     nv = (pos + 1) // m                                      # entries whose tokens all precede the query
     cap = chunk + 127                                        # window ring over the chunk's tokens
@@ -353,13 +353,14 @@ def test_c5_cache_write_and_prefill_chunk():
     row_seq = torch.zeros(R, dtype=torch.int32, device="cuda")
     say(f"  prefill rows R={R}: flat top-512 over causal prefixes of ~{N} entries + SWA")
     idx = C.indexer_topk(q_idx, keys, k, head_w=w, row_seq=row_seq, n_valid=dev(nv.astype(np.int32)))
+    # every window is 128 tokens: swa_max keeps each row in one key split
     out, lse = C.sparse_attn_decode(q, cache.codes, cache.scales, idx, swa=swa, swa_start=dev(swa_start),
-                                    swa_len=dev(swa_len), row_seq=row_seq)
+                                    swa_len=dev(swa_len), row_seq=row_seq, swa_max=128)
     torch.cuda.synchronize()
     gi, go, gl = host(idx), host(out), host(lse)
     q_idx_h, w_h, q_h, swa_h = host(q_idx), host(w), synth.bf16_host_bits(q), host(swa[0])
     keys_h = host(keys[0])
-    rows = [0, 85, 170, R - 1]
+    rows = [0, 1365, 2730, R - 1]
     views = {r: O.prefill_row_view(int(pos[r]), m) for r in rows}
     refs = check_rows(rows, gi, None, q_idx_h, w_h, lambda r: keys_h, lambda r: views[r][0], k, "C5")
     compared = 0

@@ -584,8 +584,19 @@ def test_prefill_rows_causal():
     idx = C.indexer_topk(dev(q_idx), dev(keys), k, row_seq=dev(row_seq), n_valid=dev(nv))
     out, lse = C.sparse_attn_decode(dev(q), dev(codes), dev(scales), idx, swa=dev(swa),
                                     swa_start=dev(lo), swa_len=dev(ln), row_seq=dev(row_seq))
+    # the same rows with the window bound given (one key split per row instead
+    # of splits planned for the whole window buffer), and with a bound below
+    # the windows (each window clamped to its first 64 slots)
+    out_b, lse_b = C.sparse_attn_decode(dev(q), dev(codes), dev(scales), idx, swa=dev(swa),
+                                        swa_start=dev(lo), swa_len=dev(ln), row_seq=dev(row_seq),
+                                        swa_max=128)
+    out_c, lse_c = C.sparse_attn_decode(dev(q), dev(codes), dev(scales), idx, swa=dev(swa),
+                                        swa_start=dev(lo), swa_len=dev(ln), row_seq=dev(row_seq),
+                                        swa_max=64)
     torch.cuda.synchronize()
     gi, go, gl = host(idx), host(out), host(lse)
+    gob, glb, goc, glc = host(out_b), host(lse_b), host(out_c), host(lse_c)
+    assert ln.max() == 128
     differ = 0
     for r in range(R):
         sc = O.index_scores(q_idx[r], None, keys[0][:nv[r]])
@@ -597,4 +608,9 @@ def test_prefill_rows_causal():
         Ox, lx = O.sparse_attn(q[r], codes[0], scales[0], ref, swa[0], range(lo[r], lo[r] + ln[r]))
         check_close(go[r], Ox, f"row {r} out")
         check_close(gl[r], lx, f"row {r} lse")
+        check_close(gob[r], Ox, f"row {r} out (swa_max 128)")
+        check_close(glb[r], lx, f"row {r} lse (swa_max 128)")
+        Oc, lc = O.sparse_attn(q[r], codes[0], scales[0], ref, swa[0], range(lo[r], lo[r] + min(ln[r], 64)))
+        check_close(goc[r], Oc, f"row {r} out (swa_max 64)")
+        check_close(glc[r], lc, f"row {r} lse (swa_max 64)")
     assert differ <= 1
