@@ -633,12 +633,109 @@ def sweep(args, w0):
         torch.cuda.empty_cache()
 
 
+PREFILL_C5 = dict(
+    desc="prefill chunk at 1M context: 1,048,576 bf16 tokens (512-dim, gate logits) pooled at m=2 into "
+         "524,288 FP4 entries (the cache write), then 4,096 queries at positions [T-4096, T), each a flat "
+         "causal top-512 over its ~523K visible E4M3 index keys (32 x 128) and joint attention over its "
+         "512 entries + 128-token FP8 window; 64 heads x 512 bf16",
+    T=1 << 20, m=2, R=4096, H=64, k=512, W=128)
+
+
+def run_prefill(args):
+    """One step = the C5 prefill chunk: the cache write of the whole 1M-token
+    context, the 4096-row causal indexer and the 4096-row attention.  Each
+    part is timed with HIP events (kernels on one stream, back to back);
+    value = rows of the chunk per second of the whole step."""
+    w = PREFILL_C5
+    T, m, R, H, k, W = w["T"], w["m"], w["R"], w["H"], w["k"], w["W"]
+    N = T // m
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    x = synth.latent_dev((1, T, 512), g, "normal").to(torch.bfloat16)
+    z = torch.randn((1, T, 512), generator=g, device="cuda").to(torch.bfloat16)
+    codes = torch.empty((1, N, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, N, 32), dtype=torch.uint8, device="cuda")
+    keys = synth.to_e4m3(torch.randn((1, N, 128), generator=g, device="cuda"))
+    pos = torch.arange(T - R, T, device="cuda", dtype=torch.int64)
+    n_valid = ((pos + 1) // m).to(torch.int32)
+    row_seq = torch.zeros(R, dtype=torch.int32, device="cuda")
+    q_idx = synth.to_e4m3(torch.randn((R, 32, 128), generator=g, device="cuda"))
+    head_w = torch.rand((R, 32), generator=g, device="cuda") * 0.75 + 0.25
+    q = torch.randn((R, H, 512), generator=g, device="cuda").to(torch.bfloat16)
+    base = T - R - (W - 1)                       # the window tokens of the chunk, in FP8
+    swa = synth.to_e4m3(x[:, base:].float())
+    lo = (pos - (W - 1)).clamp(min=0)
+    swa_start = (lo - base).to(torch.int32)
+    swa_len = (pos - lo + 1).to(torch.int32)
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    ws_i = torch.zeros(C.indexer_topk_workspace(q_idx, keys, k), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, C.sparse_attn_workspace(q, idx, swa=swa, swa_len=swa_len, codes=codes, swa_max=W)),
+                       dtype=torch.uint8, device="cuda")
+    parts = [
+        ("cache_write", lambda: C.kv_compress_quantize(x, m, gate=z, codes=codes, scales=scales)),
+        ("indexer", lambda: C.indexer_topk(q_idx, keys, k, head_w=head_w, row_seq=row_seq, n_valid=n_valid,
+                                           out_idx=idx, workspace=ws_i)),
+        ("attention", lambda: C.sparse_attn_decode(q, codes, scales, idx, swa=swa, swa_start=swa_start,
+                                                   swa_len=swa_len, row_seq=row_seq, out=out, lse=lse,
+                                                   workspace=ws_a, swa_max=W)),
+    ]
+    print(f"[bench] workload c5: {w['desc']}", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        for _, f in parts:
+            f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+    tot = [0.0] * len(parts)
+    for _ in range(args.steps):
+        ev[0].record()
+        for i, (_, f) in enumerate(parts):
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        for i in range(len(parts)):
+            tot[i] += ev[i].elapsed_time(ev[i + 1])
+    ms = [t / args.steps for t in tot]
+    ms_step = sum(ms)
+    for (name, _), t in zip(parts, ms):
+        print(f"[bench] {name}: {t * 1e3:.1f} us", file=sys.stderr, flush=True)
+    write_bytes = 2 * T * 512 * 2 + N * (256 + 32)             # x + gate read, FP4 entries written
+    idx_flops = float(n_valid.double().sum().item()) * 8192     # 32 heads x 128 per visible entry
+    attn_fl = 4.0 * H * (k + W) * 512 * R
+    res = {
+        "metric": METRIC, "value": round(R / (ms_step / 1e3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8/fp4 storage; fp16+bf16 MFMA, fp32 accumulation",
+        "data": "synthetic (seeded, device-generated)",
+        "config": {"workload": "c5: " + w["desc"], "tokens": T, "m": m, "entries": N, "rows": R,
+                   "heads": H, "top_k": k, "swa_window": W, "timed": "eager, HIP events per part"},
+        "parts_ms": {name: round(t, 4) for (name, _), t in zip(parts, ms)},
+        "roofline": {"bound": "mfma", "achieved": round(idx_flops / (ms[1] / 1e3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(idx_flops / (ms[1] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "indexer (fp16 MFMA scan of every visible key + top-512 per row)",
+                     "flops_per_launch": idx_flops},
+        "roofline_attn": {"bound": "mfma", "achieved": round(attn_fl / (ms[2] / 1e3) / 1e12, 2),
+                          "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                          "frac": round(attn_fl / (ms[2] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                          "kernel": "sparse attention, 4096 rows x 64 heads", "flops_per_launch": attn_fl},
+        "roofline_cache_write": {"bound": "hbm", "achieved": round(write_bytes / (ms[0] / 1e3) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(write_bytes / (ms[0] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "bytes_per_launch": write_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["c5"])
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -659,9 +756,12 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the multi-GPU sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
-    w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     C.lib()
+    if args.workload == "c5":
+        run_prefill(args)
+        return
+    w = WORKLOADS[args.workload]
     if args.sweep:
         if not w.get("sched"):
             sys.exit("bench.py: --sweep runs the 40-layer schedule (--workload sched40 or sched40fp4)")
