@@ -77,6 +77,10 @@ struct SelectArgs {
 };
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
+// Flat E4M3 scans of many rows over a one-sequence cache (a prefill chunk)
+// score groups of rows per key tile (index_score_rows_kernel).
+constexpr int32_t kScoreRowsMin = 256;
+bool score_rows_path(const ScoreArgs& a);
 int score_resident_wgs();
 hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);

@@ -236,6 +236,150 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   }
 }
 
+// ---------------------------------------------------------------------------
+// row-group score kernel: many rows over one cache (a prefill chunk)
+// ---------------------------------------------------------------------------
+
+// When every row reads the same sequence's E4M3 keys in flat mode (the rows
+// of one prefill chunk, each with its causal n_valid), a workgroup scores RG
+// consecutive rows against each key tile it loads: the tile is read from
+// memory and widened to fp16 once for all RG rows, which carry their own
+// queries, weights, histograms and visible lengths.  Per row the MFMA
+// operands, their order and the head reduction are those of
+// index_score_kernel, so the scores are bit-identical.
+constexpr int kRowGroup = 2;
+
+template <int RG>
+__global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(ScoreArgs a) {
+  constexpr int U = 4;                           // 16-item tiles per group
+  __shared__ uint32_t hist[RG][kHistBins];
+  const int rbase = blockIdx.y * RG;
+  int64_t nv[RG];
+  int64_t nmax = 0;
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    nv[i] = rbase + i < a.n_rows ? row_valid(a.im, rbase + i) : 0;   // the one sequence, or nothing
+    nmax = max(nmax, nv[i]);
+  }
+  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  if (c0 >= nmax) return;                        // uniform for the workgroup
+  const int64_t c1 = min(c0 + (int64_t)a.chunk, nmax);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* kbase = a.keys + g * 32;        // sequence 0
+
+  // queries and weights of the RG rows (rows past the end reuse the first)
+  v8i qr0[RG], qr1[RG];
+  float w0[RG][4], w1[RG][4];
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    const int r = rbase + i < a.n_rows ? rbase + i : rbase;
+    const uint8_t* qr = a.q + (int64_t)r * kIdxHeads * kIdxDim + g * 32;
+    qr0[i] = load32(qr + n * kIdxDim);
+    qr1[i] = load32(qr + (16 + n) * kIdxDim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0[i][j] = a.w ? a.w[r * kIdxHeads + 4 * g + j] : 1.0f;
+      w1[i][j] = a.w ? a.w[r * kIdxHeads + 16 + 4 * g + j] : 1.0f;
+    }
+  }
+
+  const int64_t ntiles = (c1 - c0 + 15) / 16;
+  const int64_t gstride = (int64_t)kScoreWaves * U;
+  auto load_group = [&](int64_t t0, v8i* kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t item = c0 + (t0 + u) * 16 + n;
+      const int64_t p = item < c1 ? item : c0;   // past the chunk: a visible key, discarded
+      kb[u] = load32(kbase + p * kIdxDim);
+    }
+  };
+  v8i kA[U], kB[U];
+  int64_t t0 = (int64_t)wave * U;
+  load_group(t0, kA);
+  __builtin_amdgcn_sched_barrier(0);             // the key loads go out first
+  v8h qa0[RG][4], qa1[RG][4];
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      qa0[i][v] = fp8x8_to_f16(qr0[i][2 * v], qr0[i][2 * v + 1]);
+      qa1[i][v] = fp8x8_to_f16(qr1[i][2 * v], qr1[i][2 * v + 1]);
+    }
+  }
+  for (int b = threadIdx.x; b < RG * kHistBins; b += kScoreThreads) (&hist[0][0])[b] = 0u;
+  lds_barrier();                                 // the key loads stay in flight
+
+  auto compute_group = [&](int64_t tg, const v8i* kb) {
+    float p[RG][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v8h kh[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) kh[v] = fp8x8_to_f16(kb[u][2 * v], kb[u][2 * v + 1]);
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        v4f d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa0[i][v], kh[v], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa1[i][v], kh[v], d1, 0, 0, 0);
+        }
+        float sp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sp = fmaf(w0[i][j], fmaxf(d0[j], 0.0f), sp);
+          sp = fmaf(w1[i][j], fmaxf(d1[j], 0.0f), sp);
+        }
+        p[i][u] = sp;
+      }
+    }
+    // per row, the transpose-reduce of index_score_kernel: lane (n, g) ends
+    // with the score of tile g, entry n
+    const bool b0 = g & 1, b1 = (g >> 1) & 1;
+    const int64_t item = c0 + (tg + g) * 16 + n;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      float keep0 = b0 ? p[i][1] : p[i][0], send0 = b0 ? p[i][0] : p[i][1];
+      float keep1 = b0 ? p[i][3] : p[i][2], send1 = b0 ? p[i][2] : p[i][3];
+      keep0 += __shfl_xor(send0, 16);
+      keep1 += __shfl_xor(send1, 16);
+      float sc = b1 ? keep1 : keep0;
+      sc += __shfl_xor(b1 ? keep0 : keep1, 32);
+      if (item < c1 && item < nv[i]) {
+        a.scores[(int64_t)(rbase + i) * a.row_stride + item] = sc;
+        atomicAdd(&hist[i][order_key(sc) >> (32 - kHistBits)], 1u);
+      }
+    }
+  };
+  // two groups per trip, no exit between them (a group past the chunk is
+  // computed and discarded): the waits stay exact
+  for (; t0 < ntiles; t0 += 2 * gstride) {
+    const int64_t t1 = t0 + gstride;
+    load_group(t1, kB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group(t0, kA);
+    load_group(t1 + gstride, kA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_group(t1, kB);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    if (rbase + i >= a.n_rows) break;            // uniform
+    uint32_t* ghist = a.hist + (int64_t)(rbase + i) * kHistBins;
+    for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
+      const uint32_t c = hist[i][b];
+      if (c) atomicAdd(&ghist[b], c);
+    }
+  }
+}
+
+bool score_rows_path(const ScoreArgs& a) {
+  return a.im.mode == kItemsFlat && !a.key_fp4 && a.n_seq == 1 && a.n_rows >= kScoreRowsMin;
+}
+
 // Workgroups of one score kernel that fit on the device at once.
 int score_resident_wgs() {
   static int cached = 0;
@@ -255,6 +399,26 @@ int score_resident_wgs() {
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.im.n_items == 0) return hipSuccess;
+  if (score_rows_path(a)) {
+    // row groups over one cache: each group's items in chunks of whole
+    // 256-item steps, as many as keep every resident slot busy
+    ScoreArgs b = a;
+    const int64_t groups = (a.n_rows + kRowGroup - 1) / kRowGroup;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    const int64_t slots = (int64_t)cus * 2;      // two workgroups per CU
+    const int64_t per_group = groups >= slots ? 1 : slots / groups;
+    int64_t c = (a.im.n_items + per_group - 1) / per_group;
+    c = (c + 255) / 256 * 256;
+    b.chunk = (int32_t)c;
+    const dim3 grid((unsigned)((a.im.n_items + c - 1) / c), (unsigned)groups), block(kScoreThreads);
+    hipLaunchKernelGGL((index_score_rows_kernel<kRowGroup>), grid, block, 0, stream, b);
+    return hipGetLastError();
+  }
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
   const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
 #define CSA2_SCORE(MM, KK) \

@@ -178,6 +178,33 @@ def test_indexer_flat_rows_ragged():
     assert (gi[2] == -1).all() and (gi[1][100:] == -1).all()
 
 
+def test_indexer_row_groups_one_cache():
+    """Many rows over a one-sequence cache (a prefill chunk) take the
+    row-group scan: bit-equal to the per-row scan of the same rows (issued
+    in calls of fewer rows) and to the oracle on sampled rows; ragged and
+    empty visible lengths, sequences outside the cache, an odd row count."""
+    say("indexer flat, one cache, 301 rows (row groups) against the per-row scan and the oracle")
+    N, R, k = 6007, 301, 96
+    g = np.random.default_rng(11)
+    nv = g.integers(0, N + 1, R)
+    nv[:6] = [N, 0, 1, 15, 17, N - 1]
+    rs = np.zeros(R, np.int64)
+    rs[[7, 150, 299]] = [1, -1, 5]                       # outside the cache: nothing visible
+    case = idx_case(21, 1, N, R, row_seq=rs, n_valid=nv)
+    gi, gsc = run_indexer(case, k)                        # R >= 256 rows over one sequence
+    parts = []
+    for lo, hi in ((0, 150), (150, R)):                   # the same rows below the row-group threshold
+        sub = dict(case, q=case["q"][lo:hi], w=case["w"][lo:hi], row_seq=rs[lo:hi], n_valid=nv[lo:hi])
+        parts.append(run_indexer(sub, k))
+    assert np.array_equal(gi, np.concatenate([parts[0][0], parts[1][0]]))
+    assert np.array_equal(gsc.view(np.uint32), np.concatenate([parts[0][1], parts[1][1]]).view(np.uint32))
+    for r in (7, 150, 299):
+        assert (gi[r] == -1).all()
+    sample = [0, 1, 2, 3, 4, 5, 100, 257, R - 1]
+    sub = dict(case, q=case["q"][sample], w=case["w"][sample], row_seq=rs[sample], n_valid=nv[sample])
+    check_flat_rows(sub, gi[sample], gsc[sample], k)
+
+
 def test_indexer_flat_ties_and_topk_range():
     for k in (1, 7, 512, 2048):
         say(f"indexer flat ties k={k}")
