@@ -487,13 +487,14 @@ def attn_case(seed, S, N, R, H, k, cap=128, dist="normal"):
     return c, codes, scales, idx
 
 
-def run_attn(c, codes, scales, idx, swa_start, swa_len, sm_scale=0.0, row_seq=None):
+def run_attn(c, codes, scales, idx, swa_start, swa_len, sm_scale=0.0, row_seq=None, swa_max=0):
     if row_seq is None:
         row_seq = np.arange(c.q.shape[0]) % c.S
     out, lse = C.sparse_attn_decode(
         dev(c.q), dev(codes), dev(scales), dev(idx), swa=dev(c.swa),
         swa_start=dev(np.asarray(swa_start, np.int32)), swa_len=dev(np.asarray(swa_len, np.int32)),
-        row_seq=None if row_seq is None else dev(np.asarray(row_seq, np.int32)), sm_scale=sm_scale)
+        row_seq=None if row_seq is None else dev(np.asarray(row_seq, np.int32)), sm_scale=sm_scale,
+        swa_max=swa_max)
     torch.cuda.synchronize()
     return host(out), host(lse)
 
@@ -513,6 +514,17 @@ def test_attn_single_query_h16():
     c, codes, scales, idx = attn_case(1, 1, 4096, 1, 16, 512)
     out, lse = run_attn(c, codes, scales, idx, [0], [128])
     say(f"  worst/bound {check_attn_rows(c, codes, scales, idx, [0], [128], out, lse):.3f}")
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_attn_window_bound_decode_rows(H):
+    # few rows (the narrow kernel at H=16 and 64): windows longer than
+    # swa_max are clamped to their first swa_max slots, wrapping the ring
+    say(f"sparse_attn H={H}, 2 rows, swa_max=48 below the window lengths")
+    c, codes, scales, idx = attn_case(6, 2, 2500, 2, H, 256)
+    start, ln = [100, 120], [128, 90]
+    out, lse = run_attn(c, codes, scales, idx, start, ln, swa_max=48)
+    check_attn_rows(c, codes, scales, idx, start, [48, 48], out, lse)
 
 
 @pytest.mark.parametrize("H", [32, 64, 128])
