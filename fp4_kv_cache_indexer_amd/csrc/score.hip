@@ -35,6 +35,11 @@ constexpr int kTilesPerIter = CSA2_SCORE_TILES;   // 16-item tiles per group
 // 29.8-37 us for the single-buffered, larger-group and tighter-budget forms).
 constexpr bool kScoreDB = true;
 constexpr int kScoreMinW = CSA2_SCORE_MINW;
+// Chunks of at most this many items stage their scores in LDS and write them
+// in one coalesced pass at the end (measured 0.5-1.3 us less on the C3
+// coarse scan than stores interleaved with the key stream); longer chunks
+// store as they go.
+constexpr int kScoreStage = 2048;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -80,12 +85,14 @@ template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPer
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
   __shared__ uint32_t hist[kHistBins];
+  __shared__ float sscore[kScoreStage];
   const int r = blockIdx.y;
   const int64_t nv = row_valid(a.im, r);
   const int64_t n_row = row_items(a.im, nv);
   const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
   if (c0 >= n_row) return;                       // uniform for the workgroup
   const int64_t c1 = min(c0 + (int64_t)a.chunk, n_row);
+  const bool stage = c1 - c0 <= kScoreStage;     // uniform
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -174,12 +181,11 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       sc += __shfl_xor(b1 ? keep0 : keep1, 32);
       const int64_t item = c0 + (t0 + u4 + g) * 16 + n;
       if (item < c1) {
-        if (item_pos(a.im, r, item, nv) >= 0) {
-          srow[item] = sc;
-          atomicAdd(&hist[order_key(sc) >> (32 - kHistBits)], 1u);
-        } else {
-          srow[item] = __uint_as_float(0x7FC00000u);   // not visible
-        }
+        const bool vis = item_pos(a.im, r, item, nv) >= 0;
+        const float out = vis ? sc : __uint_as_float(0x7FC00000u);   // NaN: not visible
+        if (stage) sscore[item - c0] = out;
+        else srow[item] = out;
+        if (vis) atomicAdd(&hist[order_key(sc) >> (32 - kHistBits)], 1u);
       }
     }
   };
@@ -229,6 +235,8 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     }
   }
   lds_barrier();
+  if (stage)
+    for (int64_t i = threadIdx.x; i < c1 - c0; i += kScoreThreads) srow[c0 + i] = sscore[i];
   uint32_t* ghist = a.hist + (int64_t)r * kHistBins;
   for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
     const uint32_t c = hist[b];
