@@ -429,8 +429,17 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   }
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
   const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
-#define CSA2_SCORE(MM, KK) \
-  hipLaunchKernelGGL((index_score_kernel<MM, KK, kScoreDB, kScoreMinW>), grid, block, 0, stream, a)
+  // a chunk of exactly one group per wave (the 16384-position pool, short
+  // rows) runs the straight-line form: no second, discarded group
+  const bool one = a.chunk == kScoreWaves * kTilesPerIter * 16;
+#define CSA2_SCORE(MM, KK)                                                                              \
+  do {                                                                                                  \
+    if (one)                                                                                            \
+      hipLaunchKernelGGL((index_score_kernel<MM, KK, kScoreDB, kScoreMinW, kTilesPerIter, 1>), grid, block, \
+                         0, stream, a);                                                                 \
+    else                                                                                                \
+      hipLaunchKernelGGL((index_score_kernel<MM, KK, kScoreDB, kScoreMinW>), grid, block, 0, stream, a);    \
+  } while (0)
   if (a.im.mode == kItemsBlocks) CSA2_SCORE(kItemsBlocks, 0);      // block summaries are E4M3
   else if (a.key_fp4) {
     if (a.im.mode == kItemsFlat) CSA2_SCORE(kItemsFlat, 1);
