@@ -733,7 +733,7 @@ def run_prefill(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["c5"])
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
@@ -817,6 +817,24 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {qps:.0f} queries/s",
           file=sys.stderr, flush=True)
 
+    # the distribution of single steps (a separate pass: an event pair around
+    # each step, so the block above stays free of per-step events)
+    per = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (a0, a1) in enumerate(evs):
+        a0.record()
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step_fn(w, sets[i % len(sets)])
+        a1.record()
+    torch.cuda.synchronize()
+    per = np.array([a0.elapsed_time(a1) * 1e3 for a0, a1 in evs])
+    step_dist = {"p10": round(float(np.percentile(per, 10)), 2), "median": round(float(np.median(per)), 2),
+                 "p90": round(float(np.percentile(per, 90)), 2)}
+    print(f"[bench] single steps: median {step_dist['median']} us (p10 {step_dist['p10']}, p90 {step_dist['p90']})",
+          file=sys.stderr, flush=True)
+
     # per-kernel durations from HIP events recorded around one launch site.
     # Eager steps follow a stall kernel on the same stream, so the launches
     # are queued before the GPU reaches them and the events see the kernel,
@@ -856,6 +874,7 @@ def main():
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "step_us": step_dist,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8/fp4 storage; fp16+bf16 MFMA, fp32 accumulation",
         "data": "synthetic (seeded, device-generated)",
