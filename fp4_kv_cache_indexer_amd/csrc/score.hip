@@ -255,23 +255,28 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
 // queries, weights, histograms and visible lengths.  Per row the MFMA
 // operands, their order and the head reduction are those of
 // index_score_kernel, so the scores are bit-identical.
-constexpr int kRowGroup = 2;
+#ifndef CSA2_ROW_GROUP
+#define CSA2_ROW_GROUP 4
+#endif
+constexpr int kRowGroup = CSA2_ROW_GROUP;
+constexpr int kRowTiles = kRowGroup >= 4 ? 2 : 4;   // 16-item tiles per group (registers)
 
-template <int RG>
+template <int RG, int U>
 __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(ScoreArgs a) {
-  constexpr int U = 4;                           // 16-item tiles per group
+  static_assert(U == 2 || U == 4, "16-item tiles per group: 2 or 4");
   __shared__ uint32_t hist[RG][kHistBins];
   const int rbase = blockIdx.y * RG;
-  int64_t nv[RG];
-  int64_t nmax = 0;
+  // item counts stay below kMaxItems (2^24): 32-bit indices
+  int32_t nv[RG];
+  int32_t nmax = 0;
 #pragma unroll
   for (int i = 0; i < RG; ++i) {
-    nv[i] = rbase + i < a.n_rows ? row_valid(a.im, rbase + i) : 0;   // the one sequence, or nothing
+    nv[i] = rbase + i < a.n_rows ? (int32_t)row_valid(a.im, rbase + i) : 0;   // the one sequence, or nothing
     nmax = max(nmax, nv[i]);
   }
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  const int32_t c0 = (int32_t)blockIdx.x * a.chunk;
   if (c0 >= nmax) return;                        // uniform for the workgroup
-  const int64_t c1 = min(c0 + (int64_t)a.chunk, nmax);
+  const int32_t c1 = min(c0 + a.chunk, nmax);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -293,18 +298,18 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
     }
   }
 
-  const int64_t ntiles = (c1 - c0 + 15) / 16;
-  const int64_t gstride = (int64_t)kScoreWaves * U;
-  auto load_group = [&](int64_t t0, v8i* kb) {
+  const int32_t ntiles = (c1 - c0 + 15) / 16;
+  const int32_t gstride = kScoreWaves * U;
+  auto load_group = [&](int32_t t0, v8i* kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t item = c0 + (t0 + u) * 16 + n;
-      const int64_t p = item < c1 ? item : c0;   // past the chunk: a visible key, discarded
-      kb[u] = load32(kbase + p * kIdxDim);
+      const int32_t item = c0 + (t0 + u) * 16 + n;
+      const int32_t p = item < c1 ? item : c0;   // past the chunk: a visible key, discarded
+      kb[u] = load32(kbase + (uint32_t)p * (uint32_t)kIdxDim);
     }
   };
   v8i kA[U], kB[U];
-  int64_t t0 = (int64_t)wave * U;
+  int32_t t0 = wave * U;
   load_group(t0, kA);
   __builtin_amdgcn_sched_barrier(0);             // the key loads go out first
   v8h qa0[RG][4], qa1[RG][4];
@@ -319,8 +324,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
   for (int b = threadIdx.x; b < RG * kHistBins; b += kScoreThreads) (&hist[0][0])[b] = 0u;
   lds_barrier();                                 // the key loads stay in flight
 
-  auto compute_group = [&](int64_t tg, const v8i* kb) {
-    float p[RG][4];
+  auto compute_group = [&](int32_t tg, const v8i* kb) {
+    float p[RG][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       v8h kh[4];
@@ -344,18 +349,29 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
       }
     }
     // per row, the transpose-reduce of index_score_kernel: lane (n, g) ends
-    // with the score of tile g, entry n
+    // with the score of tile g (U = 4) or g & 1 (U = 2, lanes g >= 2 hold a
+    // copy and store nothing), entry n; the adds pair the head groups as
+    // index_score_kernel does, so the scores are bit-identical
     const bool b0 = g & 1, b1 = (g >> 1) & 1;
-    const int64_t item = c0 + (tg + g) * 16 + n;
+    const int32_t item = c0 + (tg + (U == 4 ? g : (g & 1))) * 16 + n;
+    const bool owner = U == 4 || g < 2;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
-      float keep0 = b0 ? p[i][1] : p[i][0], send0 = b0 ? p[i][0] : p[i][1];
-      float keep1 = b0 ? p[i][3] : p[i][2], send1 = b0 ? p[i][2] : p[i][3];
-      keep0 += __shfl_xor(send0, 16);
-      keep1 += __shfl_xor(send1, 16);
-      float sc = b1 ? keep1 : keep0;
-      sc += __shfl_xor(b1 ? keep0 : keep1, 32);
-      if (item < c1 && item < nv[i]) {
+      float sc;
+      if (U == 4) {
+        float keep0 = b0 ? p[i][1] : p[i][0], send0 = b0 ? p[i][0] : p[i][1];
+        float keep1 = b0 ? p[i][3] : p[i][2], send1 = b0 ? p[i][2] : p[i][3];
+        keep0 += __shfl_xor(send0, 16);
+        keep1 += __shfl_xor(send1, 16);
+        sc = b1 ? keep1 : keep0;
+        sc += __shfl_xor(b1 ? keep0 : keep1, 32);
+      } else {
+        float keep = b0 ? p[i][1] : p[i][0];
+        const float send = b0 ? p[i][0] : p[i][1];
+        keep += __shfl_xor(send, 16);
+        sc = keep + __shfl_xor(keep, 32);
+      }
+      if (owner && item < c1 && item < nv[i]) {
         a.scores[(int64_t)(rbase + i) * a.row_stride + item] = sc;
         atomicAdd(&hist[i][order_key(sc) >> (32 - kHistBits)], 1u);
       }
@@ -364,7 +380,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
   // two groups per trip, no exit between them (a group past the chunk is
   // computed and discarded): the waits stay exact
   for (; t0 < ntiles; t0 += 2 * gstride) {
-    const int64_t t1 = t0 + gstride;
+    const int32_t t1 = t0 + gstride;
     load_group(t1, kB);
     __builtin_amdgcn_sched_barrier(0);
     compute_group(t0, kA);
@@ -424,7 +440,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
     c = (c + 255) / 256 * 256;
     b.chunk = (int32_t)c;
     const dim3 grid((unsigned)((a.im.n_items + c - 1) / c), (unsigned)groups), block(kScoreThreads);
-    hipLaunchKernelGGL((index_score_rows_kernel<kRowGroup>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((index_score_rows_kernel<kRowGroup, kRowTiles>), grid, block, 0, stream, b);
     return hipGetLastError();
   }
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
