@@ -153,6 +153,57 @@ __global__ __launch_bounds__(256) void block_summary_kernel(const uint8_t* __res
   *reinterpret_cast<uint32_t*>(summ + (s * nb_total + b) * kIdxDim + c4 * 4) = out;
 }
 
+// One thread = one (sequence, block, 16 channels), for 16-byte aligned keys
+// and summaries: each member is one 16-byte load (a wave's load covers 8
+// whole key rows) decoded with the hardware E4M3 conversion (exact).  The
+// members' sum is exact in float32 (multiples of 2^-9 below 2^12), so a full
+// block's mean is that sum times 1/8 -- the same value the division gives --
+// and the result equals block_summary_kernel's bit for bit.
+__global__ __launch_bounds__(256) void block_summary16_kernel(const uint8_t* __restrict__ keys,
+                                                              int64_t n_seq, int64_t n_ent,
+                                                              int64_t blk_begin, int64_t n_blk_range,
+                                                              uint8_t* __restrict__ summ) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_seq * n_blk_range * 8) return;
+  const int c16 = (int)(gid & 7);
+  const int64_t sb = gid >> 3;
+  const int64_t s = sb / n_blk_range;
+  const int64_t b = blk_begin + (sb - s * n_blk_range);
+  const int64_t nb_total = (n_ent + kBlockPos - 1) / kBlockPos;
+  const int64_t j0 = b * kBlockPos;
+  const int cnt = (int)min((int64_t)kBlockPos, n_ent - j0);
+  const uint8_t* base = keys + (s * n_ent + j0) * kIdxDim + c16 * 16;
+  uint4 w[kBlockPos];
+#pragma unroll
+  for (int j = 0; j < kBlockPos; ++j)
+    w[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(j < cnt ? j : 0) * kIdxDim);
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kBlockPos; ++j) {
+    if (j < cnt) {
+      const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww[q], true);
+        acc[4 * q] += lo[0];
+        acc[4 * q + 1] += lo[1];
+        acc[4 * q + 2] += hi[0];
+        acc[4 * q + 3] += hi[1];
+      }
+    }
+  }
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float m = cnt == kBlockPos ? acc[i] * (1.0f / kBlockPos) : __fdiv_rn(acc[i], (float)cnt);
+    out[i >> 2] |= f32_to_e4m3(m) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(summ + (s * nb_total + b) * kIdxDim + c16 * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // ---------------------------------------------------------------------------
 // FP4 index keys: 128 E2M1 codes + one E4M3 scale per 32 channels (68 B per
 // entry), quantised by the main-KV rule [daiw "four generations" table:
@@ -435,10 +486,16 @@ hipError_t launch_block_summary(const uint8_t* keys, int64_t n_seq, int64_t n_en
                                 int64_t blk_begin, int64_t blk_end, uint8_t* summ,
                                 hipStream_t stream) {
   const int64_t nr = blk_end - blk_begin;
-  const int64_t threads = n_seq * nr * 32;
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_summary_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, keys, n_seq, n_ent, blk_begin, nr, summ);
+  if (n_seq * nr == 0) return hipSuccess;
+  if (reinterpret_cast<uintptr_t>(keys) % 16 == 0 && reinterpret_cast<uintptr_t>(summ) % 16 == 0) {
+    const int64_t threads = n_seq * nr * 8;
+    hipLaunchKernelGGL(block_summary16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, keys, n_seq, n_ent, blk_begin, nr, summ);
+  } else {
+    const int64_t threads = n_seq * nr * 32;
+    hipLaunchKernelGGL(block_summary_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, keys, n_seq, n_ent, blk_begin, nr, summ);
+  }
   return hipGetLastError();
 }
 
