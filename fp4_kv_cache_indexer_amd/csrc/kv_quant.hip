@@ -66,12 +66,23 @@ __device__ __forceinline__ uint32_t pool_quantize16(const uint16_t* const* xs, c
       float mx = zv[0][c];
 #pragma unroll
       for (int j = 1; j < M; ++j) mx = fmaxf(mx, zv[j][c]);
+      float wj[M];
+      if (M == 2) {
+        // one of the two max-subtracted logits is exactly 0 and expf(0) is
+        // exactly 1: a single exponential gives the same two weights
+        const float d0 = zv[0][c] - mx, d1 = zv[1][c] - mx;
+        const float e = expf(fminf(d0, d1));
+        wj[0] = d0 == 0.0f ? 1.0f : e;
+        wj[M - 1] = d1 == 0.0f ? 1.0f : e;
+      } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) wj[j] = expf(zv[j][c] - mx);
+      }
       float num = 0.0f, den = 0.0f;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
-        const float w = expf(zv[j][c] - mx);
-        num = fmaf(w, xv[j][c], num);
-        den += w;
+        num = fmaf(wj[j], xv[j][c], num);
+        den += wj[j];
       }
       y[c] = __fdiv_rn(num, den);
     }
