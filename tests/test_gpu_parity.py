@@ -385,6 +385,27 @@ def test_index_key_quantize():
     assert np.array_equal(host(gc), codes) and np.array_equal(host(gs), scales)
 
 
+def test_block_summary_word_aligned_buffers():
+    # keys and summaries only 4-byte aligned take the 4-channel kernel; both
+    # kernels must give the oracle's summaries
+    say("index_block_summary on 4-byte aligned buffers, N=1003")
+    N = 1003
+    g = np.random.default_rng(7)
+    keys = synth.to_e4m3(g.standard_normal((2, N, 128)).astype(np.float32) * 4)
+    nb = (N + 7) // 8
+    kbuf = torch.zeros(2 * N * 128 + 16, dtype=torch.uint8, device="cuda")
+    kv = kbuf[4:4 + 2 * N * 128].view(2, N, 128)
+    kv.copy_(dev(keys))
+    sbuf = torch.zeros(2 * nb * 128 + 16, dtype=torch.uint8, device="cuda")
+    sv = sbuf[4:4 + 2 * nb * 128].view(2, nb, 128)
+    assert kv.data_ptr() % 16 == 4 and sv.data_ptr() % 16 == 4
+    C.index_block_summary(kv, summ=sv)
+    torch.cuda.synchronize()
+    gsum = host(sv)
+    for s in range(2):
+        assert np.array_equal(gsum[s], O.block_summary(keys[s])), s
+
+
 @pytest.mark.parametrize("N", [4096, 4093, 8, 5])
 def test_block_summary_fp4(N):
     say(f"block_summary_fp4 N={N}")
