@@ -5,6 +5,7 @@
 // Both are HBM streaming kernels: one thread owns one 16-channel group (K1)
 // or one 4-channel slice of a block (K2), so a wave reads contiguous runs of
 // the token/key rows and writes contiguous code/summary runs.
+#include "attn_dev.h"
 #include "csa2_dev.h"
 #include "csa2_launch.h"
 
@@ -295,6 +296,59 @@ __global__ __launch_bounds__(256) void block_summary_fp4_kernel(const uint8_t* _
   *reinterpret_cast<uint32_t*>(summ + (s * nb_total + b) * kIdxDim + c4 * 4) = out;
 }
 
+// The same summaries with one thread per (sequence, block, 16 channels), for
+// 8-byte aligned codes, 4-byte aligned scales and 16-byte aligned summaries:
+// a member is one 8-byte code load and its 4-byte scale word, decoded by the
+// hardware at unit scale (exact) and multiplied by the group scale (exact),
+// so every member value, the order of the sums and the result are those of
+// block_summary_fp4_kernel; a full block's mean is its sum times 1/8.
+__global__ __launch_bounds__(256) void block_summary_fp4_16_kernel(const uint8_t* __restrict__ codes,
+                                                                   const uint8_t* __restrict__ scales,
+                                                                   int64_t n_seq, int64_t n_ent,
+                                                                   int64_t blk_begin, int64_t n_blk_range,
+                                                                   uint8_t* __restrict__ summ) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_seq * n_blk_range * 8) return;
+  const int c16 = (int)(gid & 7);                 // channels 16*c16 .. 16*c16+15
+  const int64_t sb = gid >> 3;
+  const int64_t s = sb / n_blk_range;
+  const int64_t b = blk_begin + (sb - s * n_blk_range);
+  const int64_t nb_total = (n_ent + kBlockPos - 1) / kBlockPos;
+  const int64_t j0 = b * kBlockPos;
+  const int cnt = (int)min((int64_t)kBlockPos, n_ent - j0);
+  const uint8_t* cb = codes + (s * n_ent + j0) * 64 + c16 * 8;
+  const uint8_t* swp = scales + (s * n_ent + j0) * 4;
+  uint2 cw[kBlockPos];
+  uint32_t sw[kBlockPos];
+#pragma unroll
+  for (int j = 0; j < kBlockPos; ++j) {           // all member loads at once
+    const int jj = j < cnt ? j : 0;
+    cw[j] = *reinterpret_cast<const uint2*>(cb + (int64_t)jj * 64);
+    sw[j] = *reinterpret_cast<const uint32_t*>(swp + (int64_t)jj * 4);
+  }
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kBlockPos; ++j) {
+    if (j < cnt) {
+      const float sv = e4m3_to_f32((sw[j] >> (8 * (c16 >> 1))) & 0xFFu);   // the 32-channel group
+      float f[16];
+      fp4x8_to_f32(cw[j].x, sv, f);
+      fp4x8_to_f32(cw[j].y, sv, f + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += f[i];
+    }
+  }
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float m = cnt == kBlockPos ? acc[i] * (1.0f / kBlockPos) : __fdiv_rn(acc[i], (float)cnt);
+    out[i >> 2] |= f32_to_e4m3(m) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(summ + (s * nb_total + b) * kIdxDim + c16 * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Decode-time append: one launch per generated token and cache [0539edu §3:
 // m = 2 in the encoder, 1 in the decoder; 128-token FP8 window].
@@ -467,8 +521,14 @@ hipError_t launch_block_summary_fp4(const uint8_t* codes, const uint8_t* scales,
   const int64_t nr = blk_end - blk_begin;
   const int64_t threads = n_seq * nr * 32;
   if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_summary_fp4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, codes, scales, n_seq, n_ent, blk_begin, nr, summ);
+  if (reinterpret_cast<uintptr_t>(codes) % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 4 == 0 &&
+      reinterpret_cast<uintptr_t>(summ) % 16 == 0) {
+    hipLaunchKernelGGL(block_summary_fp4_16_kernel, dim3((unsigned)((threads / 4 + 255) / 256)), dim3(256), 0,
+                       stream, codes, scales, n_seq, n_ent, blk_begin, nr, summ);
+  } else {
+    hipLaunchKernelGGL(block_summary_fp4_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, codes, scales, n_seq, n_ent, blk_begin, nr, summ);
+  }
   return hipGetLastError();
 }
 

@@ -417,6 +417,25 @@ def test_block_summary_fp4(N):
         assert np.array_equal(gs[s], O.block_summary_fp4(codes[s], scales[s])), s
 
 
+def test_block_summary_fp4_word_aligned_buffers():
+    # FP4 codes and summaries only 4-byte aligned take the 4-channel kernel
+    say("block_summary_fp4 on 4-byte aligned buffers, N=1003")
+    N = 1003
+    _, codes, scales = fp4_key_case(77, 2, N)
+    nb = (N + 7) // 8
+    cbuf = torch.zeros(2 * N * 64 + 16, dtype=torch.uint8, device="cuda")
+    cv = cbuf[4:4 + 2 * N * 64].view(2, N, 64)
+    cv.copy_(dev(codes))
+    sbuf = torch.zeros(2 * nb * 128 + 16, dtype=torch.uint8, device="cuda")
+    sv = sbuf[4:4 + 2 * nb * 128].view(2, nb, 128)
+    assert cv.data_ptr() % 8 == 4 and sv.data_ptr() % 16 == 4
+    C.index_block_summary_fp4(cv, dev(scales), summ=sv)
+    torch.cuda.synchronize()
+    gs = host(sv)
+    for s in range(2):
+        assert np.array_equal(gs[s], O.block_summary_fp4(codes[s], scales[s])), s
+
+
 def fp4_idx_case(seed, S, N, R, **kw):
     case = idx_case(seed, S, N, R, **kw)
     _, codes, scales = fp4_key_case(seed + 100, S, N)
