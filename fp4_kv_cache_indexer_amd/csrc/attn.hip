@@ -41,7 +41,6 @@ constexpr int kPsLo = kKeyChunk * 2;            // offset of P's low fp16 terms 
 constexpr int kPsStride = kKeyChunk * 4 + 16;   // bytes per head row of P (hi + lo fp16 + pad)
 
 constexpr int kHeadsPerWG = 64;                 // up to 4 head groups of 16 per workgroup
-constexpr int kMaxPvTiles = (kD / 16) * (kHeadsPerWG / 16) / kAttnWaves;   // 16 channel tiles
 constexpr int kMaxKeysPerSplit = 1024;          // selected ids staged in LDS per workgroup
 
 struct AttnShared {
@@ -53,6 +52,7 @@ struct AttnShared {
   int32_t kvalid[kKeyChunk];
   int32_t sidx[kMaxKeysPerSplit];
 };
+static_assert(offsetof(AttnShared, sidx) % 16 == 0, "staged ids are read 4 at a time");
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -82,8 +82,13 @@ struct Gather {
 // fp16 weights P and the rescale factor of its heads to the other waves
 // through LDS.  All 8 waves then share the PV product: wave w owns one head
 // group and a block of channel tiles, so every lane rescales its
-// accumulators by a single factor.
+// accumulators by a single factor.  HG, the 16-head groups of a workgroup
+// (1, 2 or 4), is a compile-time constant so that the PV tile loop has no
+// branches: its LDS operand reads then overlap the MFMAs instead of each
+// tile waiting for its own read.
+template <int HG>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a) {
+  static_assert(HG == 1 || HG == 2 || HG == 4, "16-head groups per workgroup");
   extern __shared__ __align__(16) unsigned char attn_smem[];
   AttnShared& sh = *reinterpret_cast<AttnShared*>(attn_smem);
   const int split = blockIdx.x, r = blockIdx.y;
@@ -92,12 +97,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   const int n = lane & 15, g = lane >> 4;
   const int H = a.n_heads;
   const int hbase = blockIdx.z * kHeadsPerWG;
-  const int HG = min(kHeadsPerWG, H - hbase) / 16;          // head groups here: 1, 2 or 4
   const bool qk_wave = wave < HG;
   // PV: waves per head group, head group and first channel tile of this wave
-  const int wph = kAttnWaves / HG;
+  constexpr int wph = kAttnWaves / HG;
+  constexpr int pv_tiles = (kD / 16) / wph;
   const int pv_hg = wave / wph;
-  const int pv_tiles = (kD / 16) / wph;
   const int pv_ct0 = (wave % wph) * pv_tiles;
 
   const int64_t seq = a.row_seq ? a.row_seq[r] : r;
@@ -134,9 +138,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
   }
   float m_run = -INFINITY, l_run = 0.0f;                     // QK waves: head n of group `wave`
 
-  v4f acc[kMaxPvTiles];
+  v4f acc[pv_tiles];
 #pragma unroll
-  for (int t = 0; t < kMaxPvTiles; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < pv_tiles; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // this thread's unit of every chunk: keys t0..t0+3, channels c0..c0+7
   const int cb = tid & 63, kq = tid >> 6;
@@ -149,12 +153,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
 
   // issue every load of a chunk at once (no data-dependent branches)
   auto issue = [&](int kc, Gather& G) {
+    // the staged ids of keys kc+t0 .. kc+t0+3 in one aligned 16-byte read;
+    // a read clamped to the end of the stage only feeds keys past the
+    // staged (selected) ones, which do not use it
+    const int sb = min(kc - k0 + t0, kMaxKeysPerSplit - 4);
+    const int4 ids4 = *reinterpret_cast<const int4*>(&sh.sidx[sb]);
+    const int32_t ids[4] = {ids4.x, ids4.y, ids4.z, ids4.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = kc + t0 + j;
       const bool in_range = key < k1;
       const bool is_sel = in_range && key < nsel;
-      const int32_t p = is_sel ? sh.sidx[key - k0] : -1;
+      const int32_t p = is_sel ? ids[j] : -1;
       const bool ok = is_sel && p >= 0 && (int64_t)p < a.n_ent;
       const bool is_swa = in_range && !is_sel;
       int slot = swst + (key - nsel);
@@ -275,15 +285,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
       const v8h pb = *reinterpret_cast<const v8h*>(prow);
       const v8h pbl = *reinterpret_cast<const v8h*>(prow + kPsLo);
 #pragma unroll
-      for (int t = 0; t < kMaxPvTiles; ++t) {
-        if (t < pv_tiles) {
-          const int c = (pv_ct0 + t) * 16 + n;
-          const v8h ka = *reinterpret_cast<const v8h*>(sh.kt + kt_off(c, 16 * g));
-          v4f o = acc[t];
-          o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
-          o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pbl, o, 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pb, o, 0, 0, 0);
-        }
+      for (int t = 0; t < pv_tiles; ++t) {
+        const int c = (pv_ct0 + t) * 16 + n;
+        const v8h ka = *reinterpret_cast<const v8h*>(sh.kt + kt_off(c, 16 * g));
+        v4f o = acc[t];
+        o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pbl, o, 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, pb, o, 0, 0, 0);
       }
     }
   }
@@ -307,21 +315,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(AttnArgs a
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float* orow = a.out + rh * kD + 4 * g;
 #pragma unroll
-    for (int t = 0; t < kMaxPvTiles; ++t) {
-      if (t < pv_tiles) {
-        const v4f o = acc[t];
-        *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-      }
+    for (int t = 0; t < pv_tiles; ++t) {
+      const v4f o = acc[t];
+      *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     }
   } else {
     const int64_t base = (int64_t)split * a.n_rows * H + rh;
     float* orow = a.part_o + base * kD + 4 * g;
 #pragma unroll
-    for (int t = 0; t < kMaxPvTiles; ++t) {
-      if (t < pv_tiles) {
-        const v4f o = acc[t];
-        *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0], o[1], o[2], o[3]);
-      }
+    for (int t = 0; t < pv_tiles; ++t) {
+      const v4f o = acc[t];
+      *reinterpret_cast<float4*>(orow + (pv_ct0 + t) * 16) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -377,12 +381,21 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   if (a.heads_per_wg == 16) return launch_sparse_attn_narrow(a, stream);
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_attn_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)sizeof(AttnShared));
+  // every workgroup holds min(64, H) heads (H is 16, 32, 64 or 128)
+  const int hg = min(kHeadsPerWG, a.n_heads) / 16;
+  auto kern = hg == 4 ? &sparse_attn_kernel<4> : hg == 2 ? &sparse_attn_kernel<2> : &sparse_attn_kernel<1>;
+  static const hipError_t attr = [] {
+    hipError_t e = hipSuccess;
+    for (auto k : {&sparse_attn_kernel<1>, &sparse_attn_kernel<2>, &sparse_attn_kernel<4>}) {
+      const hipError_t ek = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnShared));
+      if (ek != hipSuccess) e = ek;
+    }
+    return e;
+  }();
   if (attr != hipSuccess) return attr;
   const int hblocks = (a.n_heads + kHeadsPerWG - 1) / kHeadsPerWG;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hblocks),
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_split, (unsigned)a.n_rows, (unsigned)hblocks),
                      dim3(kAttnThreads), sizeof(AttnShared), stream, a);
   return hipGetLastError();
 }
