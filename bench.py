@@ -641,6 +641,48 @@ PREFILL_C5 = dict(
     T=1 << 20, m=2, R=4096, H=64, k=512, W=128)
 
 
+def cpu_baseline_prefill(w, xb, zb, kb, qi, hw, qb, sw, base, seconds, write_stride=32, row_stride=64):
+    """Time the oracle on a bounded sample of the prefill step: the cache
+    write of every `write_stride`-th group of m tokens (scaled by the stride)
+    and the indexer + attention of rows 0, row_stride, 2*row_stride, ... until
+    `seconds` elapse (at least 2 rows; scaled to all rows).  Host arrays:
+    tokens and gate logits as bf16 bits [T, 512], index keys E4M3 [N, 128],
+    index queries E4M3 [R, 32, 128], head weights [R, 32], queries as bf16
+    bits [R, H, 512] and the window tokens E4M3 [T - base, 512] from token
+    `base` on."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import csa2 as O
+
+    T, m, R, k, W = w["T"], w["m"], w["R"], w["k"], w["W"]
+    N = T // m
+    groups = np.arange(0, N, write_stride)
+    tok = (groups[:, None] * m + np.arange(m)[None, :]).reshape(-1)
+    ts = time.perf_counter()
+    O.kv_compress_quantize(xb[tok], zb[tok], m)
+    t_write = (time.perf_counter() - ts) * (N / len(groups))
+    n, t_rows = 0, 0.0
+    for r in range(0, R, row_stride):
+        ts = time.perf_counter()
+        nv, lo, ln = O.prefill_row_view(T - R + r, m, W)
+        idx = O.indexer_topk_flat(qi[r], hw[r], kb, k, nv)
+        sel = idx[idx >= 0]
+        tk = (sel[:, None] * m + np.arange(m)[None, :]).reshape(-1)
+        codes, scales = O.kv_compress_quantize(xb[tk], zb[tk], m)
+        O.sparse_attn(qb[r], codes, scales, np.arange(len(sel)), sw, O.swa_slots(lo - base, ln, sw.shape[0]))
+        t_rows += time.perf_counter() - ts
+        n += 1
+        if n >= 2 and t_rows >= seconds:
+            break
+    t_step = t_write + t_rows / n * R
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    return {"value": R / t_step, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"cache write of 1 in {write_stride} entries ({len(groups)} entries, {t_write / (N / len(groups)):.1f} s, "
+                      f"scaled x{N / len(groups):.0f}) + indexer and attention of {n} rows strided by {row_stride} "
+                      f"({t_rows:.1f} s, scaled to {R} rows); oracle float64, NumPy/BLAS on {threads} threads; "
+                      f"estimated step {t_step:.0f} s"}
+
+
 def run_prefill(args):
     """One step = the C5 prefill chunk: the cache write of the whole 1M-token
     context, the 4096-row causal indexer and the 4096-row attention.  Each
@@ -727,6 +769,11 @@ def run_prefill(args):
                                  "bytes_per_launch": write_bytes},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        h16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        res["cpu_baseline"] = cpu_baseline_prefill(
+            w, h16(x[0]), h16(z[0]), keys[0].cpu().numpy(), q_idx.cpu().numpy(),
+            head_w.cpu().numpy().astype(np.float64), h16(q), swa[0].cpu().numpy(), base, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
