@@ -26,7 +26,11 @@ __device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r) {
   return nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
 }
 
+// Items row walks.  A row that sees no entry (n_valid 0, or a sequence
+// outside the cache) walks none in every mode: pool and candidate items
+// would otherwise be addressed from an invalid sequence's keys.
 __device__ __forceinline__ int64_t row_items(const ItemMap& im, int64_t nv) {
+  if (nv <= 0) return 0;
   if (im.mode == kItemsFlat) return nv;
   if (im.mode == kItemsBlocks) return (nv + kBlockPos - 1) / kBlockPos;
   return im.n_items;

@@ -27,9 +27,11 @@ the pages' own headings):
   factors), its "four generations" table (per-token global KV) and the
   "decode reads" section.
 
-Parity status: every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, exhaustive format tables, an independent library routine
-or brute force; none is "parity unpinned".
+Parity status: every public function here is exercised by a pin in
+``tests/test_oracle_*.py`` -- closed forms, exhaustive format tables, an
+independent library routine or brute force.  ``tests/test_oracle_coverage.py``
+checks that each of them is called by at least one of those pins, so a helper
+added without a pin fails the CPU suite; none is "parity unpinned".
 """
 
 from . import formats, csa2, accounting  # noqa: F401

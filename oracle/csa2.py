@@ -274,11 +274,6 @@ def index_scores(q, w, keys):
     return index_scores_dec(q, w, e4m3_decode(keys))
 
 
-def index_scores_fp4(q, w, codes, scales):
-    """index_scores for FP4 index keys (codes [N, 64], scales [N, 4])."""
-    return index_scores_dec(q, w, index_key_decode_fp4(codes, scales))
-
-
 def topk_select(scores, ids, k):
     """Top-k of (score, id) pairs: order by score descending, then id
     ascending; keep the first min(k, n); return the ids ascending, padded

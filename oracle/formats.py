@@ -1,8 +1,8 @@
 """Number formats of the CSA2 cache, written out from their definitions.
 
 * FP4 E2M1 -- the main-KV element format named ``fp4_e2m1`` in the inference
-  configuration [0539edu §3]; "2 exponent bits, 1 mantissa bit" [nxbn §3.1].
-  Bit fields (s, e, m), exponent bias 1, e = 0 is subnormal, no inf/NaN.
+  configuration [0539edu §3]; a sign bit, a 2-bit exponent with bias 1 and a
+  1-bit mantissa [nxbn §3.1].  e = 0 is subnormal; there is no inf or NaN.
 * FP8 E4M3 -- the per-16-channel scale (``e4m3_per_16_channel``) and the SWA
   cache (``swa_kv_dtype: fp8``) [0539edu §3].  Read as the OCP "FN" variant:
   bias 7, largest finite 448, no infinities, NaN = S.1111.111, subnormals down
@@ -99,8 +99,3 @@ def bf16_bits_to_f64(bits):
     """Decode bfloat16 bit patterns (uint16) exactly to float64."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
-
-
-def f64_to_f32(x):
-    """Round float64 to the nearest float32 (IEEE round-to-nearest-even)."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32)

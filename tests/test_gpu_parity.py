@@ -228,14 +228,14 @@ def test_indexer_hierarchical():
         sb = O.index_scores(q, w, bk[s][:nb])
         ref_idx, ref_blocks = O.indexer_topk_hier(q, w, case["keys"][s], bk[s], 512, nv, 300)
         check_topk(gb[r], ref_blocks, np.arange(nb), sb, 300, f"row {r} blocks")
+        # the fine stage on the pool the GPU kept (a near-tie at the coarse
+        # boundary may change it legitimately)
+        pool = O.pool_positions(gb[r], nv)
+        sc = O.index_scores(q, w, case["keys"][s][pool])
+        check_topk(gi[r], O.topk_select(sc, pool, 512), pool, sc, 512, f"row {r} fine")
+        check_topk_valid(gi[r], gb[r], q, w, case["keys"][s], nv, 512, f"row {r} fine")
         if np.array_equal(gb[r], ref_blocks):
-            pool = O.pool_positions(ref_blocks, nv)
-            sc = O.index_scores(q, w, case["keys"][s][pool])
-            check_topk(gi[r], ref_idx, pool, sc, 512, f"row {r} fine")
-        else:
-            # a near-tie at the coarse boundary changed the pool: the fine
-            # result must still be a valid top-k of the pool that was kept
-            check_topk_valid(gi[r], gb[r], q, w, case["keys"][s], nv, 512, f"row {r} fine")
+            assert np.array_equal(O.topk_select(sc, pool, 512), ref_idx)
 
 
 def check_topk_valid(ids, kept_blocks, q, w, keys, nv, k, what):
@@ -303,6 +303,50 @@ def test_indexer_block_pool():
         sc = O.index_scores(case["q"][r], case["w"][r], case["keys"][s][pool])
         ref = O.indexer_topk_pool(case["q"][r], case["w"][r], case["keys"][s], pool, 512, nv)
         check_topk(gi[r], ref, pool, sc, 512, f"row {r}")
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_indexer_rows_outside_the_cache_all_modes(fp4):
+    """Rows whose sequence is outside [0, n_seq) see no entry in every mode:
+    candidate, block pool and hierarchical calls give all -1 for them (and
+    read no key), while a valid row of the same call is selected normally."""
+    say(f"indexer rows with row_seq -1 and n_seq, {'FP4' if fp4 else 'E4M3'} keys, every mode")
+    S, N, k = 2, 5003, 64
+    rs = np.array([-1, 0, S, 1], np.int64)
+    case = idx_case(46, S, N, 4, row_seq=rs)
+    kw = {}
+    keys_o = [case["keys"][s] for s in range(S)]
+    if fp4:
+        _, codes, kscales = fp4_key_case(47, S, N)
+        case["keys"] = codes
+        kw["key_scales"] = dev(kscales)
+        keys_o = [O.Fp4Keys(codes[s], kscales[s]) for s in range(S)]
+    nb = (N + 7) // 8
+    g = np.random.default_rng(48)
+    cand = np.stack([g.permutation(N)[:900] for _ in range(4)]).astype(np.int32)
+    cblk = np.stack([np.sort(g.choice(nb, 120, replace=False)) for _ in range(4)]).astype(np.int32)
+    bk = np.stack([O.block_summary(keys_o[s]) for s in range(S)])
+    blocks = torch.full((4, 100), 7, dtype=torch.int32, device="cuda")
+    runs = {
+        "candidate": dict(cand=dev(cand)),
+        "block pool": dict(cand_blocks=dev(cblk)),
+        "hierarchical": dict(block_keys=dev(bk), keep_blocks=100, out_blocks=blocks),
+    }
+    for mode, extra in runs.items():
+        gi, gsc = run_indexer(case, k, **kw, **extra)
+        for r in (0, 2):
+            assert (gi[r] == -1).all() and (gsc[r] == 0).all(), f"{mode}: row {r} (row_seq {rs[r]})"
+        q, w = case["q"][1], case["w"][1]
+        if mode == "candidate":
+            ids = cand[1]
+        elif mode == "block pool":
+            ids = O.pool_positions(cblk[1], N)
+        else:
+            gb = host(blocks)
+            assert (gb[0] == -1).all() and (gb[2] == -1).all(), "hierarchical: kept blocks of invalid rows"
+            ids = O.pool_positions(gb[1], N)
+        sc = O.index_scores(q, w, keys_o[0][ids])
+        check_topk(gi[1], O.topk_select(sc, ids, k), ids, sc, k, f"{mode}: row 1")
 
 
 def test_indexer_wide_tie_bins():
@@ -500,10 +544,13 @@ def test_indexer_fp4_keys_hierarchical_and_block_pool():
         nb = (nv + 7) // 8
         sb = O.index_scores(case["q"][r], case["w"][r], bk[:nb])
         check_topk(gb[r], ref_blocks, np.arange(nb), sb, 300, f"row {r} blocks")
+        # the fine stage on the pool the GPU kept (equal to the oracle's
+        # unless a coarse swap inside the tie band changed it)
+        pool = O.pool_positions(gb[r], nv)
+        sc = O.index_scores(case["q"][r], case["w"][r], keys[pool])
+        check_topk(gi[r], O.topk_select(sc, pool, 512), pool, sc, 512, f"row {r} fine")
         if np.array_equal(gb[r], ref_blocks):
-            pool = O.pool_positions(ref_blocks, nv)
-            sc = O.index_scores(case["q"][r], case["w"][r], keys[pool])
-            check_topk(gi[r], ref_idx, pool, sc, 512, f"row {r} fine")
+            assert np.array_equal(O.topk_select(sc, pool, 512), ref_idx)
     # the Full layer's pool, rescored by a new query over FP4 keys
     case2 = dict(case, q=idx_case(45, 2, 8, 3)["q"])
     gi2, gsc2 = run_fp4_indexer(case2, 256, cand_blocks=blocks)
