@@ -103,7 +103,7 @@ EXPORTS = (
     "csa2_abi_version", "csa2_status_string", "csa2_last_error",
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
     "csa2_index_key_quantize", "csa2_index_block_summary_fp4", "csa2_decode_append",
-    "csa2_indexer_topk_workspace", "csa2_indexer_topk",
+    "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
 )
@@ -143,6 +143,8 @@ def lib():
     L.csa2_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
     L.csa2_indexer_topk.restype = i32
     L.csa2_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), vp, sz, vp]
+    L.csa2_indexer_topk_static.restype = i32
+    L.csa2_indexer_topk_static.argtypes = [ctypes.POINTER(IndexerArgs), vp]
     L.csa2_sparse_attn_workspace.restype = sz
     L.csa2_sparse_attn_workspace.argtypes = [ctypes.POINTER(AttnArgs)]
     L.csa2_sparse_attn_decode.restype = i32
@@ -372,6 +374,28 @@ def indexer_topk(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_
         # must be zero before first use; the library leaves it zeroed after
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(L.csa2_indexer_topk(ctypes.byref(a), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out_idx
+
+
+STATIC_SCRATCH_BYTES = 64 << 20   # CSA2_STATIC_SCRATCH_BYTES
+
+
+def indexer_topk_static(q, keys, top_k, head_w=None, row_seq=None, n_valid=None, block_keys=None,
+                        keep_blocks=2048, cand=None, out_idx=None, out_score=None, out_blocks=None,
+                        stream=None, cand_blocks=None, key_scales=None):
+    """indexer_topk without a workspace: the library's static per-GPU scratch
+    (at most STATIC_SCRATCH_BYTES; larger requests raise).  Calls that
+    overlap on one GPU race; keep them on one stream."""
+    for t, nm in ((q, "q"), (keys, "keys"), (head_w, "head_w"), (row_seq, "row_seq"),
+                  (n_valid, "n_valid"), (block_keys, "block_keys"), (cand, "cand"),
+                  (cand_blocks, "cand_blocks"), (key_scales, "key_scales")):
+        _dev(t, nm)
+    R = q.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((R, top_k), dtype=torch.int32, device=q.device)
+    a = _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, cand,
+                        out_idx, out_score, out_blocks, cand_blocks, key_scales)
+    _check(lib().csa2_indexer_topk_static(ctypes.byref(a), _stream(stream)))
     return out_idx
 
 

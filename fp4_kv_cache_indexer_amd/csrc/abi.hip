@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -242,6 +243,44 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   return CSA2_OK;
 }
 
+// ---- static scratch of csa2_indexer_topk_static ---------------------------
+
+// One array per GPU (each device holds its own copy at its own address).  In
+// host code `scratch` names a host-side stand-in: only the device address
+// from hipGetSymbolAddress, kept per device, is ever passed to a kernel.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices];
+
+int32_t static_scratch(char** out);
+int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s);
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[CSA2_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+int32_t static_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "indexer_topk_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSA2_EUNSUPPORTED, "indexer_topk_static: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "indexer_topk_static: hipGetSymbolAddress(scratch)");
+    if (!aligned(ptr, 256)) return fail(CSA2_EHIP, "indexer_topk_static: scratch not 256-byte aligned");
+    g_scratch_dev[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_dev[dev];
+  return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,8 +463,35 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   if (ws_bytes < p.total || (p.total && !ws))
     return fail(CSA2_EWORKSPACE, "indexer: workspace %zu bytes < %zu needed", ws_bytes, p.total);
   if (!aligned(ws, 256)) return fail(CSA2_EINVAL, "indexer: workspace not 256-byte aligned");
+  return run_indexer(a, p, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int32_t csa2_indexer_topk_static(const csa2_indexer_args* a, void* stream) {
+  g_err.clear();
+  IndexerPlan p;
+  int32_t st = check_indexer(a, &p, true);
+  if (st != CSA2_OK) return st;
+  if (a->n_rows == 0) return CSA2_OK;
+  if (p.total > (size_t)CSA2_STATIC_SCRATCH_BYTES)
+    return fail(CSA2_EWORKSPACE, "indexer_topk_static: %zu scratch bytes needed, the static array holds %zu",
+                p.total, (size_t)CSA2_STATIC_SCRATCH_BYTES);
+  char* w = nullptr;
+  if ((st = static_scratch(&w)) != CSA2_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
+  // the histograms (the plan's first bytes, up to the first score row) must
+  // start at zero; the array keeps whatever the last call on this GPU left
+  const size_t n_words = p.off_scores0 / 4;
+  hipError_t e = csa2::launch_zero_words(reinterpret_cast<uint32_t*>(w), n_words, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer_topk_static: clearing the histograms");
+  return run_indexer(a, p, w, s);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s) {
+  int32_t st;
 
   csa2::ItemMap im0{};
   im0.n_seq = a->n_seq;
@@ -516,6 +582,10 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* a, void* ws, size_t ws_bytes,
   return stage(CSA2_SITE_SCORE_POOL, im1, a->keys, a->n_ent, p.stride1, scores1, hist1, a->top_k,
                a->out_idx, a->out_score);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* a) {
   AttnPlan p;

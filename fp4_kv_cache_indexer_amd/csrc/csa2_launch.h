@@ -89,6 +89,9 @@ hipError_t launch_topk_select(const SelectArgs& a, hipStream_t stream);
 constexpr int64_t kRowMaxItems = 1 << 15;
 constexpr int32_t kRowMinRows = 256;
 hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream);
+// Zero n 32-bit words with a fill kernel (no memset node: the call may be
+// captured into a graph).
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);
 
 struct AttnArgs {
   int32_t n_rows, n_heads;

@@ -750,6 +750,18 @@ hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(((int64_t)n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, (int64_t)n);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_filter(const SelectArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.n_chunks == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)a.n_chunks, (unsigned)a.n_rows),

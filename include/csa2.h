@@ -297,6 +297,28 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Indexer + top-k that allocates nothing and takes no workspace: for callers
+ * that cannot call hipMalloc (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, modes, results and
+ * errors are those of csa2_indexer_topk.  Its scratch lives in a static
+ * device array of CSA2_STATIC_SCRATCH_BYTES inside the library; each GPU the
+ * library runs on holds its own copy until the process ends.
+ *   - A call whose csa2_indexer_topk_workspace() exceeds
+ *     CSA2_STATIC_SCRATCH_BYTES returns CSA2_EWORKSPACE before anything is
+ *     enqueued (e.g. hierarchical rows over 2^20 entries need about 1.6 MiB
+ *     each, so up to ~38 such rows fit).
+ *   - Every call first clears the part of the array that must start at zero
+ *     (the score histograms) with a small fill kernel on `stream`, then runs
+ *     the kernels of csa2_indexer_topk.
+ *   - All calls on one GPU share that GPU's array: calls that overlap on one
+ *     GPU (unordered streams, several host threads) race and give wrong
+ *     results.  Order them on one stream.
+ */
+#define CSA2_STATIC_SCRATCH_BYTES (64u << 20)
+
+int32_t csa2_indexer_topk_static(const csa2_indexer_args* args, void* stream);
+
+/*
  * Joint sparse + sliding-window attention for one decode step per row
  * [daiw "four factors" (one 512-dim latent shared by all heads);
  *  0539edu §3 (top_k, swa_window_size, fp8 SWA)].

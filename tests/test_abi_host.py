@@ -107,6 +107,21 @@ def test_indexer_validation_without_gpu():
 
 
 @needs_lib
+def test_static_indexer_refuses_oversized_requests_without_gpu():
+    """csa2_indexer_topk_static validates like csa2_indexer_topk and refuses a
+    request whose scratch exceeds the static array, before touching the GPU."""
+    L = C.lib()
+    a = _idx_args(q=None)
+    assert L.csa2_indexer_topk_static(ctypes.byref(a), None) == 1
+    big = _idx_args(n_rows=64, n_seq=64, n_ent=262144)
+    assert L.csa2_indexer_topk_workspace(ctypes.byref(big)) > C.STATIC_SCRATCH_BYTES
+    assert L.csa2_indexer_topk_static(ctypes.byref(big), None) == 3
+    assert "static" in C.last_error()
+    zero = _idx_args(n_rows=0)
+    assert L.csa2_indexer_topk_static(ctypes.byref(zero), None) == 0
+
+
+@needs_lib
 def test_attn_and_cache_write_validation_without_gpu():
     L = C.lib()
     a = C.AttnArgs()
