@@ -10,8 +10,11 @@
 //               per row then settles the k-th composite key exactly with an
 //               MSB-first radix select over the candidates of bin b* and
 //               writes the kept ones in candidate order (ascending position).
-//   short rows: one 1024-thread workgroup per row does both, with the
-//               candidates in LDS (the workspace when they do not fit).
+//   rows of up to 16384 items: one 1024-thread workgroup per row holds the
+//               row's keys in registers (16 per thread) and does both.
+//   longer rows with many rows per call (a prefill chunk): one workgroup
+//               per row streams the row, compacting candidates in LDS (the
+//               workspace when they do not fit), and selects.
 // The select leaves the row histogram zeroed for the next call.
 #include "csa2_dev.h"
 #include "csa2_launch.h"
@@ -68,23 +71,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
   return off + x - v;
 }
 
-constexpr int kStageCap = 4096;     // boundary-bin candidates staged in LDS
-
 constexpr int kSelThreads = 1024;  // select workgroup
-constexpr int kRegKeys = 8;        // candidates per thread held in registers by the select
-constexpr int kMaxChunks = kMaxItems / kFiltChunk;
-
-struct TopkShared {
-  int wsum[kSelThreads / 64];
-  int pair[3], n_stage;
-  int digit, above, dcount;
-  uint32_t hist[256];
-  int coff[kMaxChunks + 1];          // first flattened candidate of each chunk
-  union {
-    uint64_t stage[kStageCap];                                 // radix select
-    struct { int32_t pos[kMaxTopK]; float score[kMaxTopK]; } sel;  // candidate-mode sort
-  } u;
-};
 
 // One radix step's decision, taken by wave 0 from sh.hist[0..256): the digit
 // whose keys hold the need-th largest key (digits descending), the count of
@@ -219,13 +206,274 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
   if (tid == 0) a.cand_count[(int64_t)r * a.n_chunks + c] = (uint32_t)written;
 }
 
-// Select.  One workgroup per row settles the k-th composite key T exactly:
-// its top 12 bits are b*, the rest is found digit by digit (MSB first) among
-// the candidates of bin b*.  The kept candidates (keys >= T) are written in
-// candidate order, which is ascending position (candidate mode sorts).  The
-// row's histogram is then cleared for the next call.
+// Smallest score whose composite key lies in bin b* or above, as a float:
+// for non-NaN x, x >= it exactly when order_key(x) >= b* << (32 - kHistBits)
+// (the float order is the key order, and -0 and +0 share a key and compare
+// equal).  NaN, the mark of items a row cannot see, compares false.  Bins
+// below that of -inf hold only NaN patterns, so their threshold is -inf;
+// bins above that of +inf hold none but NaN, whose threshold keeps nothing.
+__device__ __forceinline__ float bin_floor(int bstar) {
+  if (bstar < 0) return -INFINITY;                           // every visible item is kept
+  const uint32_t k0 = (uint32_t)bstar << (32 - kHistBits);
+  const float f = order_key_inv(k0);
+  return (f != f && k0 < 0x80000000u) ? -INFINITY : f;
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident selection.  Every thread of a 1024-thread workgroup holds
+// NK composite keys of a run of consecutive items (0 = not a candidate), the
+// runs in item order across threads.  The row's histogram gives b*; the k-th
+// key T is settled by a radix select over the keys of bin b* with one barrier
+// per digit (three LDS histograms in rotation: the one a step fills, the one
+// the next step fills -- cleared two steps before -- and the one being
+// cleared), every wave taking the same digit decision from the same counts;
+// the kept keys (K >= T) are written in item order after one block scan.
+// ---------------------------------------------------------------------------
+
+constexpr int kRegThreads = 1024;
+constexpr int kRegWaves = kRegThreads / 64;
+
+struct __align__(16) RegShared {
+  uint32_t h[3][256];               // radix digit counts, rotated per step
+  int wsum[2][kRegWaves];           // wave totals of the two block scans
+  int thr[4];                       // b*, items above b*, items in b*
+  int flag;
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts and row
+// broadcasts; lanes a shift does not reach add 0).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order, and the
+// total; one barrier.  wsum must not be reused by another scan before a
+// further barrier.
+__device__ __forceinline__ int reg_block_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = x;
+  lds_barrier();
+  const int ws = lane < kRegWaves ? wsum[lane] : 0;
+  const int wi = wave_incl_scan(ws);
+  total = __builtin_amdgcn_readlane(wi, kRegWaves - 1);
+  const int before = wave > 0 ? __builtin_amdgcn_readlane(wi, wave - 1) : 0;
+  return before + x - v;
+}
+
+// b* and the counts of the row's histogram (thread t holds bins
+// 4095-4t .. 4092-4t, descending): the bin of the kk-th largest score, the
+// items above it and in it; b* = -1 when every visible item is kept.  Two
+// barriers; sh.thr is read back by every thread.
+// (Returned as RowThreshold{b*, above, in b*, kk}: its third field holds the
+// count in b* here, not the count in b* or above.)
+__device__ __forceinline__ RowThreshold reg_threshold(uint4 hq, int k, RegShared& sh) {
+  const uint32_t hv[4] = {hq.w, hq.z, hq.y, hq.x};           // descending bins
+  const int loc = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+  int total;
+  const int above = reg_block_scan(loc, sh.wsum[0], total);  // items in the bins above this thread's
+  const uint32_t kk = min((uint32_t)k, (uint32_t)total);
+  if (threadIdx.x == 0 && kk >= (uint32_t)total) { sh.thr[0] = -1; sh.thr[1] = 0; sh.thr[2] = total; }
+  if (kk < (uint32_t)total && (uint32_t)above < kk && (uint32_t)(above + loc) >= kk) {
+    uint32_t cum = (uint32_t)above;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cum < kk && cum + hv[i] >= kk) {
+        sh.thr[0] = kHistBins - 1 - 4 * (int)threadIdx.x - i; sh.thr[1] = (int)cum; sh.thr[2] = (int)hv[i];
+      }
+      cum += hv[i];
+    }
+  }
+  lds_barrier();
+  return RowThreshold{sh.thr[0], sh.thr[1], sh.thr[2], kk};
+}
+
+// The k-th composite key among the candidates: b* fixes its top 12 bits,
+// radix steps over the keys of bin b* the rest.  need = kk - items above b*,
+// in_bin = items in b*.  sh.h[0] and sh.h[1] must be zero on entry (and
+// their zeroing ordered before it by a barrier).  Uniform result.
+template <int NK>
+__device__ __forceinline__ uint64_t reg_radix(const uint64_t (&K)[NK], int bstar, int need, int in_bin,
+                                              RegShared& sh) {
+  if (bstar < 0) return 0;                                   // every candidate is kept
+  uint64_t prefix = (uint64_t)bstar;
+  if (need == in_bin) return prefix << 52;                   // the whole bin is kept
+  const int lane = threadIdx.x & 63;
+  for (int step = 0; step < 7; ++step) {
+    const int dshift = digit_shift(step), w = digit_width(step);
+    const uint32_t dmask = (1u << w) - 1u;
+    uint32_t* H = sh.h[step % 3];
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      if (K[i] != 0 && (K[i] >> (dshift + w)) == prefix) atomicAdd(&H[(K[i] >> dshift) & dmask], 1u);
+    lds_barrier();
+    // every wave: lane l holds digits 255-4l .. 252-4l (descending); the
+    // digit whose count crosses `need` from the top
+    const uint4 hq = *reinterpret_cast<const uint4*>(&H[252 - 4 * lane]);
+    const uint32_t hv[4] = {hq.w, hq.z, hq.y, hq.x};
+    const int loc = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+    const int incl = wave_incl_scan(loc);
+    const int excl = incl - loc;
+    int digit = 0, above = 0, dcount = 0;
+    if (excl < need && incl >= need) {
+      int cum = excl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < need && cum + (int)hv[i] >= need) { digit = 255 - 4 * lane - i; above = cum; dcount = (int)hv[i]; }
+        cum += (int)hv[i];
+      }
+    }
+    const uint64_t hit = __ballot(excl < need && incl >= need);
+    const int src = (int)__builtin_ctzll(hit);
+    digit = __builtin_amdgcn_readlane(digit, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    dcount = __builtin_amdgcn_readlane(dcount, src);
+    if (threadIdx.x < 256) sh.h[(step + 2) % 3][threadIdx.x] = 0u;   // read by the previous step only
+    need -= above;
+    prefix = (prefix << w) | (uint64_t)digit;
+    if (dcount == need || dshift == 0) return prefix << dshift;
+  }
+  return prefix;                                             // not reached
+}
+
+// Writes the kept keys (K != 0 and K >= T, none when kk == 0) of one set of
+// per-thread runs at slots base + their rank in item order (those below k)
+// to out_idx / out_score; returns how many the set keeps.  One barrier.
+template <int NK>
+__device__ __forceinline__ int reg_emit_at(const uint64_t (&K)[NK], uint64_t T, uint32_t kk, int k, int base,
+                                           int32_t* oi, float* os, RegShared& sh) {
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) cnt += (kk > 0 && K[i] != 0 && K[i] >= T) ? 1 : 0;
+  int total;
+  int slot = base + reg_block_scan(cnt, sh.wsum[1], total);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    if (kk > 0 && K[i] != 0 && K[i] >= T) {
+      if (slot < k) {
+        oi[slot] = comp_pos(K[i]);
+        if (os) os[slot] = comp_score(K[i]);
+      }
+      ++slot;
+    }
+  }
+  lds_barrier();                         // wsum[1] is free for the next set
+  return total;
+}
+
+// As reg_emit_at from slot 0, then the -1 padding up to k; returns the count
+// written (<= k).
+template <int NK>
+__device__ __forceinline__ int reg_emit(const uint64_t (&K)[NK], uint64_t T, uint32_t kk, int k, int32_t* oi,
+                                        float* os, RegShared& sh) {
+  const int n = min(reg_emit_at(K, T, kk, k, 0, oi, os, sh), k);
+  for (int j = n + (int)threadIdx.x; j < k; j += kRegThreads) {
+    oi[j] = -1;
+    if (os) os[j] = 0.0f;
+  }
+  return n;
+}
+
+// Whole rows of at most kRegRowItems items (flat, block or pool mode): thread
+// t holds items 16t .. 16t+15.
+constexpr int kRegRowNK = 16;
+__global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a) {
+  __shared__ RegShared sh;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = row_valid(a.im, r);
+  const int n_row = (int)row_items(a.im, nv);
+  int32_t* oi = a.out_idx + (int64_t)r * a.k;
+  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
+  if (n_row == 0) {                                            // uniform: nothing visible
+    for (int j = tid; j < a.k; j += kRegThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.0f;
+    }
+    return;
+  }
+  uint32_t* gh = a.hist + (int64_t)r * kHistBins;
+  const uint4 hq = *reinterpret_cast<const uint4*>(gh + kHistBins - 4 - 4 * tid);
+  const float* srow = a.scores + (int64_t)r * a.row_stride;
+  const int i0 = kRegRowNK * tid;
+  float4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int iu = i0 + 4 * u;
+    v[u] = *reinterpret_cast<const float4*>(srow + (iu < a.row_stride ? iu : 0));
+  }
+  int32_t blk[2] = {0, 0};
+  if (a.im.mode == kItemsPool) {                               // uniform
+    const int32_t* lrow = a.im.list + (int64_t)r * a.im.list_len;
+    blk[0] = lrow[min(2 * tid, a.im.list_len - 1)];
+    blk[1] = lrow[min(2 * tid + 1, a.im.list_len - 1)];
+  }
+  if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
+  const RowThreshold th = reg_threshold(hq, a.k, sh);        // its barriers order the zeroing too
+  const float thr = bin_floor(th.bstar);
+  uint64_t K[kRegRowNK];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = i0 + 4 * u + j;
+      const float x = x4[j];
+      const bool cand = item < n_row && x >= thr;              // NaN (not visible) compares false
+      const int32_t pos = a.im.mode == kItemsPool ? blk[(4 * u + j) >> 3] * kBlockPos + (item & 7) : item;
+      K[4 * u + j] = cand ? comp_key(order_key(x), pos) : 0ull;
+    }
+  }
+  const uint64_t T = reg_radix(K, th.bstar, (int)th.kk - th.c_above, th.n_cand, sh);
+  reg_emit(K, T, th.kk, a.k, oi, os, sh);
+  // leave the row's histogram zeroed for the next call
+  *reinterpret_cast<uint4*>(gh + kHistBins - 4 - 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Select after the filter: one workgroup per row settles the k-th composite
+// key T among the filter's candidates (compacted per chunk in item order, so
+// candidate order is ascending position) and writes the kept ones in that
+// order; candidate mode (caller lists in any order) sorts them by position
+// in LDS first.  Thread t speculatively loads 8 candidate slots of chunk
+// t / TPC (TPC threads per chunk) before the chunks' counts are known; when
+// no chunk holds more candidates than its threads' slots, the keys are then
+// in registers (slots past a chunk's count are masked).  Otherwise (wide
+// ties) the same steps walk every chunk's candidates in global memory,
+// 8192 per pass.
+constexpr int kSelNK = 8;
+
+struct __align__(16) SelShared {
+  RegShared reg;
+  int32_t pos[kMaxTopK];                  // candidate mode: kept ids and scores, sorted here
+  float score[kMaxTopK];
+};
+
+// One pass of the global walk: the 8 candidate slots of global slot index
+// (pass * kSelThreads + t) * 8 (chunk-major; past a chunk's count -> 0).
+__device__ __forceinline__ void sel_pass_keys(const SelectArgs& a, int r, int nch, int pass, uint64_t (&K)[kSelNK]) {
+  const int64_t g = ((int64_t)pass * kSelThreads + threadIdx.x) * kSelNK;
+  const int c = (int)min(g / kFiltChunk, (int64_t)nch - 1);
+  const int s0 = (int)(g - (int64_t)c * kFiltChunk);
+  const bool in = g < (int64_t)nch * kFiltChunk;
+  const int cnt = (int)a.cand_count[(int64_t)r * a.n_chunks + c];
+  const uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk + (in ? s0 : 0);
+#pragma unroll
+  for (int i = 0; i < kSelNK; i += 2) {
+    const uint4 q = *reinterpret_cast<const uint4*>(crow + i);
+    K[i] = (in && s0 + i < cnt) ? (((uint64_t)q.y << 32) | q.x) : 0ull;
+    K[i + 1] = (in && s0 + i + 1 < cnt) ? (((uint64_t)q.w << 32) | q.z) : 0ull;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) {
-  __shared__ TopkShared sh;
+  __shared__ SelShared shs;
+  RegShared& sh = shs.reg;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = row_valid(a.im, r);
   const int64_t n_row = row_items(a.im, nv);
@@ -238,207 +486,97 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
     }
     return;
   }
-  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
-  uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  const int64_t crow0 = (int64_t)r * a.n_chunks * kFiltChunk;
-  const uint32_t* cnt = a.cand_count + (int64_t)r * a.n_chunks;
-  // the chunks' candidate counts and the histogram are independent: both
-  // loads fly together
-  constexpr int kCpt = kMaxChunks / kSelThreads;
-  int cc[kCpt];
-#pragma unroll
-  for (int i = 0; i < kCpt; ++i) {
-    const int ch = kCpt * tid + i;
-    cc[i] = (int)cnt[min(ch, nch - 1)];
-  }
-  uint32_t hv[kHistBins / kSelThreads];
-  hist_load<kSelThreads>(gh, hv);
-  const RowThreshold th = hist_threshold<kSelThreads>(hv, a.k, sh.wsum, sh.pair);
-  const int bstar = th.bstar, c_above = th.c_above;
-  const uint32_t kk = th.kk;
-
-  // flattened candidate offsets: chunk ch holds [coff[ch], coff[ch + 1])
-  int n_cand;
-  {
-    int loc = 0;
-#pragma unroll
-    for (int i = 0; i < kCpt; ++i) {
-      const int ch = kCpt * tid + i;
-      cc[i] = ch < nch ? cc[i] : 0;
-      loc += cc[i];
-    }
-    int base = block_excl_scan<kSelThreads>(loc, sh.wsum, n_cand);
-#pragma unroll
-    for (int i = 0; i < kCpt; ++i) {
-      const int ch = kCpt * tid + i;
-      if (ch < nch) sh.coff[ch] = base;
-      base += cc[i];
-    }
-    if (tid == 0) sh.coff[nch] = n_cand;
-    __syncthreads();
-  }
-
-  // threshold T: the kk-th largest composite key (kept keys are >= T); its
-  // top 12 bits are b*, the rest is found digit by digit among the
-  // candidates of bin b*
   const bool sort = a.im.mode == kItemsCand;
-  uint64_t T = 0;
-  int nsel;
-  if (n_cand <= kSelThreads * kRegKeys) {                   // uniform
-    // each thread holds a run of kRegKeys consecutive candidates
-    const int j0 = tid * kRegKeys;
-    const int nm = max(0, min(kRegKeys, n_cand - j0));
-    uint64_t K[kRegKeys];
-    {
-      int lo = 0, hi = nch;                                  // last chunk with coff <= j0
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sh.coff[mid] <= j0) lo = mid; else hi = mid;
-      }
-      int ch = lo;
+  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
+  const int tpc = min(kFiltChunk / kSelNK, kSelThreads / nch);  // 0 when there are more chunks than threads
+  uint32_t* gh = a.hist + (int64_t)r * kHistBins;
+  const uint4 hq = *reinterpret_cast<const uint4*>(gh + kHistBins - 4 - 4 * tid);
+  const int c = tpc > 0 ? min(tid / tpc, nch - 1) : 0;           // threads past the chunks repeat the last
+  const int s0 = tpc > 0 ? kSelNK * (tid % tpc) : 0;
+  const int cnt = (int)a.cand_count[(int64_t)r * a.n_chunks + c];
+  const uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk + s0;
+  uint64_t K[kSelNK];
 #pragma unroll
-      for (int i = 0; i < kRegKeys; ++i) {
-        K[i] = 0;
-        if (i < nm) {
-          while (sh.coff[ch + 1] <= j0 + i) ++ch;
-          K[i] = a.cand[crow0 + (int64_t)ch * kFiltChunk + (j0 + i - sh.coff[ch])];
-        }
-      }
-    }
-    if (bstar >= 0) {
-      int need = (int)kk - c_above;
-      uint64_t prefix = (uint64_t)bstar;
-      for (int step = 0; step < 7; ++step) {
-        const int dshift = digit_shift(step), w = digit_width(step);
-        const uint32_t dmask = (1u << w) - 1u;
-        if (tid < 256) sh.hist[tid] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kRegKeys; ++i)
-          if (i < nm && (K[i] >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K[i] >> dshift) & dmask], 1u);
-        __syncthreads();
-        pick_digit(sh, need);
-        __syncthreads();
-        need -= sh.above;
-        prefix = (prefix << w) | (uint64_t)sh.digit;
-        const bool done = sh.dcount == need || dshift == 0;  // every key with this prefix is kept
-        __syncthreads();
-        if (done) {
-          T = prefix << dshift;
-          break;
-        }
-      }
-    }
-    // kept keys, written in candidate order
-    int nk = 0;
-#pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) nk += (i < nm && kk > 0 && K[i] >= T) ? 1 : 0;
-    int nout;
-    int slot = block_excl_scan<kSelThreads>(nk, sh.wsum, nout);
-#pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
-      if (i < nm && kk > 0 && K[i] >= T) {
-        if (slot < a.k) {
-          if (sort) {
-            sh.u.sel.pos[slot] = comp_pos(K[i]);
-            sh.u.sel.score[slot] = comp_score(K[i]);
-          } else {
-            oi[slot] = comp_pos(K[i]);
-            if (os) os[slot] = comp_score(K[i]);
-          }
-        }
-        ++slot;
-      }
-    }
-    nsel = min(nout, a.k);
-  } else {
-    // many candidates (wide ties): walk them in global memory, staging the
-    // candidates of bin b* in LDS when they fit
-    if (bstar >= 0) {
-      if (tid == 0) sh.n_stage = 0;
-      __syncthreads();
-      for (int ch = 0; ch < nch; ++ch) {
-        const int cn = (int)cnt[ch];
-        for (int j = tid; j < cn; j += kSelThreads) {
-          const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
-          if ((int)(K >> 52) == bstar) {
-            const int slot = atomicAdd(&sh.n_stage, 1);
-            if (slot < kStageCap) sh.u.stage[slot] = K;
-          }
-        }
-      }
-      __syncthreads();
-      const int n_st = sh.n_stage;
-      const bool staged = n_st <= kStageCap;
-      int need = (int)kk - c_above;
-      uint64_t prefix = (uint64_t)bstar;
-      for (int step = 0; step < 7; ++step) {
-        const int dshift = digit_shift(step), w = digit_width(step);
-        const uint32_t dmask = (1u << w) - 1u;
-        if (tid < 256) sh.hist[tid] = 0u;
-        __syncthreads();
-        if (staged) {
-          for (int j = tid; j < n_st; j += kSelThreads) {
-            const uint64_t K = sh.u.stage[j];
-            if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
-          }
-        } else {
-          for (int ch = 0; ch < nch; ++ch) {
-            const int cn = (int)cnt[ch];
-            for (int j = tid; j < cn; j += kSelThreads) {
-              const uint64_t K = a.cand[crow0 + (int64_t)ch * kFiltChunk + j];
-              if ((K >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K >> dshift) & dmask], 1u);
-            }
-          }
-        }
-        __syncthreads();
-        pick_digit(sh, need);
-        __syncthreads();
-        need -= sh.above;
-        prefix = (prefix << w) | (uint64_t)sh.digit;
-        const bool done = sh.dcount == need || dshift == 0;
-        __syncthreads();
-        if (done) {
-          T = prefix << dshift;
-          break;
-        }
-      }
-    }
-    int nout = 0;
-    for (int base = 0; base < n_cand; base += kSelThreads) {
-      const int j = base + tid;
-      uint64_t K = 0;
-      bool keep = false;
-      if (j < n_cand && kk > 0) {
-        int lo = 0, hi = nch;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (sh.coff[mid] <= j) lo = mid; else hi = mid;
-        }
-        K = a.cand[crow0 + (int64_t)lo * kFiltChunk + (j - sh.coff[lo])];
-        keep = K >= T;
-      }
-      int t;
-      const int slot = nout + block_excl_scan<kSelThreads>(keep ? 1 : 0, sh.wsum, t);
-      if (keep && slot < a.k) {
-        if (sort) {
-          sh.u.sel.pos[slot] = comp_pos(K);
-          sh.u.sel.score[slot] = comp_score(K);
-        } else {
-          oi[slot] = comp_pos(K);
-          if (os) os[slot] = comp_score(K);
-        }
-      }
-      nout += t;
-    }
-    nsel = min(nout, a.k);
+  for (int i = 0; i < kSelNK; i += 2) {
+    const uint4 q = *reinterpret_cast<const uint4*>(crow + i);
+    K[i] = ((uint64_t)q.y << 32) | q.x;
+    K[i + 1] = ((uint64_t)q.w << 32) | q.z;
   }
-
-  // candidate mode: the caller's list has any order, sort by position
-  if (sort) {
+  if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
+  if (tid == 0) sh.flag = tpc > 0 ? 0 : 1;
+  lds_barrier();
+  if (tpc > 0 && tid % tpc == 0 && tid < nch * tpc && cnt > kSelNK * tpc) sh.flag = 1;
+  const RowThreshold th = reg_threshold(hq, a.k, sh);        // its barriers publish the flag
+  const bool spill = sh.flag != 0;                             // uniform: a chunk overflows its slots
+  int32_t* sel_pos = sort ? shs.pos : oi;
+  float* sel_score = sort ? shs.score : os;
+  int nsel;
+  if (!spill) {
+    const bool mine = tid < nch * tpc;
+#pragma unroll
+    for (int i = 0; i < kSelNK; ++i) K[i] = (mine && s0 + i < cnt) ? K[i] : 0ull;
+    const uint64_t T = reg_radix(K, th.bstar, (int)th.kk - th.c_above, th.n_cand, sh);
+    nsel = reg_emit(K, T, th.kk, a.k, sel_pos, sel_score, sh);
+  } else {
+    const int passes = (int)(((int64_t)nch * kFiltChunk + kSelThreads * kSelNK - 1) / (kSelThreads * kSelNK));
+    // T: the radix steps of reg_radix, each counting over every pass
+    uint64_t T = 0;
+    int need = (int)th.kk - th.c_above;
+    if (th.bstar >= 0 && need != th.n_cand) {
+      uint64_t prefix = (uint64_t)th.bstar;
+      const int lane = tid & 63;
+      for (int step = 0; step < 7; ++step) {
+        const int dshift = digit_shift(step), w = digit_width(step);
+        const uint32_t dmask = (1u << w) - 1u;
+        uint32_t* H = sh.h[step % 3];
+        for (int pass = 0; pass < passes; ++pass) {
+          sel_pass_keys(a, r, nch, pass, K);
+#pragma unroll
+          for (int i = 0; i < kSelNK; ++i)
+            if (K[i] != 0 && (K[i] >> (dshift + w)) == prefix) atomicAdd(&H[(K[i] >> dshift) & dmask], 1u);
+        }
+        lds_barrier();
+        const uint4 q = *reinterpret_cast<const uint4*>(&H[252 - 4 * lane]);
+        const uint32_t hv[4] = {q.w, q.z, q.y, q.x};
+        const int loc = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+        const int incl = wave_incl_scan(loc), excl = incl - loc;
+        int digit = 0, above = 0, dcount = 0, cum = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (excl < need && incl >= need && cum < need && cum + (int)hv[i] >= need) {
+            digit = 255 - 4 * lane - i; above = cum; dcount = (int)hv[i];
+          }
+          cum += (int)hv[i];
+        }
+        const int src = (int)__builtin_ctzll(__ballot(excl < need && incl >= need));
+        digit = __builtin_amdgcn_readlane(digit, src);
+        above = __builtin_amdgcn_readlane(above, src);
+        dcount = __builtin_amdgcn_readlane(dcount, src);
+        if (tid < 256) sh.h[(step + 2) % 3][tid] = 0u;
+        need -= above;
+        prefix = (prefix << w) | (uint64_t)digit;
+        if (dcount == need || dshift == 0) { T = prefix << dshift; break; }
+      }
+    } else if (th.bstar >= 0) {
+      T = (uint64_t)th.bstar << 52;
+    }
+    // the kept keys, pass by pass, in candidate order
+    int base = 0;
+    for (int pass = 0; pass < passes; ++pass) {
+      sel_pass_keys(a, r, nch, pass, K);
+      base += reg_emit_at(K, T, th.kk, a.k, base, sel_pos, sel_score, sh);
+    }
+    nsel = min(base, a.k);
+    for (int j = nsel + tid; j < a.k; j += kSelThreads) {
+      sel_pos[j] = -1;
+      if (sel_score) sel_score[j] = 0.0f;
+    }
+  }
+  if (sort) {                                                  // candidate lists come in any order
+    __syncthreads();
     int n2 = 1;
     while (n2 < nsel) n2 <<= 1;
-    for (int i = nsel + tid; i < n2; i += kSelThreads) { sh.u.sel.pos[i] = 0x7FFFFFFF; sh.u.sel.score[i] = 0.f; }
+    for (int i = nsel + tid; i < n2; i += kSelThreads) { shs.pos[i] = 0x7FFFFFFF; shs.score[i] = 0.f; }
     __syncthreads();
     for (int size = 2; size <= n2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -446,28 +584,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
           const int j = i ^ stride;
           if (j > i) {
             const bool up = (i & size) == 0;
-            const int32_t pi = sh.u.sel.pos[i], pj = sh.u.sel.pos[j];
+            const int32_t pi = shs.pos[i], pj = shs.pos[j];
             if ((pi > pj) == up) {
-              sh.u.sel.pos[i] = pj; sh.u.sel.pos[j] = pi;
-              const float t2 = sh.u.sel.score[i]; sh.u.sel.score[i] = sh.u.sel.score[j]; sh.u.sel.score[j] = t2;
+              shs.pos[i] = pj; shs.pos[j] = pi;
+              const float t2 = shs.score[i]; shs.score[i] = shs.score[j]; shs.score[j] = t2;
             }
           }
         }
         __syncthreads();
       }
     }
-    for (int j = tid; j < nsel; j += kSelThreads) {
-      oi[j] = sh.u.sel.pos[j];
-      if (os) os[j] = sh.u.sel.score[j];
+    for (int j = tid; j < a.k; j += kSelThreads) {
+      oi[j] = j < nsel ? shs.pos[j] : -1;
+      if (os) os[j] = j < nsel ? shs.score[j] : 0.0f;
     }
   }
-  for (int j = nsel + tid; j < a.k; j += kSelThreads) {
-    oi[j] = -1;
-    if (os) os[j] = 0.0f;
-  }
-
   // leave the row's histogram zeroed for the next call
-  for (int b = tid; b < kHistBins; b += kSelThreads) gh[b] = 0u;
+  *reinterpret_cast<uint4*>(gh + kHistBins - 4 - 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -520,18 +653,6 @@ __device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float
   }
 }
 
-// Smallest score whose composite key lies in bin b* or above, as a float:
-// for non-NaN x, x >= it exactly when order_key(x) >= b* << (32 - kHistBits)
-// (the float order is the key order, and -0 and +0 share a key and compare
-// equal).  NaN, the mark of items a row cannot see, compares false.  Bins
-// below that of -inf hold only NaN patterns, so their threshold is -inf;
-// bins above that of +inf hold none but NaN, whose threshold keeps nothing.
-__device__ __forceinline__ float bin_floor(int bstar) {
-  if (bstar < 0) return -INFINITY;                           // every visible item is kept
-  const uint32_t k0 = (uint32_t)bstar << (32 - kHistBits);
-  const float f = order_key_inv(k0);
-  return (f != f && k0 < 0x80000000u) ? -INFINITY : f;
-}
 
 // Appends the round's items at or above the threshold to cbuf in item order.
 // Within a sub-round u an item's slot counts the kept items of lower lanes
@@ -742,6 +863,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
 
 hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
+  if (a.im.n_items <= kRegThreads * kRegRowNK && a.im.mode != kItemsCand) {
+    hipLaunchKernelGGL(topk_reg_row_kernel, dim3((unsigned)a.n_rows), dim3(kRegThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)sizeof(RowShared));
