@@ -166,22 +166,23 @@ class InputSet:
 
 def step(w, s):
     """One decode step for the whole batch (all hot-path rows)."""
-    # a0-a1: the new token -- the window of layer 0, the last entry (m tokens
-    # pooled; m = 1 in the decoder layers) with its index key and the summary
-    # of its block -- and the windows of the group's other layers
-    C.decode_append(s.x_tok, s.pos, s.codes, s.scales, s.k_tok, s.keys, m=w["m"], gate=s.z_tok,
-                    pend_x=s.pend_x, pend_gate=s.pend_z, key_scales=s.kscales, block_keys=s.summ,
-                    swa=s.rings[0])
+    # the windows of the group's other layers take the new token
     if s.ring_x is not None:
         C.window_append(s.ring_x, s.ring_pos, s.rings.view(-1, 128, 512), row_seq=s.ring_rows)
     idx = None
     for L, mode in enumerate(layers_of(w)):
-        # a2-a3: indexer scores + top-k (coarse-to-fine at 1M context); a7:
+        # a0-a3: the Full layer appends the new token -- the window of layer
+        # 0, the last entry (m tokens pooled; m = 1 in the decoder layers)
+        # with its index key and the summary of its block -- and selects with
+        # the indexer (coarse-to-fine at 1M context), in one library call
+        # (hierarchical: the append runs inside the coarse scan's launch); a7:
         # Reuse layers keep the selection, Reindex layers select anew (within
         # the Full layer's pool when the workload says so)
         if mode == "full":
-            C.indexer_topk(s.lq_idx[L], s.keys, w["k"], block_keys=s.summ, keep_blocks=w["keep"] or 2048,
-                           out_idx=s.idx, out_blocks=s.blocks, workspace=s.ws_idx, key_scales=s.kscales)
+            C.append_indexer_topk(s.x_tok, s.pos, s.codes, s.scales, s.k_tok, s.lq_idx[L], s.keys, w["k"], s.summ,
+                                  m=w["m"], gate=s.z_tok, pend_x=s.pend_x, pend_gate=s.pend_z,
+                                  key_scales=s.kscales, swa=s.rings[0], keep_blocks=w["keep"] or 2048,
+                                  out_idx=s.idx, out_blocks=s.blocks, workspace=s.ws_idx)
             idx = s.idx
         elif mode == "reindex":
             if s.pool:

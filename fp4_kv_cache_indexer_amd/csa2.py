@@ -103,7 +103,7 @@ EXPORTS = (
     "csa2_abi_version", "csa2_status_string", "csa2_last_error",
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
     "csa2_index_key_quantize", "csa2_index_block_summary_fp4", "csa2_decode_append",
-    "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static",
+    "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static", "csa2_append_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
 )
@@ -143,6 +143,8 @@ def lib():
     L.csa2_indexer_topk_workspace.argtypes = [ctypes.POINTER(IndexerArgs)]
     L.csa2_indexer_topk.restype = i32
     L.csa2_indexer_topk.argtypes = [ctypes.POINTER(IndexerArgs), vp, sz, vp]
+    L.csa2_append_indexer_topk.restype = i32
+    L.csa2_append_indexer_topk.argtypes = [ctypes.POINTER(AppendArgs), ctypes.POINTER(IndexerArgs), vp, sz, vp]
     L.csa2_indexer_topk_static.restype = i32
     L.csa2_indexer_topk_static.argtypes = [ctypes.POINTER(IndexerArgs), vp]
     L.csa2_sparse_attn_workspace.restype = sz
@@ -265,14 +267,8 @@ def index_block_summary_fp4(codes, scales, summ=None, blk_begin=0, blk_end=None,
     return summ
 
 
-def decode_append(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None, pend_gate=None,
-                  key_scales=None, block_keys=None, swa=None, row_seq=None, stream=None):
-    """Append one token per row (x: bf16 [R, 512], pos: int64 [R]) to the
-    caches of sequences row_seq (identity when None): window ring slot
-    pos % swa_cap, the pending group for m > 1, and when a group completes
-    entry pos // m (codes/scales), its index key (key: bf16 [R, 128]; E4M3
-    keys [S, N, 128] or FP4 keys [S, N, 64] with key_scales [S, N, 4]) and
-    the summary of its block (block_keys [S, ceil(N/8), 128])."""
+def _append_struct(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None, pend_gate=None,
+                   key_scales=None, block_keys=None, swa=None, row_seq=None):
     for name, t in (("x", x), ("pos", pos), ("codes", codes), ("scales", scales), ("key", key),
                     ("keys", keys), ("gate", gate), ("pend_x", pend_x), ("pend_gate", pend_gate),
                     ("key_scales", key_scales), ("block_keys", block_keys), ("swa", swa),
@@ -298,7 +294,45 @@ def decode_append(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None,
     a.block_keys = _ptr(block_keys)
     a.swa = _ptr(swa)
     a.swa_cap = 0 if swa is None else swa.shape[1]
+    return a
+
+
+def decode_append(x, pos, codes, scales, key, keys, m=1, gate=None, pend_x=None, pend_gate=None,
+                  key_scales=None, block_keys=None, swa=None, row_seq=None, stream=None):
+    """Append one token per row (x: bf16 [R, 512], pos: int64 [R]) to the
+    caches of sequences row_seq (identity when None): window ring slot
+    pos % swa_cap, the pending group for m > 1, and when a group completes
+    entry pos // m (codes/scales), its index key (key: bf16 [R, 128]; E4M3
+    keys [S, N, 128] or FP4 keys [S, N, 64] with key_scales [S, N, 4]) and
+    the summary of its block (block_keys [S, ceil(N/8), 128])."""
+    a = _append_struct(x, pos, codes, scales, key, keys, m, gate, pend_x, pend_gate, key_scales, block_keys,
+                       swa, row_seq)
     _check(lib().csa2_decode_append(ctypes.byref(a), _stream(stream)))
+
+
+def append_indexer_topk(x, pos, codes, scales, key, q, keys, top_k, block_keys, m=1, gate=None, pend_x=None,
+                        pend_gate=None, key_scales=None, swa=None, row_seq=None, head_w=None, n_valid=None,
+                        keep_blocks=2048, out_idx=None, out_score=None, out_blocks=None, workspace=None,
+                        stream=None):
+    """decode_append(...) then indexer_topk(q, keys, top_k, block_keys=...)
+    over the same rows and caches, as one library call (the append runs
+    inside the coarse scan's launch).  Returns out_idx."""
+    a = _append_struct(x, pos, codes, scales, key, keys, m, gate, pend_x, pend_gate, key_scales, block_keys,
+                       swa, row_seq)
+    for t, nm in ((q, "q"), (head_w, "head_w"), (n_valid, "n_valid")):
+        _dev(t, nm)
+    R = q.shape[0]
+    if out_idx is None:
+        out_idx = torch.empty((R, top_k), dtype=torch.int32, device=q.device)
+    b = _indexer_struct(q, keys, top_k, head_w, row_seq, n_valid, block_keys, keep_blocks, None,
+                        out_idx, out_score, out_blocks, None, key_scales)
+    L = lib()
+    need = L.csa2_indexer_topk_workspace(ctypes.byref(b))
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(L.csa2_append_indexer_topk(ctypes.byref(a), ctypes.byref(b), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return out_idx
 
 
 def window_append(x, pos, swa, row_seq=None, stream=None):

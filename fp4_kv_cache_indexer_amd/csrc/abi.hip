@@ -160,13 +160,15 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
   return CSA2_OK;
 }
 
-int32_t score_chunk(int64_t n_items, int64_t rows) {
+int32_t score_chunk(int64_t n_items, int64_t rows, int extra_per_row = 0) {
   // one full round of resident workgroups: as many chunks as fit on the
   // device at once (no tail round), in whole 16-item tiles, so that every
   // slot gets a chunk and no compute unit takes a third more work than
-  // another (a wave's last group of tiles may be partial)
+  // another (a wave's last group of tiles may be partial); extra_per_row
+  // slots per row are left to other workgroups of the same launch
   const int64_t slots = csa2::score_resident_wgs();
-  const int64_t per_row_wgs = rows >= slots ? 1 : slots / rows;
+  int64_t per_row_wgs = rows >= slots ? 1 : slots / rows - extra_per_row;
+  if (per_row_wgs < 1) per_row_wgs = 1;
   int64_t c = (n_items + per_row_wgs - 1) / per_row_wgs;
   c = (c + 15) / 16 * 16;
   if (c < 256) c = 256;
@@ -243,6 +245,72 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   return CSA2_OK;
 }
 
+// Validates an append and fills the kernel arguments (k->n_rows = 0 when
+// there is nothing to launch).
+int32_t check_append(const csa2_append_args* a, csa2::AppendArgs* out) {
+  if (!a) return fail(CSA2_EINVAL, "decode_append: NULL args");
+  if (!a->codes) {                // window-only rows
+    if (a->n_rows < 0 || a->n_seq < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
+    if (a->n_rows == 0) { out->n_rows = 0; return CSA2_OK; }
+    if (!a->swa || a->swa_cap < 1 || !a->pos || !a->x_bf16)
+      return fail(CSA2_EINVAL, "decode_append: window-only rows need swa, swa_cap >= 1, pos and x");
+    if (!aligned(a->x_bf16, 16) || !aligned(a->pos, 8) || !aligned(a->swa, 4) ||
+        (a->row_seq && !aligned(a->row_seq, 4)))
+      return fail(CSA2_EINVAL, "decode_append: x/pos/swa/row_seq misaligned");
+    csa2::AppendArgs k{};
+    k.n_rows = a->n_rows;
+    k.n_seq = a->n_seq;
+    k.row_seq = a->row_seq;
+    k.pos = a->pos;
+    k.m = 1;
+    k.x = static_cast<const uint16_t*>(a->x_bf16);
+    k.swa = a->swa;
+    k.swa_cap = a->swa_cap;
+    *out = k;
+    return CSA2_OK;
+  }
+  if (a->m != 1 && a->m != 2 && a->m != 4) return fail(CSA2_EUNSUPPORTED, "decode_append: m=%d not in {1,2,4}", a->m);
+  if (a->key_format != CSA2_KEY_E4M3 && a->key_format != CSA2_KEY_FP4)
+    return fail(CSA2_EUNSUPPORTED, "decode_append: key_format %d unknown", a->key_format);
+  if (a->n_rows < 0 || a->n_seq < 0 || a->n_ent < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
+  if (a->n_rows == 0) { out->n_rows = 0; return CSA2_OK; }
+  if (!a->pos || !a->x_bf16 || !a->scales || !a->key_bf16 || !a->keys)
+    return fail(CSA2_EINVAL, "decode_append: pos, x, scales, key and keys are required with codes");
+  if (a->m > 1 && !a->pend_x) return fail(CSA2_EINVAL, "decode_append: m > 1 needs pend_x");
+  if (a->m > 1 && a->gate_bf16 && !a->pend_gate) return fail(CSA2_EINVAL, "decode_append: a gate needs pend_gate");
+  if (a->key_format == CSA2_KEY_FP4 && !a->key_scales) return fail(CSA2_EINVAL, "decode_append: FP4 keys need key_scales");
+  if (a->swa && a->swa_cap < 1) return fail(CSA2_EINVAL, "decode_append: swa_cap %d < 1", a->swa_cap);
+  if (!aligned(a->x_bf16, 16) || (a->gate_bf16 && !aligned(a->gate_bf16, 16)) ||
+      (a->pend_x && !aligned(a->pend_x, 16)) || (a->pend_gate && !aligned(a->pend_gate, 16)) ||
+      !aligned(a->key_bf16, 8) || !aligned(a->pos, 8) || (a->row_seq && !aligned(a->row_seq, 4)))
+    return fail(CSA2_EINVAL, "decode_append: x/gate/pending/key/pos misaligned");
+  if (!aligned(a->codes, 8) || !aligned(a->keys, 8) || (a->block_keys && !aligned(a->block_keys, 4)) ||
+      (a->swa && !aligned(a->swa, 4)))
+    return fail(CSA2_EINVAL, "decode_append: codes/keys/block_keys/swa misaligned");
+  csa2::AppendArgs k;
+  k.n_rows = a->n_rows;
+  k.n_seq = a->n_seq;
+  k.row_seq = a->row_seq;
+  k.pos = a->pos;
+  k.m = a->m;
+  k.x = static_cast<const uint16_t*>(a->x_bf16);
+  k.gate = a->m > 1 ? static_cast<const uint16_t*>(a->gate_bf16) : nullptr;
+  k.pend_x = static_cast<uint16_t*>(a->pend_x);
+  k.pend_gate = static_cast<uint16_t*>(a->pend_gate);
+  k.n_ent = a->n_ent;
+  k.codes = a->codes;
+  k.scales = a->scales;
+  k.key = static_cast<const uint16_t*>(a->key_bf16);
+  k.key_fp4 = a->key_format == CSA2_KEY_FP4;
+  k.keys = a->keys;
+  k.key_scales = a->key_scales;
+  k.block_keys = a->block_keys;
+  k.swa = a->swa;
+  k.swa_cap = a->swa ? a->swa_cap : 1;
+  *out = k;
+  return CSA2_OK;
+}
+
 // ---- static scratch of csa2_indexer_topk_static ---------------------------
 
 // One array per GPU (each device holds its own copy at its own address).  In
@@ -253,7 +321,8 @@ std::mutex g_scratch_mu;
 char* g_scratch_dev[kMaxDevices];
 
 int32_t static_scratch(char** out);
-int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s);
+int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s,
+                    const csa2::AppendArgs* fused = nullptr);
 
 }  // namespace
 
@@ -327,66 +396,10 @@ int32_t csa2_kv_compress_quantize(const void* x_bf16, const void* gate_bf16, int
 
 int32_t csa2_decode_append(const csa2_append_args* a, void* stream) {
   g_err.clear();
-  if (!a) return fail(CSA2_EINVAL, "decode_append: NULL args");
+  csa2::AppendArgs k{};
+  const int32_t st = check_append(a, &k);
+  if (st != CSA2_OK || k.n_rows == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!a->codes) {                // window-only rows
-    if (a->n_rows < 0 || a->n_seq < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
-    if (a->n_rows == 0) return CSA2_OK;
-    if (!a->swa || a->swa_cap < 1 || !a->pos || !a->x_bf16)
-      return fail(CSA2_EINVAL, "decode_append: window-only rows need swa, swa_cap >= 1, pos and x");
-    if (!aligned(a->x_bf16, 16) || !aligned(a->pos, 8) || !aligned(a->swa, 4) ||
-        (a->row_seq && !aligned(a->row_seq, 4)))
-      return fail(CSA2_EINVAL, "decode_append: x/pos/swa/row_seq misaligned");
-    csa2::AppendArgs k{};
-    k.n_rows = a->n_rows;
-    k.n_seq = a->n_seq;
-    k.row_seq = a->row_seq;
-    k.pos = a->pos;
-    k.m = 1;
-    k.x = static_cast<const uint16_t*>(a->x_bf16);
-    k.swa = a->swa;
-    k.swa_cap = a->swa_cap;
-    hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
-    return e == hipSuccess ? CSA2_OK : hip_fail(e, "decode_append launch");
-  }
-  if (a->m != 1 && a->m != 2 && a->m != 4) return fail(CSA2_EUNSUPPORTED, "decode_append: m=%d not in {1,2,4}", a->m);
-  if (a->key_format != CSA2_KEY_E4M3 && a->key_format != CSA2_KEY_FP4)
-    return fail(CSA2_EUNSUPPORTED, "decode_append: key_format %d unknown", a->key_format);
-  if (a->n_rows < 0 || a->n_seq < 0 || a->n_ent < 0) return fail(CSA2_EINVAL, "decode_append: negative size");
-  if (a->n_rows == 0) return CSA2_OK;
-  if (!a->pos || !a->x_bf16 || !a->scales || !a->key_bf16 || !a->keys)
-    return fail(CSA2_EINVAL, "decode_append: pos, x, scales, key and keys are required with codes");
-  if (a->m > 1 && !a->pend_x) return fail(CSA2_EINVAL, "decode_append: m > 1 needs pend_x");
-  if (a->m > 1 && a->gate_bf16 && !a->pend_gate) return fail(CSA2_EINVAL, "decode_append: a gate needs pend_gate");
-  if (a->key_format == CSA2_KEY_FP4 && !a->key_scales) return fail(CSA2_EINVAL, "decode_append: FP4 keys need key_scales");
-  if (a->swa && a->swa_cap < 1) return fail(CSA2_EINVAL, "decode_append: swa_cap %d < 1", a->swa_cap);
-  if (!aligned(a->x_bf16, 16) || (a->gate_bf16 && !aligned(a->gate_bf16, 16)) ||
-      (a->pend_x && !aligned(a->pend_x, 16)) || (a->pend_gate && !aligned(a->pend_gate, 16)) ||
-      !aligned(a->key_bf16, 8) || !aligned(a->pos, 8) || (a->row_seq && !aligned(a->row_seq, 4)))
-    return fail(CSA2_EINVAL, "decode_append: x/gate/pending/key/pos misaligned");
-  if (!aligned(a->codes, 8) || !aligned(a->keys, 8) || (a->block_keys && !aligned(a->block_keys, 4)) ||
-      (a->swa && !aligned(a->swa, 4)))
-    return fail(CSA2_EINVAL, "decode_append: codes/keys/block_keys/swa misaligned");
-  csa2::AppendArgs k;
-  k.n_rows = a->n_rows;
-  k.n_seq = a->n_seq;
-  k.row_seq = a->row_seq;
-  k.pos = a->pos;
-  k.m = a->m;
-  k.x = static_cast<const uint16_t*>(a->x_bf16);
-  k.gate = a->m > 1 ? static_cast<const uint16_t*>(a->gate_bf16) : nullptr;
-  k.pend_x = static_cast<uint16_t*>(a->pend_x);
-  k.pend_gate = static_cast<uint16_t*>(a->pend_gate);
-  k.n_ent = a->n_ent;
-  k.codes = a->codes;
-  k.scales = a->scales;
-  k.key = static_cast<const uint16_t*>(a->key_bf16);
-  k.key_fp4 = a->key_format == CSA2_KEY_FP4;
-  k.keys = a->keys;
-  k.key_scales = a->key_scales;
-  k.block_keys = a->block_keys;
-  k.swa = a->swa;
-  k.swa_cap = a->swa ? a->swa_cap : 1;
   hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "decode_append launch");
 }
@@ -486,11 +499,43 @@ int32_t csa2_indexer_topk_static(const csa2_indexer_args* a, void* stream) {
   return run_indexer(a, p, w, s);
 }
 
+int32_t csa2_append_indexer_topk(const csa2_append_args* ap, const csa2_indexer_args* a, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  g_err.clear();
+  csa2::AppendArgs k{};
+  int32_t st = check_append(ap, &k);
+  if (st != CSA2_OK) return st;
+  IndexerPlan p;
+  if ((st = check_indexer(a, &p, true)) != CSA2_OK) return st;
+  if (a->n_rows > 0 && (ws_bytes < p.total || (p.total && !ws)))
+    return fail(CSA2_EWORKSPACE, "append_indexer: workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if (a->n_rows > 0 && !aligned(ws, 256)) return fail(CSA2_EINVAL, "append_indexer: workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // one launch for the append and the coarse scan when they describe the
+  // same rows of the same caches, row r being sequence r (no row_seq): each
+  // row's scan then reads only the block summaries its own append refreshes
+  const bool fuse = p.mode == 1 && k.n_rows > 0 && ap->codes && ap->block_keys == a->block_keys &&
+                    ap->keys == a->keys && ap->key_format == a->key_format &&
+                    (a->key_format == CSA2_KEY_E4M3 || ap->key_scales == a->key_scales) &&
+                    ap->n_rows == a->n_rows && !ap->row_seq && !a->row_seq && ap->n_seq == a->n_seq &&
+                    ap->n_ent == a->n_ent && (ap->m == 1 || ap->m == 2);
+  if (!fuse) {
+    if (k.n_rows > 0) {
+      hipError_t e = timed(CSA2_SITE_APPEND, s, [&] { return csa2::launch_decode_append(k, s); });
+      if (e != hipSuccess) return hip_fail(e, "decode_append launch");
+    }
+    if (a->n_rows == 0) return CSA2_OK;
+    return run_indexer(a, p, static_cast<char*>(ws), s);
+  }
+  return run_indexer(a, p, static_cast<char*>(ws), s, &k);
+}
+
 }  // extern "C"
 
 namespace {
 
-int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s) {
+int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, hipStream_t s,
+                    const csa2::AppendArgs* fused) {
   int32_t st;
 
   csa2::ItemMap im0{};
@@ -529,7 +574,11 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
     sa.row_stride = stride;
     sa.scores = scores;
     sa.hist = hist;
-    sa.chunk = score_chunk(im.n_items, p.R);
+    // the coarse stage of a fused decode step also runs the append, in one
+    // extra workgroup per row (its slots are kept free)
+    sa.fuse_append = (fused && im.mode == csa2::kItemsBlocks) ? 1 : 0;
+    if (sa.fuse_append) sa.app = *fused;
+    sa.chunk = score_chunk(im.n_items, p.R, sa.fuse_append);
     if ((e2 = timed(site, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
       return hip_fail(e2, "indexer score");
     se.im = im;

@@ -45,6 +45,30 @@ struct ItemMap {
 constexpr int kFiltChunk = 4096;          // items per filter workgroup
 constexpr int64_t kMaxItems = 1LL << 24;  // items one top-k stage walks per row
 
+// One new token per row: window ring, pending group or a completed entry
+// with its index key and block summary.
+struct AppendArgs {
+  int32_t n_rows;
+  int64_t n_seq;
+  const int32_t* row_seq;
+  const int64_t* pos;
+  int32_t m;
+  const uint16_t* x;
+  const uint16_t* gate;
+  uint16_t* pend_x;
+  uint16_t* pend_gate;
+  int64_t n_ent;
+  uint8_t* codes;
+  uint8_t* scales;
+  const uint16_t* key;
+  bool key_fp4;
+  uint8_t* keys;
+  uint8_t* key_scales;
+  uint8_t* block_keys;
+  uint8_t* swa;
+  int32_t swa_cap;
+};
+
 struct ScoreArgs {
   ItemMap im;
   int32_t row_stride;       // floats between score rows (multiple of 4)
@@ -60,6 +84,12 @@ struct ScoreArgs {
   float* scores;            // [R][n_items]
   uint32_t* hist;           // [R][kHistBins]
   int32_t chunk;            // items per workgroup
+  // The decode step's append (coarse stage only): row r's token is appended
+  // by an extra workgroup of row r (the grid's last column), and the
+  // workgroup whose chunk holds the block of the entry the token completes
+  // scores that block's refreshed summary, computed in its own registers.
+  int32_t fuse_append;      // 0 or 1
+  AppendArgs app;
 };
 
 struct SelectArgs {
@@ -116,30 +146,6 @@ struct AttnArgs {
   int32_t keys_per_split;   // multiple of the key chunk
   float* part_o;            // [n_split][R][H][512] when n_split > 1
   float* part_ml;           // [n_split][R][H][2]
-};
-
-// One new token per row: window ring, pending group or a completed entry
-// with its index key and block summary.
-struct AppendArgs {
-  int32_t n_rows;
-  int64_t n_seq;
-  const int32_t* row_seq;
-  const int64_t* pos;
-  int32_t m;
-  const uint16_t* x;
-  const uint16_t* gate;
-  uint16_t* pend_x;
-  uint16_t* pend_gate;
-  int64_t n_ent;
-  uint8_t* codes;
-  uint8_t* scales;
-  const uint16_t* key;
-  bool key_fp4;
-  uint8_t* keys;
-  uint8_t* key_scales;
-  uint8_t* block_keys;
-  uint8_t* swa;
-  int32_t swa_cap;
 };
 
 hipError_t launch_decode_append(const AppendArgs& a, hipStream_t stream);

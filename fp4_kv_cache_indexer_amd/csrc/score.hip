@@ -11,6 +11,7 @@
 //   wide as the top-k tie band; the fp16 MFMA matches a float32 FMA chain.)
 //   Each workgroup also histograms the top 12 bits of the order key of its
 //   scores in LDS and folds that into a per-row histogram for the top-k.
+#include "append_dev.h"
 #include "csa2_dev.h"
 #include "csa2_launch.h"
 #include "items.h"
@@ -74,6 +75,37 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
   return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// The append of one row inside the coarse scan's launch (its last column),
+// for the (m, gate) forms a decode step uses.
+__device__ __forceinline__ void fused_append_row(const AppendArgs& ap, int r, int t) {
+  if (ap.m == 1) {
+    if (ap.key_fp4) decode_append_row<1, false, 1>(ap, r, t); else decode_append_row<1, false, 0>(ap, r, t);
+  } else if (ap.gate) {
+    if (ap.key_fp4) decode_append_row<2, true, 1>(ap, r, t); else decode_append_row<2, true, 0>(ap, r, t);
+  } else {
+    if (ap.key_fp4) decode_append_row<2, false, 1>(ap, r, t); else decode_append_row<2, false, 0>(ap, r, t);
+  }
+}
+
+// The refreshed summary of the block of entry e (sequence s) by lanes 0..31
+// of wave 0, 4 channels each, into sp_key (bytes 4t..4t+3).
+__device__ __forceinline__ void fused_block_summary(const AppendArgs& ap, int r, int64_t s, int64_t e,
+                                                    uint8_t* sp_key) {
+  const int t = threadIdx.x;
+  if (t >= 32) return;
+  uint32_t old_w[kBlockPos - 1], old_s[kBlockPos - 1];
+  const int cnt = (int)(e - (e / kBlockPos) * kBlockPos) + 1;
+  uint32_t out;
+  if (ap.key_fp4) {
+    append_members4<1>(ap, s, e, t, old_w, old_s);
+    out = append_summary4<1>(old_w, old_s, cnt, append_key4<1>(ap.key + (int64_t)r * kIdxDim, t));
+  } else {
+    append_members4<0>(ap, s, e, t, old_w, old_s);
+    out = append_summary4<0>(old_w, old_s, cnt, append_key4<0>(ap.key + (int64_t)r * kIdxDim, t));
+  }
+  *reinterpret_cast<uint32_t*>(sp_key + 4 * t) = out;
+}
+
 // DB: double-buffer the tile groups of a wave; MINW: waves per SIMD the
 // register budget must allow.
 // G > 0: the chunk is exactly G groups per wave and the group loop is fully
@@ -81,18 +113,36 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
 // in flight exactly); G == 0: runtime trip count.
 // KF: key format, 0 = E4M3 (128 B per key), 1 = FP4 (64 B of codes + a
 // 4-byte word of E4M3 scales, one per 32 channels).
-template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0>
+// APP: the coarse stage of a decode step, which also runs the step's append
+// (see ScoreArgs::fuse_append).
+template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0, bool APP = false>
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
   __shared__ uint32_t hist[kHistBins];
   __shared__ float sscore[kScoreStage];
+  __shared__ __align__(16) uint8_t sp_key[APP ? kIdxDim : 16];
   const int r = blockIdx.y;
+  if (APP && blockIdx.x == gridDim.x - 1) {      // uniform: the row's append
+    fused_append_row(a.app, r, threadIdx.x);
+    return;
+  }
   const int64_t nv = row_valid(a.im, r);
   const int64_t n_row = row_items(a.im, nv);
   const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
   if (c0 >= n_row) return;                       // uniform for the workgroup
   const int64_t c1 = min(c0 + (int64_t)a.chunk, n_row);
   const bool stage = c1 - c0 <= kScoreStage;     // uniform
+  // the block whose summary the row's append refreshes, when this chunk
+  // holds it: scored from its new summary, recomputed here
+  int64_t sp = -1;
+  if (APP && a.app.block_keys) {
+    int64_t aseq;
+    const int64_t e = append_entry(a.app, r, aseq);
+    if (e >= 0 && e / kBlockPos >= c0 && e / kBlockPos < c1) {
+      sp = e / kBlockPos;
+      fused_block_summary(a.app, r, aseq, e, sp_key);   // ordered before the scoring by the barrier below
+    }
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -144,7 +194,17 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       }
     }
   };
-  auto compute_group = [&](int64_t t0, const v8i* kb) {
+  auto compute_group = [&](int64_t t0, v8i* kb) {
+    if (APP && sp >= 0) {                        // uniform: the refreshed block's key from LDS
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + (t0 + u) * 16 + n == sp) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(sp_key + 32 * g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(sp_key + 32 * g + 16);
+          kb[u] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      }
+    }
 #pragma unroll
     for (int u4 = 0; u4 < U; u4 += 4) {
       float p[4];
@@ -444,7 +504,7 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int64_t chunks = ((int64_t)a.im.n_items + a.chunk - 1) / a.chunk;
-  const dim3 grid((unsigned)chunks, (unsigned)a.n_rows), block(kScoreThreads);
+  const dim3 grid((unsigned)(chunks + (a.fuse_append ? 1 : 0)), (unsigned)a.n_rows), block(kScoreThreads);
   // a chunk of exactly one group per wave (the 16384-position pool, short
   // rows) runs the straight-line form: no second, discarded group
   const bool one = a.chunk == kScoreWaves * kTilesPerIter * 16;
@@ -456,7 +516,14 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
     else                                                                                                \
       hipLaunchKernelGGL((index_score_kernel<MM, KK, kScoreDB, kScoreMinW>), grid, block, 0, stream, a);    \
   } while (0)
-  if (a.im.mode == kItemsBlocks) CSA2_SCORE(kItemsBlocks, 0);      // block summaries are E4M3
+  if (a.im.mode == kItemsBlocks && a.fuse_append) {                // the coarse stage of a decode step
+    if (one)
+      hipLaunchKernelGGL((index_score_kernel<kItemsBlocks, 0, kScoreDB, kScoreMinW, kTilesPerIter, 1, true>), grid,
+                         block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((index_score_kernel<kItemsBlocks, 0, kScoreDB, kScoreMinW, kTilesPerIter, 0, true>), grid,
+                         block, 0, stream, a);
+  } else if (a.im.mode == kItemsBlocks) CSA2_SCORE(kItemsBlocks, 0);      // block summaries are E4M3
   else if (a.key_fp4) {
     if (a.im.mode == kItemsFlat) CSA2_SCORE(kItemsFlat, 1);
     else if (a.im.mode == kItemsPool) CSA2_SCORE(kItemsPool, 1);

@@ -297,6 +297,26 @@ int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step's cache append and selection [0539edu §3: the candidate
+ * pool bounds the indexer's work; daiw "decode reads": decode is bound by
+ * the bytes each step reads]: exactly csa2_decode_append(app) followed by
+ * csa2_indexer_topk(idx) on the same stream, with the same validation,
+ * results and errors (nothing is enqueued when either is invalid), and the
+ * workspace of csa2_indexer_topk.  When the two describe the same rows of the
+ * same caches with row r being sequence r -- idx hierarchical, app->codes
+ * set, the same keys, key_scales, key format, block_keys, n_seq, n_ent and
+ * n_rows, both row_seq NULL, m 1 or 2 -- the append runs inside the coarse
+ * scan's launch (one extra workgroup per row), and the scan scores the block
+ * the new entry falls in from its refreshed summary, computed by the
+ * workgroup that owns it with the arithmetic of the append; the append then
+ * costs no step of its own.  Otherwise (e.g. rows mapped by row_seq, where
+ * one row may read a sequence another row appends to) the two run one after
+ * the other.
+ */
+int32_t csa2_append_indexer_topk(const csa2_append_args* app, const csa2_indexer_args* idx, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Indexer + top-k that allocates nothing and takes no workspace: for callers
  * that cannot call hipMalloc (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation).  Arguments, modes, results and

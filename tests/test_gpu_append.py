@@ -184,3 +184,91 @@ def test_window_append_many_rings():
         for slot in range(cap):
             last = max(p for p in range(T) if p % cap == slot)
             assert np.array_equal(got[r, slot], e4m3_of_bf16(x[r, last])), (r, slot)
+
+
+@pytest.mark.parametrize("m,gate,fp4", [(1, False, False), (1, False, True), (2, True, False), (2, True, True),
+                                        (2, False, False)])
+def test_append_indexer_fused_equals_sequential(m, gate, fp4):
+    """csa2_append_indexer_topk over one decode step (the append runs inside
+    the coarse scan's launch and the scan scores the refreshed block from a
+    summary it computes itself) leaves the same caches and gives the same
+    selection, bit for bit, as csa2_decode_append followed by
+    csa2_indexer_topk, from the same cache state.  Row r is sequence r; the
+    rows' tokens complete the last entry of a block, one inside a block, the
+    first of a new block, none (an open group at m = 2, or position -1) or
+    belong to no sequence (r >= n_seq).  A call with row_seq buffers (where
+    a row may read a sequence another row appends to) takes the sequential
+    form: its rows 1 and 4 share a sequence, row 4 appending nothing."""
+    say(f"append + indexer fused vs sequential: m={m} gate={gate} fp4={fp4}")
+    S, N, k, keep = 5, 2003, 96, 60
+    R = 6
+    g = np.random.default_rng(90 + m + 2 * fp4 + 4 * gate)
+    gt = torch.Generator(device="cuda")
+    gt.manual_seed(93 + m)
+    base = Caches(S, N, m, fp4, gate)
+    base.codes.copy_(torch.randint(0, 256, base.codes.shape, generator=gt, device="cuda", dtype=torch.uint8))
+    base.scales.copy_(synth.to_e4m3(torch.randn(base.scales.shape, generator=gt, device="cuda")))
+    kb = torch.randn((S, N, 128), generator=gt, device="cuda").to(torch.bfloat16)
+    if fp4:
+        C.index_key_quantize(kb, codes=base.keys, scales=base.kscales)
+        C.index_block_summary_fp4(base.keys, base.kscales, summ=base.summ)
+    else:
+        base.keys.copy_(synth.to_e4m3(kb.float()))
+        C.index_block_summary(base.keys, summ=base.summ)
+    base.swa.copy_(torch.randint(0, 120, base.swa.shape, generator=gt, device="cuda", dtype=torch.uint8))
+    base.pend_x.copy_(torch.randn(base.pend_x.shape, generator=gt, device="cuda").to(torch.bfloat16))
+    if base.pend_z is not None:
+        base.pend_z.copy_(torch.randn(base.pend_z.shape, generator=gt, device="cuda").to(torch.bfloat16))
+    ent = np.array([N - 1, 8 * 100 + 3, 8 * 150, 8 * 40 + 5, 0, 17])
+    pos = ent * m + (m - 1)
+    if m > 1:
+        pos[3] -= 1                                          # the first token of its group: nothing completes
+    pos[4] = -1
+    row_map = np.array([0, 1, 2, 3, 1, -1])                  # the row_seq form's mapping
+    torch.cuda.synchronize()
+    xt = synth.to_bf16_bits(g.standard_normal((R, 512)).astype(np.float32))
+    zt = synth.to_bf16_bits(g.standard_normal((R, 512)).astype(np.float32)) if gate else None
+    kt = synth.to_bf16_bits(g.standard_normal((R, 128)).astype(np.float32))
+    q = dev(synth.to_e4m3(g.standard_normal((R, 32, 128)).astype(np.float32)))
+    w = dev(g.uniform(0.25, 1.0, (R, 32)).astype(np.float32))
+    nv = dev(np.array([N, 8 * 100 + 4, 8 * 150 + 1, N, N, N], np.int32))
+
+    def clone(c):
+        d = Caches(S, N, m, fp4, gate)
+        for name in ("codes", "scales", "keys", "kscales", "summ", "swa", "pend_x", "pend_z"):
+            if getattr(c, name) is not None:
+                getattr(d, name).copy_(getattr(c, name))
+        return d
+
+    def run(form, row_seq):
+        c = clone(base)
+        rs = None if row_seq is None else dev(row_seq.astype(np.int32))
+        args = dict(m=m, gate=None if zt is None else dev(zt).view(torch.bfloat16),
+                    pend_x=c.pend_x if m > 1 else None, pend_gate=c.pend_z if (m > 1 and gate) else None,
+                    key_scales=c.kscales, swa=c.swa)
+        out_score = torch.zeros((R, k), dtype=torch.float32, device="cuda")
+        blocks = torch.zeros((R, keep), dtype=torch.int32, device="cuda")
+        xd, kd, pd = dev(xt).view(torch.bfloat16), dev(kt).view(torch.bfloat16), dev(pos.astype(np.int64))
+        if form == "sequential":
+            C.decode_append(xd, pd, c.codes, c.scales, kd, c.keys, row_seq=rs, block_keys=c.summ, **args)
+            idx = C.indexer_topk(q, c.keys, k, head_w=w, row_seq=rs, n_valid=nv, block_keys=c.summ,
+                                 keep_blocks=keep, out_score=out_score, out_blocks=blocks, key_scales=c.kscales)
+        else:
+            idx = C.append_indexer_topk(xd, pd, c.codes, c.scales, kd, q, c.keys, k, c.summ, row_seq=rs, head_w=w,
+                                        n_valid=nv, keep_blocks=keep, out_score=out_score, out_blocks=blocks,
+                                        **args)
+        torch.cuda.synchronize()
+        return (form, c, host(idx), host(out_score), host(blocks))
+
+    pairs = [(run("sequential", None), run("fused", None)),
+             (run("sequential", row_map), run("fused call with row_seq", row_map))]
+    for (_, ref_c, ref_i, ref_s, ref_b), (form, c, gi, gs, gb) in pairs:
+        for name in ("codes", "scales", "keys", "kscales", "summ", "swa", "pend_x", "pend_z"):
+            if getattr(c, name) is not None:
+                assert torch.equal(getattr(c, name), getattr(ref_c, name)), f"{form}: {name}"
+        assert np.array_equal(gi, ref_i), f"{form}: ids"
+        assert np.array_equal(gs.view(np.uint32), ref_s.view(np.uint32)), f"{form}: scores"
+        assert np.array_equal(gb, ref_b), f"{form}: kept blocks"
+        assert (ref_i[:4, 0] >= 0).all() and (ref_i[5] == -1).all()
+        # the step changed the caches: the appended rows' summaries moved
+        assert not torch.equal(ref_c.summ, base.summ)
