@@ -27,7 +27,6 @@ namespace csa2 {
 // ---------------------------------------------------------------------------
 
 constexpr int kFiltThreads = 256;
-constexpr int kFiltRound = kFiltThreads * 4;           // items per compaction round
 
 // Composite order key: score order first, then lower position first.
 __device__ __forceinline__ uint64_t comp_key(uint32_t okey, int64_t pos) {
@@ -150,60 +149,76 @@ __device__ __forceinline__ RowThreshold hist_threshold(const uint32_t (&hv)[kHis
   return RowThreshold{sh3[0], sh3[1], sh3[2], kk};
 }
 
-template <int NT>
-__device__ __forceinline__ RowThreshold row_threshold(const uint32_t* gh, int k, int* wsum, int* sh3) {
-  uint32_t hv[kHistBins / NT];
-  hist_load<NT>(gh, hv);
-  return hist_threshold<NT>(hv, k, wsum, sh3);
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts and row
+// broadcasts; lanes a shift does not reach add 0).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
 }
 
-// Filter.  Workgroup (chunk c, row r) finds b* and writes every item of its
-// chunk in b* or above -- a superset of the chunk's share of the top-k -- as
-// composite keys, compacted in item order, plus their count.
-__global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a) {
-  __shared__ int wsum[kFiltThreads / 64];
-  __shared__ int pair[3];
-  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = row_valid(a.im, r);
-  const int64_t n_row = row_items(a.im, nv);
-  const int64_t c0 = (int64_t)c * kFiltChunk;
-  if (c0 >= n_row) return;                                     // uniform
-  const int64_t c1 = min(c0 + (int64_t)kFiltChunk, n_row);
+// Exclusive prefix sum over the NT threads of a workgroup in thread order,
+// and the total; one barrier.  wsum[NT/64] must not be reused by another scan
+// before a further barrier.
+template <int NT>
+__device__ __forceinline__ int dpp_block_scan(int v, int* wsum, int& total) {
+  constexpr int kW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = x;
+  lds_barrier();
+  const int ws = lane < kW ? wsum[lane] : 0;
+  const int wi = wave_incl_scan(ws);
+  total = __builtin_amdgcn_readlane(wi, kW - 1);
+  const int before = wave > 0 ? __builtin_amdgcn_readlane(wi, wave - 1) : 0;
+  return before + x - v;
+}
 
-  // this thread's items, 4 consecutive per round, loaded before the scan
-  const float* srow = a.scores + (int64_t)r * a.row_stride;
-  constexpr int kRounds = kFiltChunk / kFiltRound;
-  float v[kRounds][4];
+// b* and the counts of a row's histogram, thread t holding the kB = 4096/NT
+// bins 4095 - kB*t - i (i < kB, descending): the bin of the kk-th largest
+// score, the items above it and in it; b* = -1 when every visible item is
+// kept.  Two barriers; thr[0..2] is read back by every thread.  (Returned as
+// RowThreshold{b*, above, in b*, kk}: its third field holds the count in b*.)
+template <int NT>
+__device__ __forceinline__ RowThreshold dpp_threshold(const uint32_t (&hv)[kHistBins / NT], int k, int* wsum,
+                                                      int* thr) {
+  constexpr int kB = kHistBins / NT;
+  int loc = 0;
 #pragma unroll
-  for (int rd = 0; rd < kRounds; ++rd) {
-    const float4 q = load_items4(srow, c0 + (int64_t)rd * kFiltRound + 4 * tid, c1, a.row_stride);
-    v[rd][0] = q.x; v[rd][1] = q.y; v[rd][2] = q.z; v[rd][3] = q.w;
+  for (int i = 0; i < kB; ++i) loc += (int)hv[i];
+  int total;
+  const int above = dpp_block_scan<NT>(loc, wsum, total);   // items in the bins above this thread's
+  const uint32_t kk = min((uint32_t)k, (uint32_t)total);
+  if (threadIdx.x == 0 && kk >= (uint32_t)total) { thr[0] = -1; thr[1] = 0; thr[2] = total; }
+  if (kk < (uint32_t)total && (uint32_t)above < kk && (uint32_t)(above + loc) >= kk) {
+    uint32_t cum = (uint32_t)above;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      if (cum < kk && cum + hv[i] >= kk) {
+        thr[0] = kHistBins - 1 - kB * (int)threadIdx.x - i; thr[1] = (int)cum; thr[2] = (int)hv[i];
+      }
+      cum += hv[i];
+    }
   }
-  const RowThreshold th = row_threshold<kFiltThreads>(a.hist + (int64_t)r * kHistBins, a.k, wsum, pair);
+  lds_barrier();
+  return RowThreshold{thr[0], thr[1], thr[2], kk};
+}
 
-  // compaction in item order
-  uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk;
-  int written = 0;
+// Loads the kB bins of thread t, descending (see dpp_threshold).
+template <int NT>
+__device__ __forceinline__ void hist_load_desc(const uint32_t* gh, uint32_t (&hv)[kHistBins / NT]) {
+  constexpr int kB = kHistBins / NT;
 #pragma unroll
-  for (int rd = 0; rd < kRounds; ++rd) {
-    const int64_t i0 = c0 + (int64_t)rd * kFiltRound + 4 * tid;
-    uint32_t ok[4];
-    int flag = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ok[j] = order_key(v[rd][j]);
-      const bool keep = (v[rd][j] == v[rd][j]) && (int)(ok[j] >> (32 - kHistBits)) >= th.bstar;
-      flag |= (int)keep << j;
-    }
-    int tot;
-    int slot = block_excl_scan<kFiltThreads>(__popc(flag), wsum, tot);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (flag & (1 << j)) crow[written + slot++] = comp_key(ok[j], item_pos(a.im, r, i0 + j, nv));
-    }
-    written += tot;
+  for (int q = 0; q < kB / 4; ++q) {
+    const uint4 h = *reinterpret_cast<const uint4*>(gh + kHistBins - kB * (threadIdx.x + 1) + 4 * (kB / 4 - 1 - q));
+    hv[4 * q] = h.w; hv[4 * q + 1] = h.z; hv[4 * q + 2] = h.y; hv[4 * q + 3] = h.x;
   }
-  if (tid == 0) a.cand_count[(int64_t)r * a.n_chunks + c] = (uint32_t)written;
 }
 
 // Smallest score whose composite key lies in bin b* or above, as a float:
@@ -218,6 +233,51 @@ __device__ __forceinline__ float bin_floor(int bstar) {
   const float f = order_key_inv(k0);
   return (f != f && k0 < 0x80000000u) ? -INFINITY : f;
 }
+
+// Filter.  Workgroup (chunk c, row r) finds b* and writes every item of its
+// chunk in b* or above -- a superset of the chunk's share of the top-k -- as
+// composite keys, compacted in item order, plus their count.  Thread t owns
+// the chunk's items 16t .. 16t+15, so one block scan places them all.
+constexpr int kFiltPer = kFiltChunk / kFiltThreads;           // items per thread
+static_assert(kFiltPer == 16, "16 items per filter thread");
+__global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a) {
+  __shared__ int wsum[2][kFiltThreads / 64];
+  __shared__ int thr[4];
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = row_valid(a.im, r);
+  const int64_t n_row = row_items(a.im, nv);
+  const int64_t c0 = (int64_t)c * kFiltChunk;
+  if (c0 >= n_row) return;                                     // uniform
+  const int64_t c1 = min(c0 + (int64_t)kFiltChunk, n_row);
+
+  // this thread's items and its bins, loaded before the threshold search
+  const float* srow = a.scores + (int64_t)r * a.row_stride;
+  const int64_t i0 = c0 + (int64_t)kFiltPer * tid;
+  float v[kFiltPer];
+#pragma unroll
+  for (int u = 0; u < kFiltPer / 4; ++u) {
+    const float4 q = load_items4(srow, i0 + 4 * u, c1, a.row_stride);
+    v[4 * u] = q.x; v[4 * u + 1] = q.y; v[4 * u + 2] = q.z; v[4 * u + 3] = q.w;
+  }
+  uint32_t hv[kHistBins / kFiltThreads];
+  hist_load_desc<kFiltThreads>(a.hist + (int64_t)r * kHistBins, hv);
+  const RowThreshold th = dpp_threshold<kFiltThreads>(hv, a.k, wsum[0], thr);
+
+  // compaction in item order
+  const float thf = bin_floor(th.bstar);
+  uint32_t flag = 0;
+#pragma unroll
+  for (int i = 0; i < kFiltPer; ++i) flag |= (uint32_t)(v[i] >= thf) << i;   // NaN (not visible) compares false
+  int tot;
+  int slot = dpp_block_scan<kFiltThreads>(__popc(flag), wsum[1], tot);
+  uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk;
+#pragma unroll
+  for (int i = 0; i < kFiltPer; ++i) {
+    if ((flag >> i) & 1u) crow[slot++] = comp_key(order_key(v[i]), item_pos(a.im, r, i0 + i, nv));
+  }
+  if (tid == 0) a.cand_count[(int64_t)r * a.n_chunks + c] = (uint32_t)tot;
+}
+
 
 // ---------------------------------------------------------------------------
 // Register-resident selection.  Every thread of a 1024-thread workgroup holds
@@ -239,61 +299,6 @@ struct __align__(16) RegShared {
   int thr[4];                       // b*, items above b*, items in b*
   int flag;
 };
-
-// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts and row
-// broadcasts; lanes a shift does not reach add 0).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-  return x;
-}
-
-// Exclusive prefix sum over the workgroup's threads in thread order, and the
-// total; one barrier.  wsum must not be reused by another scan before a
-// further barrier.
-__device__ __forceinline__ int reg_block_scan(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int x = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = x;
-  lds_barrier();
-  const int ws = lane < kRegWaves ? wsum[lane] : 0;
-  const int wi = wave_incl_scan(ws);
-  total = __builtin_amdgcn_readlane(wi, kRegWaves - 1);
-  const int before = wave > 0 ? __builtin_amdgcn_readlane(wi, wave - 1) : 0;
-  return before + x - v;
-}
-
-// b* and the counts of the row's histogram (thread t holds bins
-// 4095-4t .. 4092-4t, descending): the bin of the kk-th largest score, the
-// items above it and in it; b* = -1 when every visible item is kept.  Two
-// barriers; sh.thr is read back by every thread.
-// (Returned as RowThreshold{b*, above, in b*, kk}: its third field holds the
-// count in b* here, not the count in b* or above.)
-__device__ __forceinline__ RowThreshold reg_threshold(uint4 hq, int k, RegShared& sh) {
-  const uint32_t hv[4] = {hq.w, hq.z, hq.y, hq.x};           // descending bins
-  const int loc = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
-  int total;
-  const int above = reg_block_scan(loc, sh.wsum[0], total);  // items in the bins above this thread's
-  const uint32_t kk = min((uint32_t)k, (uint32_t)total);
-  if (threadIdx.x == 0 && kk >= (uint32_t)total) { sh.thr[0] = -1; sh.thr[1] = 0; sh.thr[2] = total; }
-  if (kk < (uint32_t)total && (uint32_t)above < kk && (uint32_t)(above + loc) >= kk) {
-    uint32_t cum = (uint32_t)above;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (cum < kk && cum + hv[i] >= kk) {
-        sh.thr[0] = kHistBins - 1 - 4 * (int)threadIdx.x - i; sh.thr[1] = (int)cum; sh.thr[2] = (int)hv[i];
-      }
-      cum += hv[i];
-    }
-  }
-  lds_barrier();
-  return RowThreshold{sh.thr[0], sh.thr[1], sh.thr[2], kk};
-}
 
 // The k-th composite key among the candidates: b* fixes its top 12 bits,
 // radix steps over the keys of bin b* the rest.  need = kk - items above b*,
@@ -353,7 +358,7 @@ __device__ __forceinline__ int reg_emit_at(const uint64_t (&K)[NK], uint64_t T, 
 #pragma unroll
   for (int i = 0; i < NK; ++i) cnt += (kk > 0 && K[i] != 0 && K[i] >= T) ? 1 : 0;
   int total;
-  int slot = base + reg_block_scan(cnt, sh.wsum[1], total);
+  int slot = base + dpp_block_scan<kRegThreads>(cnt, sh.wsum[1], total);
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     if (kk > 0 && K[i] != 0 && K[i] >= T) {
@@ -399,7 +404,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
     return;
   }
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  const uint4 hq = *reinterpret_cast<const uint4*>(gh + kHistBins - 4 - 4 * tid);
+  uint32_t hv[kHistBins / kRegThreads];
+  hist_load_desc<kRegThreads>(gh, hv);
   const float* srow = a.scores + (int64_t)r * a.row_stride;
   const int i0 = kRegRowNK * tid;
   float4 v[4];
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
     blk[1] = lrow[min(2 * tid + 1, a.im.list_len - 1)];
   }
   if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
-  const RowThreshold th = reg_threshold(hq, a.k, sh);        // its barriers order the zeroing too
+  const RowThreshold th = dpp_threshold<kRegThreads>(hv, a.k, sh.wsum[0], sh.thr);   // its barriers order the zeroing too
   const float thr = bin_floor(th.bstar);
   uint64_t K[kRegRowNK];
 #pragma unroll
@@ -490,7 +496,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
   const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
   const int tpc = min(kFiltChunk / kSelNK, kSelThreads / nch);  // 0 when there are more chunks than threads
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
-  const uint4 hq = *reinterpret_cast<const uint4*>(gh + kHistBins - 4 - 4 * tid);
+  uint32_t hv[kHistBins / kSelThreads];
+  hist_load_desc<kSelThreads>(gh, hv);
   const int c = tpc > 0 ? min(tid / tpc, nch - 1) : 0;           // threads past the chunks repeat the last
   const int s0 = tpc > 0 ? kSelNK * (tid % tpc) : 0;
   const int cnt = (int)a.cand_count[(int64_t)r * a.n_chunks + c];
@@ -506,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
   if (tid == 0) sh.flag = tpc > 0 ? 0 : 1;
   lds_barrier();
   if (tpc > 0 && tid % tpc == 0 && tid < nch * tpc && cnt > kSelNK * tpc) sh.flag = 1;
-  const RowThreshold th = reg_threshold(hq, a.k, sh);        // its barriers publish the flag
+  const RowThreshold th = dpp_threshold<kSelThreads>(hv, a.k, sh.wsum[0], sh.thr);   // its barriers publish the flag
   const bool spill = sh.flag != 0;                             // uniform: a chunk overflows its slots
   int32_t* sel_pos = sort ? shs.pos : oi;
   float* sel_score = sort ? shs.score : os;
