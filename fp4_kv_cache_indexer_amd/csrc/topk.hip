@@ -386,11 +386,69 @@ __device__ __forceinline__ int reg_emit(const uint64_t (&K)[NK], uint64_t T, uin
   return n;
 }
 
+// The k-th composite key among n composite keys in LDS (the candidates of a
+// row, bin b* or above), as reg_radix: thread t counts keys t, t + 1024, ...
+// of bin b*'s prefix per digit.  sh.h[0] and sh.h[1] must be zero on entry.
+__device__ __forceinline__ uint64_t lds_radix(const uint64_t* cand, int n, int bstar, int need, int in_bin,
+                                              RegShared& sh) {
+  if (bstar < 0) return 0;                                   // every candidate is kept
+  uint64_t prefix = (uint64_t)bstar;
+  if (need == in_bin) return prefix << 52;                   // the whole bin is kept
+  const int lane = threadIdx.x & 63;
+  for (int step = 0; step < 7; ++step) {
+    const int dshift = digit_shift(step), w = digit_width(step);
+    const uint32_t dmask = (1u << w) - 1u;
+    uint32_t* H = sh.h[step % 3];
+    for (int j = threadIdx.x; j < n; j += kRegThreads) {
+      const uint64_t K = cand[j];
+      if ((K >> (dshift + w)) == prefix) atomicAdd(&H[(K >> dshift) & dmask], 1u);
+    }
+    lds_barrier();
+    const uint4 hq = *reinterpret_cast<const uint4*>(&H[252 - 4 * lane]);
+    const uint32_t hv[4] = {hq.w, hq.z, hq.y, hq.x};
+    const int loc = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+    const int incl = wave_incl_scan(loc);
+    const int excl = incl - loc;
+    int digit = 0, above = 0, dcount = 0;
+    if (excl < need && incl >= need) {
+      int cum = excl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < need && cum + (int)hv[i] >= need) { digit = 255 - 4 * lane - i; above = cum; dcount = (int)hv[i]; }
+        cum += (int)hv[i];
+      }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(excl < need && incl >= need));
+    digit = __builtin_amdgcn_readlane(digit, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    dcount = __builtin_amdgcn_readlane(dcount, src);
+    if (threadIdx.x < 256) sh.h[(step + 2) % 3][threadIdx.x] = 0u;
+    need -= above;
+    prefix = (prefix << w) | (uint64_t)digit;
+    if (dcount == need || dshift == 0) return prefix << dshift;
+  }
+  return prefix;                                             // not reached
+}
+
 // Whole rows of at most kRegRowItems items (flat, block or pool mode): thread
-// t holds items 16t .. 16t+15.
+// t loads items 16t .. 16t+15.  When the row's candidates (its items in b*
+// or above, counted by the histogram) fit in LDS they are compacted there in
+// item order first -- each thread writing only its candidates' (score,
+// position) at the slots one block scan gives -- and the radix steps and the
+// output walk the candidates alone, a few per thread; otherwise every thread
+// keeps its 16 keys in registers (reg_radix, reg_emit).
 constexpr int kRegRowNK = 16;
+constexpr int kRowCompactCap = 12288;            // candidates compacted in LDS
+
+struct __align__(16) RegRowShared {
+  RegShared reg;
+  uint64_t cand[kRowCompactCap];                 // (score bits, position), then their composite keys
+};
+
 __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a) {
-  __shared__ RegShared sh;
+  extern __shared__ __align__(16) unsigned char reg_row_smem[];
+  RegRowShared& shr = *reinterpret_cast<RegRowShared*>(reg_row_smem);
+  RegShared& sh = shr.reg;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = row_valid(a.im, r);
   const int n_row = (int)row_items(a.im, nv);
@@ -423,21 +481,82 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
   if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
   const RowThreshold th = dpp_threshold<kRegThreads>(hv, a.k, sh.wsum[0], sh.thr);   // its barriers order the zeroing too
   const float thr = bin_floor(th.bstar);
-  uint64_t K[kRegRowNK];
+  const int n_cand = th.c_above + th.n_cand;                   // items in b* or above (every visible one if b* < 0)
+  const int need = (int)th.kk - th.c_above;
+  if (n_cand <= kRowCompactCap) {                              // uniform
+    // 1. the candidates' (score, position), compacted in item order
+    uint32_t mask = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    for (int u = 0; u < 4; ++u) {
+      const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int item = i0 + 4 * u + j;
-      const float x = x4[j];
-      const bool cand = item < n_row && x >= thr;              // NaN (not visible) compares false
-      const int32_t pos = a.im.mode == kItemsPool ? blk[(4 * u + j) >> 3] * kBlockPos + (item & 7) : item;
-      K[4 * u + j] = cand ? comp_key(order_key(x), pos) : 0ull;
+      for (int j = 0; j < 4; ++j) mask |= (uint32_t)(i0 + 4 * u + j < n_row && x4[j] >= thr) << (4 * u + j);
     }
+    int tot;
+    int slot = dpp_block_scan<kRegThreads>(__popc(mask), sh.wsum[1], tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int item = i0 + 4 * u + j;
+        const int32_t pos = a.im.mode == kItemsPool ? blk[(4 * u + j) >> 3] * kBlockPos + (item & 7) : item;
+        if ((mask >> (4 * u + j)) & 1u) {
+          shr.cand[slot] = ((uint64_t)(uint32_t)pos << 32) | __float_as_uint(x4[j]);
+          ++slot;
+        }
+      }
+    }
+    lds_barrier();
+    const int nc = min(tot, kRowCompactCap);                   // tot == n_cand: the histogram counted them
+    for (int j = tid; j < nc; j += kRegThreads) {
+      const uint64_t c = shr.cand[j];
+      shr.cand[j] = comp_key(order_key(__uint_as_float((uint32_t)c)), (int32_t)(c >> 32));
+    }
+    lds_barrier();
+    // 2. the k-th key among them
+    const uint64_t T = lds_radix(shr.cand, nc, th.bstar, need, th.n_cand, sh);
+    // 3. the kept ones (>= T), in candidate order: thread t a run of them
+    const int per = (nc + kRegThreads - 1) / kRegThreads;
+    const int j0 = tid * per, j1 = min(j0 + per, nc);
+    int cnt = 0;
+    if (th.kk > 0)
+      for (int j = j0; j < j1; ++j) cnt += shr.cand[j] >= T ? 1 : 0;
+    int nout;
+    int o = dpp_block_scan<kRegThreads>(cnt, sh.wsum[1], nout);
+    if (th.kk > 0) {
+      for (int j = j0; j < j1; ++j) {
+        const uint64_t K = shr.cand[j];
+        if (K >= T) {
+          if (o < a.k) {
+            oi[o] = comp_pos(K);
+            if (os) os[o] = comp_score(K);
+          }
+          ++o;
+        }
+      }
+    }
+    for (int j = min(nout, a.k) + tid; j < a.k; j += kRegThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.0f;
+    }
+  } else {
+    uint64_t K[kRegRowNK];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int item = i0 + 4 * u + j;
+        const float x = x4[j];
+        const bool cand = item < n_row && x >= thr;            // NaN (not visible) compares false
+        const int32_t pos = a.im.mode == kItemsPool ? blk[(4 * u + j) >> 3] * kBlockPos + (item & 7) : item;
+        K[4 * u + j] = cand ? comp_key(order_key(x), pos) : 0ull;
+      }
+    }
+    const uint64_t T = reg_radix(K, th.bstar, need, th.n_cand, sh);
+    reg_emit(K, T, th.kk, a.k, oi, os, sh);
   }
-  const uint64_t T = reg_radix(K, th.bstar, (int)th.kk - th.c_above, th.n_cand, sh);
-  reg_emit(K, T, th.kk, a.k, oi, os, sh);
   // leave the row's histogram zeroed for the next call
   *reinterpret_cast<uint4*>(gh + kHistBins - 4 - 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
 }
@@ -871,7 +990,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
 hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   if (a.im.n_items <= kRegThreads * kRegRowNK && a.im.mode != kItemsCand) {
-    hipLaunchKernelGGL(topk_reg_row_kernel, dim3((unsigned)a.n_rows), dim3(kRegThreads), 0, stream, a);
+    static const hipError_t rattr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_reg_row_kernel),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                        (int)sizeof(RegRowShared));
+    if (rattr != hipSuccess) return rattr;
+    hipLaunchKernelGGL(topk_reg_row_kernel, dim3((unsigned)a.n_rows), dim3(kRegThreads), sizeof(RegRowShared),
+                       stream, a);
     return hipGetLastError();
   }
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel),
