@@ -381,6 +381,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   if (a.heads_per_wg == 16) return launch_sparse_attn_narrow(a, stream);
+  if (a.n_heads >= 32) return launch_sparse_attn_tile(a, stream);
   // every workgroup holds min(64, H) heads (H is 16, 32, 64 or 128)
   const int hg = min(kHeadsPerWG, a.n_heads) / 16;
   auto kern = hg == 4 ? &sparse_attn_kernel<4> : hg == 2 ? &sparse_attn_kernel<2> : &sparse_attn_kernel<1>;
