@@ -8,7 +8,7 @@
 // through a four-stage pipeline, one barrier per step; chunk c is
 //   * written at step c by 2 dequantising waves, which gather the selected
 //     FP4 entries (256 code + 32 E4M3 scale bytes each) or FP8 window tokens
-//     three chunks ahead and write them exactly, as fp16, into one key-major
+//     four chunks ahead and write them exactly, as fp16, into one key-major
 //     tile (4 tiles in rotation);
 //   * multiplied at step c + 1 by 2 score waves, one per 32-head tile:
 //     S^T[key][head] = K Q^T (v_mfma_f32_32x32x16_f16, Q held in registers);
@@ -411,13 +411,24 @@ __global__ __launch_bounds__(kTThreads, 2) void sparse_attn_tile_kernel(AttnArgs
   const int64_t rh0 = (int64_t)r * H + hbase;
   if (qk_wave) {
     // score waves: Q of head tile `wave` (head 32*wave + l32), channels
-    // 16ks + 8*h32 .. +8 for ks < 32, scaled by a power of two into fp16
+    // 16ks + 8*h32 .. +8 for ks < 32, scaled by a power of two into fp16.
+    // The tile's 32 rows (32 KB, contiguous) come in with one 1 KB row per
+    // load and pass through key tile 2 + wave (first written at step 2):
+    // row t's 16-byte block l at block l ^ tsw(t).
     {
       const int hq = hbase + 32 * wave + l32;
       const bool hok = hq < H;
-      const uint16_t* qrow = a.q + ((int64_t)r * H + (hok ? hq : 0)) * kD + 8 * h32;
+      const int nrow = min(32, H - (hbase + 32 * wave));
+      const uint16_t* qsrc = a.q + ((int64_t)r * H + hbase + 32 * wave) * kD + 8 * lane;
+      uint8_t* qs = sh.k[2 + wave];
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qrow + 16 * ks);
+      for (int t = 0; t < 32; ++t)
+        qreg[t] = t < nrow ? *reinterpret_cast<const uint4*>(qsrc + t * kD) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 32; ++t) *reinterpret_cast<uint4*>(qs + t * kTRow + 16 * (lane ^ tsw(t))) = qreg[t];
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks)
+        qreg[ks] = *reinterpret_cast<const uint4*>(qs + l32 * kTRow + 16 * ((2 * ks + h32) ^ tsw(l32)));
       // the largest magnitude from the bits (finite bf16: the order of the
       // magnitude bits is the order of the magnitudes)
       uint32_t mbits = 0u;
@@ -517,30 +528,32 @@ __global__ __launch_bounds__(kTThreads, 2) void sparse_attn_tile_kernel(AttnArgs
       }
     }
   } else {
-    // dequantising waves: chunk i is gathered three steps ahead into set
-    // i % 3 and written into tile i % 4 at step i.  The loop is unrolled by
-    // three so that the sets stay in registers; it leaves by a break after
-    // any step, so every path back to its head has issued the three sets in
-    // order.
-    TGather G0, G1, G2;
+    // dequantising waves: chunk i is gathered four steps ahead into set
+    // i % 4 and written into tile i % 4 at step i.  The loop is unrolled by
+    // four so that the sets stay in registers; it leaves by a break after any
+    // step, so every path back to its head has issued the four sets in order.
+    TGather G0, G1, G2, G3;
     if (nsteps > 0) {
       gather(0, G0);
       gather(1, G1);
       gather(2, G2);
+      gather(3, G3);
     }
-    auto step = [&](int i, TGather& G) __attribute__((always_inline)) {
-      if (i < nch) dequant(G, i & (kTTiles - 1));
-      gather(i + 3, G);
+    auto step = [&](int i, TGather& G, int buf) __attribute__((always_inline)) {
+      if (i < nch) dequant(G, buf);
+      gather(i + 4, G);
       lds_barrier();
     };
 #pragma unroll 1
-    for (int i = 0;; i += 3) {
+    for (int i = 0;; i += 4) {
       if (i >= nsteps) break;
-      step(i, G0);
+      step(i, G0, 0);
       if (i + 1 >= nsteps) break;
-      step(i + 1, G1);
+      step(i + 1, G1, 1);
       if (i + 2 >= nsteps) break;
-      step(i + 2, G2);
+      step(i + 2, G2, 2);
+      if (i + 3 >= nsteps) break;
+      step(i + 3, G3, 3);
     }
     lds_barrier();
     __builtin_amdgcn_s_waitcnt(0);             // the trailing (dummy) gathers retired
