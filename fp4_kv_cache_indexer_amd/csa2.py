@@ -12,7 +12,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+# CSA2_LIBRARY may name another build of the same library (e.g. one whose
+# host code carries AddressSanitizer)
+_LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 _lib = None
 
 LATENT_DIM = 512
@@ -104,7 +106,7 @@ EXPORTS = (
     "csa2_kv_compress_quantize", "csa2_index_block_summary",
     "csa2_index_key_quantize", "csa2_index_block_summary_fp4", "csa2_decode_append",
     "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static", "csa2_append_indexer_topk",
-    "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode",
+    "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode", "csa2_attn_plan_override",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
 )
 
@@ -149,6 +151,8 @@ def lib():
     L.csa2_indexer_topk_static.argtypes = [ctypes.POINTER(IndexerArgs), vp]
     L.csa2_sparse_attn_workspace.restype = sz
     L.csa2_sparse_attn_workspace.argtypes = [ctypes.POINTER(AttnArgs)]
+    L.csa2_attn_plan_override.restype = i32
+    L.csa2_attn_plan_override.argtypes = [i32, i32]
     L.csa2_sparse_attn_decode.restype = i32
     L.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
     L.csa2_kernel_timer_start.restype = i32
@@ -459,6 +463,12 @@ def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_sca
     a.lse = _ptr(lse)
     a.swa_max = int(swa_max)
     return a
+
+
+def attn_plan_override(heads_per_wg=0, n_split=0):
+    """Pin the attention geometry (16 or 64 heads per workgroup, key splits per
+    row) for later calls; (0, 0) restores the automatic plan."""
+    _check(lib().csa2_attn_plan_override(int(heads_per_wg), int(n_split)))
 
 
 def sparse_attn_workspace(q, idx, swa=None, swa_len=None, codes=None, swa_max=0):

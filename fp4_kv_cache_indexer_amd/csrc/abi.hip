@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -182,6 +183,10 @@ struct AttnPlan {
   size_t off_o, off_ml, total;
 };
 
+// Plan override for tests and benchmarks (csa2_attn_plan_override): heads per
+// workgroup and key splits, 0 = chosen per call.
+std::atomic<int32_t> g_attn_hpw{0}, g_attn_split{0};
+
 int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   if (!a) return fail(CSA2_EINVAL, "attn: args is NULL");
   if (a->n_rows < 0) return fail(CSA2_EINVAL, "attn: n_rows < 0");
@@ -216,12 +221,17 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   const int64_t wg16 = (int64_t)a->n_rows * ((a->n_heads + 15) / 16);
   const int64_t ns16 = wg16 > 0 ? std::min(max_split, (int64_t)CSA2_RESIDENT_ATTN_WGS / wg16) : 0;
   p->heads_per_wg = (ns16 >= 1 && (nk + ns16 - 1) / ns16 <= CSA2_NARROW_MAX_SPLIT_KEYS) ? 16 : 64;
+  const int32_t hpw_forced = g_attn_hpw.load(std::memory_order_relaxed);
+  if (hpw_forced) p->heads_per_wg = hpw_forced;
   const int64_t hg = (a->n_heads + p->heads_per_wg - 1) / p->heads_per_wg;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
-  if (p->heads_per_wg == 16) ns = ns16;             // as many splits as run at once
+  if (p->heads_per_wg == 16) ns = std::max<int64_t>(ns16, 1);   // as many splits as run at once
   if (ns > max_split) ns = max_split;
-  const int64_t min_split = (nk + 1023) / 1024;    // at most 1024 selected ids staged per split
+  const int32_t split_forced = g_attn_split.load(std::memory_order_relaxed);
+  if (split_forced) ns = split_forced;
+  // at most 1024 selected ids staged per split, 512 keys per narrow workgroup
+  const int64_t min_split = p->heads_per_wg == 16 ? (nk + 511) / 512 : (nk + 1023) / 1024;
   if (ns < min_split) ns = min_split;
   if (ns < 1) ns = 1;
   int64_t kps = (nk + ns - 1) / ns;
@@ -635,6 +645,16 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
 }  // namespace
 
 extern "C" {
+
+int32_t csa2_attn_plan_override(int32_t heads_per_wg, int32_t n_split) {
+  g_err.clear();
+  if (heads_per_wg != 0 && heads_per_wg != 16 && heads_per_wg != 64)
+    return fail(CSA2_EINVAL, "attn plan: heads_per_wg %d not 0, 16 or 64", heads_per_wg);
+  if (n_split < 0 || n_split > 64) return fail(CSA2_EINVAL, "attn plan: n_split %d outside [0, 64]", n_split);
+  g_attn_hpw.store(heads_per_wg, std::memory_order_relaxed);
+  g_attn_split.store(n_split, std::memory_order_relaxed);
+  return CSA2_OK;
+}
 
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* a) {
   AttnPlan p;

@@ -383,6 +383,19 @@ typedef struct {
                                longer windows are clamped to it                 */
 } csa2_attn_args;
 
+/*
+ * Attention plan override, for tests and benchmarks that pin the geometry of
+ * the attention kernels (every geometry computes the same function to the
+ * precision stated above).  heads_per_wg: 16 (one 16-head group per
+ * workgroup) or 64 (up to 64 heads per workgroup), 0 = chosen per call;
+ * n_split: key splits per row, 1..64, 0 = chosen per call, raised to the
+ * least count the chosen kernel supports (512 keys per split with 16 heads,
+ * 1024 with 64).  Process-wide, for calls of csa2_sparse_attn_workspace and
+ * csa2_sparse_attn_decode made after it; (0, 0) restores the automatic plan.
+ * Returns CSA2_EINVAL for other values and changes nothing then.
+ */
+int32_t csa2_attn_plan_override(int32_t heads_per_wg, int32_t n_split);
+
 /* Workspace bytes csa2_sparse_attn_decode needs (0 on error or if none).
  * Reads only the sizes and whether swa_len is set. */
 size_t csa2_sparse_attn_workspace(const csa2_attn_args* args);

@@ -195,3 +195,23 @@ def test_decode_append_validation_without_gpu():
     assert L.csa2_decode_append(ctypes.byref(args(n_rows=0, pos=None)), None) == 0   # nothing to do
     w = args(codes=None, swa=ctypes.c_void_p(0x2002), swa_cap=128)
     assert L.csa2_decode_append(ctypes.byref(w), None) == 1                          # swa misaligned
+
+
+def test_attn_plan_override_without_gpu():
+    """The plan override takes 0/16/64 heads per workgroup and 0..64 splits,
+    refuses anything else, and changes the workspace the plan asks for."""
+    L = C.lib()
+    for hpw, ns in ((32, 0), (0, 65), (-16, 1), (16, -1)):
+        assert L.csa2_attn_plan_override(hpw, ns) == 1, (hpw, ns)          # CSA2_EINVAL
+    a = C.AttnArgs()
+    a.n_rows, a.n_heads, a.n_seq, a.top_k, a.n_ent = 4, 64, 4, 512, 8192
+    try:
+        assert L.csa2_attn_plan_override(64, 1) == 0
+        assert L.csa2_sparse_attn_workspace(ctypes.byref(a)) == 0        # one split: no partials
+        assert L.csa2_attn_plan_override(64, 4) == 0
+        ws4 = L.csa2_sparse_attn_workspace(ctypes.byref(a))
+        assert ws4 >= 4 * 4 * 64 * 512 * 4                              # 4 splits of [R][H][512] float32
+        assert L.csa2_attn_plan_override(16, 1) == 0                   # raised to the narrow kernel's least
+        assert L.csa2_sparse_attn_workspace(ctypes.byref(a)) == 0       # 512 keys: one split still fits
+    finally:
+        assert L.csa2_attn_plan_override(0, 0) == 0
