@@ -45,6 +45,23 @@ constexpr int kScoreStage = 2048;
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
+// Non-temporal variants for keys that are streamed once: the summary scan
+// and the pool scan of the hierarchical indexer read faster with them; the
+// flat scan over many sequences reads slower, and keeps the plain loads.
+typedef unsigned int u4nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const uint8_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u4nt*>(p)));
+}
+template <bool NT>
+__device__ __forceinline__ v8i load32k(const uint8_t* p) {
+  const uint4 a = NT ? load16_nt(p) : *reinterpret_cast<const uint4*>(p);
+  const uint4 b = NT ? load16_nt(p + 16) : *reinterpret_cast<const uint4*>(p + 16);
+  v8i v;
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  return v;
+}
+
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4 a = *reinterpret_cast<const uint4*>(p);
   const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
@@ -186,11 +203,13 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
       const int64_t p = pos[u] >= 0 ? pos[u] : safe_pos;
       if (KF) {
-        const uint4 c = *reinterpret_cast<const uint4*>(kbase + p * kKeyBytes);
+        constexpr bool NT = MODE != 0;
+        const uint4 c = NT ? load16_nt(kbase + p * kKeyBytes) : *reinterpret_cast<const uint4*>(kbase + p * kKeyBytes);
         kb[u][0] = c.x; kb[u][1] = c.y; kb[u][2] = c.z; kb[u][3] = c.w;
-        kb[u][4] = *reinterpret_cast<const uint32_t*>(sbase + p * 4);
+        kb[u][4] = NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + p * 4))
+                      : *reinterpret_cast<const uint32_t*>(sbase + p * 4);
       } else {
-        kb[u] = load32(kbase + p * kKeyBytes);
+        kb[u] = load32k<MODE != 0>(kbase + p * kKeyBytes);
       }
     }
   };
