@@ -63,12 +63,20 @@ struct Gather32 {
 __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char narrow_smem[];
   NarrowShared& sh = *reinterpret_cast<NarrowShared*>(narrow_smem);
-  const int split = blockIdx.x, r = blockIdx.y;
+  // Workgroups go to the 8 XCDs in turn by linear id; work item t is taken
+  // by workgroup (t mod B) * 8 + t / B, so that XCD x holds the contiguous
+  // items [xB, xB + B), head group fastest: the head groups of one (row,
+  // split), which gather the same keys, share one L2.
+  const int H = a.n_heads;
+  const int nhg = H / kHeads;
+  const int t = (int)(blockIdx.x & 7u) * a.xcd_block + (int)(blockIdx.x >> 3);
+  if (t >= a.n_split * a.n_rows * nhg) return;   // padding of the last blocks
+  const int hg = t % nhg, sr = t / nhg;
+  const int split = sr % a.n_split, r = sr / a.n_split;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int H = a.n_heads;
-  const int hbase = blockIdx.z * kHeads;
+  const int hbase = hg * kHeads;
 
   const int64_t seq = a.row_seq ? a.row_seq[r] : r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
@@ -313,9 +321,15 @@ hipError_t launch_sparse_attn_narrow(const AttnArgs& a, hipStream_t stream) {
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)sizeof(NarrowShared));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(sparse_attn_narrow_kernel, dim3((unsigned)a.n_split, (unsigned)a.n_rows,
-                                                     (unsigned)(a.n_heads / kHeads)),
-                     dim3(kThreads), sizeof(NarrowShared), stream, a);
+  // the XCD-major order of the work items (see the kernel): blocks of B
+  // items, B a multiple of the head groups
+  const int nhg = a.n_heads / kHeads;
+  const int64_t total = (int64_t)a.n_split * a.n_rows * nhg;
+  if (total > (int64_t)1 << 30) return hipErrorInvalidValue;
+  AttnArgs k = a;
+  k.xcd_block = (int32_t)(((total + 7) / 8 + nhg - 1) / nhg * nhg);
+  hipLaunchKernelGGL(sparse_attn_narrow_kernel, dim3((unsigned)(8 * k.xcd_block)), dim3(kThreads),
+                     sizeof(NarrowShared), stream, k);
   return hipGetLastError();
 }
 

@@ -146,6 +146,7 @@ struct AttnArgs {
   int32_t keys_per_split;   // multiple of the key chunk
   float* part_o;            // [n_split][R][H][512] when n_split > 1
   float* part_ml;           // [n_split][R][H][2]
+  int32_t xcd_block;        // set by the launcher of the 16-head kernel: work items per XCD
 };
 
 hipError_t launch_decode_append(const AppendArgs& a, hipStream_t stream);
