@@ -790,6 +790,8 @@ def main():
     ap.add_argument("--sites", action="store_true",
                     help="also print the event-timed average duration of every launch site")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--attn-plan", metavar="HPW,NS", default=None,
+                    help="pin the attention geometry: heads per workgroup (16 or 64) and key splits")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a copy kernel of this size (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--sweep", action="store_true",
@@ -806,6 +808,10 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     C.lib()
+    if args.attn_plan:
+        hpw, ns = (int(v) for v in args.attn_plan.split(","))
+        C.attn_plan_override(hpw, ns)
+        print(f"[bench] attention plan pinned: {hpw} heads per workgroup, {ns} key splits", file=sys.stderr)
     if args.workload == "c5":
         run_prefill(args)
         return

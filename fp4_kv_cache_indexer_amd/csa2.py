@@ -107,7 +107,7 @@ EXPORTS = (
     "csa2_index_key_quantize", "csa2_index_block_summary_fp4", "csa2_decode_append",
     "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static", "csa2_append_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode", "csa2_attn_plan_override",
-    "csa2_kernel_timer_start", "csa2_kernel_timer_stop",
+    "csa2_kernel_timer_start", "csa2_kernel_timer_stop", "csa2_mfma_dot_probe",
 )
 
 KEY_E4M3, KEY_FP4 = 0, 1          # index-key formats (CSA2_KEY_*)
@@ -153,6 +153,8 @@ def lib():
     L.csa2_sparse_attn_workspace.argtypes = [ctypes.POINTER(AttnArgs)]
     L.csa2_attn_plan_override.restype = i32
     L.csa2_attn_plan_override.argtypes = [i32, i32]
+    L.csa2_mfma_dot_probe.restype = i32
+    L.csa2_mfma_dot_probe.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.csa2_sparse_attn_decode.restype = i32
     L.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
     L.csa2_kernel_timer_start.restype = i32
@@ -463,6 +465,18 @@ def _attn_struct(q, codes, scales, idx, swa, swa_start, swa_len, row_seq, sm_sca
     a.lse = _ptr(lse)
     a.swa_max = int(swa_max)
     return a
+
+
+def mfma_dot_probe(q, k, stream=None):
+    """q uint8 [n_q, 128], k uint8 [n_k, 128] E4M3 (n_q, n_k multiples of 16):
+    the 128-term dot products through the fp16 and the fp8 matrix-core paths,
+    as float32 [n_q, n_k] each."""
+    _dev(q, "q"), _dev(k, "k")
+    nq, nk = q.shape[0], k.shape[0]
+    o16 = torch.empty((nq, nk), dtype=torch.float32, device=q.device)
+    o8 = torch.empty((nq, nk), dtype=torch.float32, device=q.device)
+    _check(lib().csa2_mfma_dot_probe(_ptr(q), _ptr(k), nq, nk, _ptr(o16), _ptr(o8), _stream(stream)))
+    return o16, o8
 
 
 def attn_plan_override(heads_per_wg=0, n_split=0):

@@ -230,8 +230,9 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   if (ns > max_split) ns = max_split;
   const int32_t split_forced = g_attn_split.load(std::memory_order_relaxed);
   if (split_forced) ns = split_forced;
-  // at most 1024 selected ids staged per split, 512 keys per narrow workgroup
-  const int64_t min_split = p->heads_per_wg == 16 ? (nk + 511) / 512 : (nk + 1023) / 1024;
+  // at most 512 selected ids staged per 16-head workgroup, 1024 keys per
+  // 64-head workgroup
+  const int64_t min_split = p->heads_per_wg == 16 ? (a->top_k + 511) / 512 : (nk + 1023) / 1024;
   if (ns < min_split) ns = min_split;
   if (ns < 1) ns = 1;
   int64_t kps = (nk + ns - 1) / ns;
@@ -701,6 +702,19 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* ws, size_t ws_byt
   if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   e = timed(CSA2_SITE_ATTN_COMBINE, s, [&] { return csa2::launch_attn_combine(k, s); });
   return e == hipSuccess ? CSA2_OK : hip_fail(e, "attn combine launch");
+}
+
+int32_t csa2_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int32_t n_k, float* out_f16,
+                            float* out_f8, void* stream) {
+  g_err.clear();
+  if (n_q <= 0 || n_k <= 0 || n_q % 16 || n_k % 16 || n_q > (1 << 20) || n_k > (1 << 20))
+    return fail(CSA2_EINVAL, "mfma probe: n_q %d, n_k %d not positive multiples of 16 up to 2^20", n_q, n_k);
+  if (!q || !k || !out_f16 || !out_f8) return fail(CSA2_EINVAL, "mfma probe: null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out_f16, 4) || !aligned(out_f8, 4))
+    return fail(CSA2_EINVAL, "mfma probe: misaligned pointer");
+  const hipError_t e = csa2::launch_mfma_dot_probe(q, k, n_q, n_k, out_f16, out_f8, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mfma probe");
+  return CSA2_OK;
 }
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {

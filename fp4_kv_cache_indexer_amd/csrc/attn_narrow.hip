@@ -23,6 +23,8 @@
 // PV operand the transpose read builds, so lane (n, g) of every wave reads
 // the 32 bytes lanes (n, g) of waves 0 and 1 wrote.  Split partials are
 // merged by attn_combine_kernel.
+#include <algorithm>
+
 #include "attn_dev.h"
 #include "csa2_launch.h"
 
@@ -36,7 +38,7 @@ constexpr int kHeads = 16;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTilesPerWave = (kD / 16) / kWaves;   // 4 output channel tiles per wave
-constexpr int kMaxSplitKeys = 512;             // keys of one workgroup at most
+constexpr int kMaxSplitKeys = 512;             // selected ids of one workgroup at most
 constexpr float kSlack = 8.0f;                 // log2 growth of the max tolerated before rescaling
 
 struct NarrowShared {
@@ -316,7 +318,8 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
 
 hipError_t launch_sparse_attn_narrow(const AttnArgs& a, hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
-  if (a.keys_per_split > kMaxSplitKeys || a.n_heads % kHeads) return hipErrorInvalidValue;
+  // a split stages at most kMaxSplitKeys selected ids (window keys need none)
+  if (std::min(a.keys_per_split, a.top_k) > kMaxSplitKeys || a.n_heads % kHeads) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_attn_narrow_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)sizeof(NarrowShared));

@@ -155,5 +155,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attn_narrow(const AttnArgs& a, hipStream_t stream);   // 16 heads per workgroup
 hipError_t launch_sparse_attn_tile(const AttnArgs& a, hipStream_t stream);     // 64 heads, 32x32 MFMA tiles
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int32_t n_k, float* out16,
+                                 float* out8, hipStream_t stream);
 
 }  // namespace csa2

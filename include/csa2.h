@@ -389,8 +389,8 @@ typedef struct {
  * precision stated above).  heads_per_wg: 16 (one 16-head group per
  * workgroup) or 64 (up to 64 heads per workgroup), 0 = chosen per call;
  * n_split: key splits per row, 1..64, 0 = chosen per call, raised to the
- * least count the chosen kernel supports (512 keys per split with 16 heads,
- * 1024 with 64).  Process-wide, for calls of csa2_sparse_attn_workspace and
+ * least count the chosen kernel supports (512 selected entries per split
+ * with 16 heads, 1024 keys with 64).  Process-wide, for calls of csa2_sparse_attn_workspace and
  * csa2_sparse_attn_decode made after it; (0, 0) restores the automatic plan.
  * Returns CSA2_EINVAL for other values and changes nothing then.
  */
@@ -430,6 +430,21 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace,
 
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches);
 int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);
+
+/*
+ * Matrix-core precision probe (diagnostics) [0539edu §3: the indexer's head
+ * scores are q . k over 128 dims with E4M3 operands and float32 accumulation].
+ * For every pair (i, j) of q [n_q][128] and k [n_k][128] (E4M3 bytes, device
+ * memory, 16-byte aligned) writes, on `stream`, the 128-term dot product
+ * computed two ways: out_f16[i][j] by widening to fp16 and summing with
+ * v_mfma_f32_16x16x32_f16 in four steps (the indexer's arithmetic), and
+ * out_f8[i][j] by one v_mfma_scale_f32_16x16x128_f8f6f4 on the E4M3 bytes
+ * with unit scales.  n_q and n_k: positive multiples of 16, at most 2^20.
+ * Outputs float32 [n_q][n_k], caller-owned.  Returns CSA2_EINVAL for other
+ * sizes or null/misaligned pointers, CSA2_EHIP if the launch fails.
+ */
+int32_t csa2_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int32_t n_k, float* out_f16,
+                            float* out_f8, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """Attention geometry invariance: the same rows through the 16-head (narrow)
-and 64-head (tile) kernels, each at two key-split counts, pinned with
+and 64-head (tile) kernels, each at two key-split counts (one split
+included), pinned with
 csa2_attn_plan_override.  Every geometry must meet the oracle's attention
 tolerance on the same inputs; the spread between geometries is printed.
 
@@ -19,7 +20,7 @@ from parity import check_close, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
-GEOMETRIES = [(16, 2), (16, 5), (64, 1), (64, 4)]
+GEOMETRIES = [(16, 1), (16, 5), (64, 1), (64, 4)]
 
 
 @pytest.fixture(scope="module", autouse=True)
