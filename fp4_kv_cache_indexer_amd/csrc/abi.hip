@@ -86,8 +86,20 @@ struct IndexerPlan {
   int32_t items0, items1;   // items a row walks in stage 0 / 1
   int32_t stride0, stride1; // score row strides (floats, multiple of 4)
   int32_t chunks;           // filter chunks per row (max over stages)
+  int64_t group_rows;       // rows per pass of a one-stage call (R if a single pass)
   size_t off_hist0, off_hist1, off_scores0, off_scores1, off_blocks, off_cand, off_count, total;
 };
+
+// Score rows of a one-stage call held at once: a call whose score block
+// would exceed this runs its rows in passes of at least kRowMinRows rows
+// (the row-group scan and the long-row select still apply to every pass).
+constexpr size_t kScoreBlockBudget = (size_t)512 << 20;
+
+// Whether a stage of `rows` rows over `items` items selects through the
+// candidate filter (and needs its candidate area).
+bool uses_filter(int64_t items, int64_t rows) {
+  return items > csa2::kRowMaxItems && rows < csa2::kRowMinRows;
+}
 
 int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptrs) {
   if (!a) return fail(CSA2_EINVAL, "indexer: args is NULL");
@@ -147,16 +159,30 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
   p->stride1 = (int32_t)round_up((size_t)p->items1, 4);
   const int64_t imax = p->items0 > p->items1 ? p->items0 : p->items1;
   p->chunks = (int32_t)((imax + csa2::kFiltChunk - 1) / csa2::kFiltChunk);
+  // rows per pass: every row at once unless a one-stage call's score block
+  // exceeds the budget; then passes of ceil(R / n) rows, n as small as keeps
+  // them within the budget but no pass below kRowMinRows rows
+  p->group_rows = p->R;
+  const size_t row_bytes = (size_t)p->stride0 * 4;
+  if (p->mode != 1 && p->R > 0 && (size_t)p->R * row_bytes > kScoreBlockBudget) {
+    const int64_t target = std::max<int64_t>(csa2::kRowMinRows, (int64_t)(kScoreBlockBudget / row_bytes));
+    int64_t passes = (p->R + target - 1) / target;
+    passes = std::min<int64_t>(passes, std::max<int64_t>(1, p->R / csa2::kRowMinRows));
+    p->group_rows = (p->R + passes - 1) / passes;
+  }
+  const int64_t G = p->group_rows;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
-  const size_t hist = (size_t)p->R * csa2::kHistBins * 4;
+  const size_t hist = (size_t)G * csa2::kHistBins * 4;
   p->off_hist0 = take(hist);
   p->off_hist1 = p->mode == 1 ? take(hist) : 0;
-  p->off_scores0 = take((size_t)p->R * p->stride0 * 4);
-  p->off_scores1 = p->mode == 1 ? take((size_t)p->R * p->stride1 * 4) : 0;
-  p->off_blocks = p->mode == 1 ? take((size_t)p->R * p->keep * 4) : 0;
-  p->off_cand = take((size_t)p->R * p->chunks * csa2::kFiltChunk * 8);
-  p->off_count = take((size_t)p->R * p->chunks * 4);
+  p->off_scores0 = take((size_t)G * p->stride0 * 4);
+  p->off_scores1 = p->mode == 1 ? take((size_t)G * p->stride1 * 4) : 0;
+  p->off_blocks = p->mode == 1 ? take((size_t)G * p->keep * 4) : 0;
+  // the candidate area only where a stage goes through the filter
+  const bool filt = uses_filter(p->items0, G) || (p->mode == 1 && uses_filter(p->items1, G));
+  p->off_cand = take(filt ? (size_t)G * p->chunks * csa2::kFiltChunk * 8 : 0);
+  p->off_count = take(filt ? (size_t)G * p->chunks * 4 : 0);
   p->total = off;
   return CSA2_OK;
 }
@@ -589,7 +615,7 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
     // extra workgroup per row (its slots are kept free)
     sa.fuse_append = (fused && im.mode == csa2::kItemsBlocks) ? 1 : 0;
     if (sa.fuse_append) sa.app = *fused;
-    sa.chunk = score_chunk(im.n_items, p.R, sa.fuse_append);
+    sa.chunk = score_chunk(im.n_items, sa.n_rows, sa.fuse_append);
     if ((e2 = timed(site, s, [&] { return csa2::launch_index_score(sa, s); })) != hipSuccess)
       return hip_fail(e2, "indexer score");
     se.im = im;
@@ -599,7 +625,7 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
     se.hist = hist;
     se.out_idx = out_idx;
     se.out_score = out_score;
-    if (im.n_items <= csa2::kRowMaxItems || p.R >= csa2::kRowMinRows) {
+    if (!uses_filter(im.n_items, se.n_rows)) {
       if ((e2 = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_row(se, s); })) != hipSuccess)
         return hip_fail(e2, "indexer top-k");
       return CSA2_OK;
@@ -611,19 +637,29 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
     return CSA2_OK;
   };
 
-  if (p.mode == 3) {
-    im0.mode = csa2::kItemsPool;
-    im0.list = a->cand_blocks;
-    im0.list_len = a->n_cand_blocks;
-    return stage(CSA2_SITE_SCORE_POOL, im0, a->keys, a->n_ent, p.stride0, scores0, hist0, a->top_k,
-                 a->out_idx, a->out_score);
-  }
-  if (p.mode == 0 || p.mode == 2) {
-    im0.mode = p.mode == 0 ? csa2::kItemsFlat : csa2::kItemsCand;
-    im0.list = a->cand;
-    im0.list_len = a->n_cand;
-    return stage(p.mode == 0 ? CSA2_SITE_SCORE_FLAT : CSA2_SITE_SCORE_CAND, im0, a->keys, a->n_ent,
-                 p.stride0, scores0, hist0, a->top_k, a->out_idx, a->out_score);
+  if (p.mode != 1) {
+    // one stage: flat, candidate list or candidate blocks, rows in passes of
+    // p.group_rows through one score block (stream-ordered: a pass's select
+    // has read the block before the next pass scores into it)
+    const int site = p.mode == 0 ? CSA2_SITE_SCORE_FLAT : p.mode == 2 ? CSA2_SITE_SCORE_CAND : CSA2_SITE_SCORE_POOL;
+    im0.mode = p.mode == 0 ? csa2::kItemsFlat : p.mode == 2 ? csa2::kItemsCand : csa2::kItemsPool;
+    const int32_t* list = p.mode == 2 ? a->cand : p.mode == 3 ? a->cand_blocks : nullptr;
+    im0.list_len = p.mode == 2 ? a->n_cand : p.mode == 3 ? a->n_cand_blocks : 0;
+    for (int64_t g0 = 0; g0 < p.R; g0 += p.group_rows) {
+      const int32_t rows = (int32_t)std::min<int64_t>(p.group_rows, p.R - g0);
+      csa2::ItemMap img = im0;
+      img.row_seq = a->row_seq ? a->row_seq + g0 : nullptr;
+      img.row_base = g0;
+      img.n_valid = a->n_valid ? a->n_valid + g0 : nullptr;
+      img.list = list ? list + g0 * im0.list_len : nullptr;
+      sa.n_rows = se.n_rows = rows;
+      sa.q = a->q + g0 * CSA2_IDX_HEADS * CSA2_IDX_DIM;
+      sa.w = a->head_w ? a->head_w + g0 * CSA2_IDX_HEADS : nullptr;
+      if ((st = stage(site, img, a->keys, a->n_ent, p.stride0, scores0, hist0, a->top_k, a->out_idx + g0 * a->top_k,
+                      a->out_score ? a->out_score + g0 * a->top_k : nullptr)) != CSA2_OK)
+        return st;
+    }
+    return CSA2_OK;
   }
 
   // hierarchical: coarse blocks -> kept blocks -> pool positions -> top-k

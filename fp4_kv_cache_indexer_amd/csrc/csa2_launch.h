@@ -34,7 +34,8 @@ enum ItemMode : int32_t {
 struct ItemMap {
   int32_t mode;
   int64_t n_seq;            // rows whose sequence is outside [0, n_seq) see nothing
-  const int32_t* row_seq;   // [R] or null
+  const int32_t* row_seq;   // [R] or null (row r reads sequence row_base + r)
+  int64_t row_base;         // first row of this launch among the call's rows
   int32_t n_items;          // item stride per row (scores row length)
   const int32_t* n_valid;   // [R] or null
   int64_t n_ent;            // default n_valid

@@ -14,7 +14,7 @@ namespace csa2 {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
-  return im.row_seq ? (int64_t)im.row_seq[r] : (int64_t)r;
+  return im.row_seq ? (int64_t)im.row_seq[r] : im.row_base + r;
 }
 
 // Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's

@@ -290,7 +290,15 @@ typedef struct {
  * with the same n_rows and the same mode (flat, hierarchical or candidate)
  * can reuse it without clearing it again, also from a captured HIP graph.
  * Zero it again before a call with another n_rows or mode, and after a call
- * that returned CSA2_EHIP or a device fault. */
+ * that returned CSA2_EHIP or a device fault.
+ *
+ * Size: score histograms and a float32 score block of one row per row, plus
+ * a candidate area where a stage selects through the candidate filter (rows
+ * over 32768 items in calls of fewer than 256 rows).  A one-stage call (flat,
+ * cand or cand_blocks) whose score block would exceed 512 MiB runs its rows in
+ * passes of equal size, at least 256 rows each, through one block of that
+ * many rows: e.g. 4096 rows over 524,288 entries take 16 passes of 256 rows
+ * and about 0.52 GB.  The passes give the results one pass of all rows gives. */
 size_t csa2_indexer_topk_workspace(const csa2_indexer_args* args);
 
 int32_t csa2_indexer_topk(const csa2_indexer_args* args, void* workspace,

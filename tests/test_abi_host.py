@@ -215,3 +215,25 @@ def test_attn_plan_override_without_gpu():
         assert L.csa2_sparse_attn_workspace(ctypes.byref(a)) == 0       # 512 keys: one split still fits
     finally:
         assert L.csa2_attn_plan_override(0, 0) == 0
+
+
+def test_indexer_workspace_passes_without_gpu():
+    """One-stage calls whose score block would pass 512 MiB plan passes of at
+    least 256 rows: 4096 rows over 524,288 entries fit in about 0.52 GB; small
+    calls keep one pass; the candidate area appears only with the filter."""
+    L = C.lib()
+
+    def ws(R, N, **kw):
+        a = C.IndexerArgs()
+        a.n_rows, a.n_seq, a.n_ent, a.top_k, a.key_format = R, 1, N, 512, 0
+        for name, v in kw.items():
+            setattr(a, name, v)
+        return L.csa2_indexer_topk_workspace(ctypes.byref(a))
+
+    big = ws(4096, 524288)
+    assert 256 * 524288 * 4 <= big < 1 << 30, big
+    assert ws(4097, 524288) < 1 << 30
+    assert ws(300, 6007) >= 300 * 6008 * 4                  # one pass
+    few = ws(8, 1 << 20)                                      # filter path: candidate area
+    assert few >= 8 * (1 << 20) * (4 + 8), few
+    assert ws(256, 1 << 20) < 256 * (1 << 20) * 8            # long-row select: no candidate area

@@ -162,6 +162,39 @@ def check_flat_rows(case, gi, gsc, top_k):
     return diffs
 
 
+def test_indexer_rows_in_passes():
+    """A one-stage call whose score block would pass 512 MiB runs its rows in
+    passes through one block: 600 rows over a 262,144-entry cache take two
+    passes of 300 rows; bit-equal to two calls of 300 rows (one pass each)
+    and to the oracle on sampled rows (ragged visible lengths, one empty row).
+    With row_seq NULL, the second pass's rows keep their own sequences (past
+    the one-sequence cache: nothing)."""
+    say("indexer flat, 600 rows over one 262144-entry cache, in two passes")
+    N, R, k = 262144, 600, 512
+    g = np.random.default_rng(31)
+    nv = g.integers(N // 2, N + 1, R)
+    nv[:3] = [N, 1, 0]
+    rs = np.zeros(R, np.int64)
+    case = idx_case(41, 1, N, R, row_seq=rs, n_valid=nv)
+    ws = C.indexer_topk_workspace(dev(case["q"]), dev(case["keys"]), k)
+    assert ws < (R // 2 + 8) * N * 4 + (64 << 20), f"workspace {ws} not sized for one pass of {R // 2} rows"
+    gi, gsc = run_indexer(case, k)
+    parts = []
+    for lo, hi in ((0, 300), (300, R)):
+        parts.append(run_indexer(dict(case, q=case["q"][lo:hi], w=case["w"][lo:hi], row_seq=rs[lo:hi],
+                                      n_valid=nv[lo:hi]), k))
+    assert np.array_equal(gi, np.concatenate([parts[0][0], parts[1][0]]))
+    assert np.array_equal(gsc.view(np.uint32), np.concatenate([parts[0][1], parts[1][1]]).view(np.uint32))
+    assert (gi[2] == -1).all() and gi[1][0] == 0 and (gi[1][1:] == -1).all()
+    sample = [0, 3, 299, 300, 599]
+    sub = dict(case, q=case["q"][sample], w=case["w"][sample], row_seq=rs[sample], n_valid=nv[sample])
+    check_flat_rows(sub, gi[sample], gsc[sample], k)
+    gi2, _ = run_indexer(dict(case, row_seq=None, n_valid=None), k)
+    one, _ = run_indexer(dict(case, q=case["q"][:1], w=case["w"][:1], row_seq=None, n_valid=None), k)
+    assert np.array_equal(gi2[0], one[0])
+    assert (gi2[1:] == -1).all()
+
+
 def test_indexer_flat_single_query_4096():
     say("indexer flat N=4096 R=1 k=512")
     case = idx_case(1, 1, 4096, 1, w=False)
