@@ -88,6 +88,7 @@ struct IndexerPlan {
   int32_t chunks;           // filter chunks per row (max over stages)
   int64_t group_rows;       // rows per pass of a one-stage call (R if a single pass)
   size_t off_hist0, off_hist1, off_scores0, off_scores1, off_blocks, off_cand, off_count, total;
+  bool has_cand;            // the candidate area exists (some stage filters)
 };
 
 // Score rows of a one-stage call held at once: a call whose score block
@@ -181,6 +182,7 @@ int32_t check_indexer(const csa2_indexer_args* a, IndexerPlan* p, bool check_ptr
   p->off_blocks = p->mode == 1 ? take((size_t)G * p->keep * 4) : 0;
   // the candidate area only where a stage goes through the filter
   const bool filt = uses_filter(p->items0, G) || (p->mode == 1 && uses_filter(p->items1, G));
+  p->has_cand = filt;
   p->off_cand = take(filt ? (size_t)G * p->chunks * csa2::kFiltChunk * 8 : 0);
   p->off_count = take(filt ? (size_t)G * p->chunks * 4 : 0);
   p->total = off;
@@ -592,8 +594,10 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
 
   csa2::SelectArgs se{};
   se.n_rows = a->n_rows;
-  se.cand = reinterpret_cast<uint64_t*>(w + p.off_cand);
-  se.cand_count = reinterpret_cast<uint32_t*>(w + p.off_count);
+  // no candidate area: the row select keeps its candidates in LDS, and a
+  // threshold bin too large for LDS is resolved from the stored scores
+  se.cand = p.has_cand ? reinterpret_cast<uint64_t*>(w + p.off_cand) : nullptr;
+  se.cand_count = p.has_cand ? reinterpret_cast<uint32_t*>(w + p.off_count) : nullptr;
   se.n_chunks = p.chunks;
 
   // histograms start at zero (the caller zeroes the workspace once) and the
@@ -625,7 +629,9 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
     se.hist = hist;
     se.out_idx = out_idx;
     se.out_score = out_score;
-    if (!uses_filter(im.n_items, se.n_rows)) {
+    // the plan's decision: a last pass of fewer rows than the plan sized the
+    // workspace for still selects per row when no candidate area exists
+    if (!(p.has_cand && uses_filter(im.n_items, se.n_rows))) {
       if ((e2 = timed(CSA2_SITE_SELECT, s, [&] { return csa2::launch_topk_row(se, s); })) != hipSuccess)
         return hip_fail(e2, "indexer top-k");
       return CSA2_OK;

@@ -100,8 +100,9 @@ struct SelectArgs {
   int32_t row_stride;       // floats between score rows (multiple of 4)
   const float* scores;      // [R][row_stride]
   uint32_t* hist;           // [R][kHistBins], zeroed after use
-  uint64_t* cand;           // [R][n_chunks][kFiltChunk] candidate composite keys
-  uint32_t* cand_count;     // [R][n_chunks]
+  uint64_t* cand;           // [R][n_chunks][kFiltChunk] candidate composite keys, or null
+                            // (then a row select never spills its candidates to memory)
+  uint32_t* cand_count;     // [R][n_chunks], or null with cand
   int32_t n_chunks;         // ceil(n_items / kFiltChunk)
   int32_t* out_idx;         // [R][k]
   float* out_score;         // [R][k] or null

@@ -928,6 +928,101 @@ __device__ __forceinline__ int row_select(const SelectArgs& a, int r, int64_t nv
   return min(nout, a.k);
 }
 
+// A row whose threshold bin holds more candidates than LDS takes, with no
+// candidate area in global memory (a one-stage call that does not filter):
+// the exact threshold key by the same radix steps as row_select, each a pass
+// over the row's stored scores, then the kept items in item order, straight
+// to the output.  Only degenerate rows come here (a threshold bin of more
+// than kRowCap scores: many equal scores, such as a row of zero queries).
+// Returns the number of ids written (<= k).
+__device__ __forceinline__ int row_select_stream(const SelectArgs& a, int r, int64_t nv, int64_t n_row,
+                                                 const RowThreshold& th, RowShared& sh, int32_t* oi, float* os,
+                                                 bool sort) {
+  const int tid = threadIdx.x;
+  const float* srow = a.scores + (int64_t)r * a.row_stride;
+  const float thr = bin_floor(th.bstar);
+  const int32_t* lrow = a.im.mode == kItemsPool ? a.im.list + (int64_t)r * a.im.list_len : nullptr;
+  // candidate j of this thread's four items i0 .. i0 + 3 (as row_compact:
+  // visible and at or above the threshold bin; NaN compares false)
+  auto keys4 = [&](int64_t i0, uint64_t (&K)[4]) {
+    uint32_t f = 0;
+    const float4 v = i0 < n_row ? *reinterpret_cast<const float4*>(srow + i0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = i0 + j;
+      K[j] = 0;
+      if (i < n_row && x[j] >= thr) {
+        int64_t pos = i;
+        if (a.im.mode == kItemsPool) pos = (int64_t)lrow[i >> 3] * kBlockPos + (i & 7);
+        else if (a.im.mode == kItemsCand) pos = item_pos(a.im, r, i, nv);
+        K[j] = comp_key(order_key(x[j]), pos);
+        f |= 1u << j;
+      }
+    }
+    return f;
+  };
+  constexpr int64_t kStep = 4 * kRowThreads;
+
+  uint64_t T = 0;
+  int need = (int)th.kk - th.c_above;
+  uint64_t prefix = (uint64_t)th.bstar;
+  for (int step = 0; step < 7; ++step) {
+    const int dshift = digit_shift(step), w = digit_width(step);
+    const uint32_t dmask = (1u << w) - 1u;
+    if (tid < 256) sh.hist[tid] = 0u;
+    if (tid == 0) { sh.digit = 0; sh.above = 0; sh.dcount = 0; }
+    __syncthreads();
+    for (int64_t base = 0; base < n_row; base += kStep) {
+      uint64_t K[4];
+      const uint32_t f = keys4(base + 4 * tid, K);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (((f >> j) & 1u) && (K[j] >> (dshift + w)) == prefix) atomicAdd(&sh.hist[(K[j] >> dshift) & dmask], 1u);
+    }
+    __syncthreads();
+    pick_digit(sh, need);
+    __syncthreads();
+    need -= sh.above;
+    prefix = (prefix << w) | (uint64_t)sh.digit;
+    const bool done = sh.dcount == need || dshift == 0;    // every key with this prefix is kept
+    __syncthreads();
+    if (done) {
+      T = prefix << dshift;
+      break;
+    }
+  }
+
+  // the kept keys (>= T) in item order
+  int written = 0;
+  for (int64_t base = 0; base < n_row; base += kStep) {
+    uint64_t K[4];
+    uint32_t f = keys4(base + 4 * tid, K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (K[j] < T) f &= ~(1u << j);
+    int tot;
+    int slot = written + dpp_block_scan<kRowThreads>(__popc(f), sh.wsum, tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((f >> j) & 1u) {
+        if (slot < a.k) {
+          if (sort) {
+            sh.sel_pos[slot] = comp_pos(K[j]);
+            sh.sel_score[slot] = comp_score(K[j]);
+          } else {
+            oi[slot] = comp_pos(K[j]);
+            if (os) os[slot] = comp_score(K[j]);
+          }
+        }
+        ++slot;
+      }
+    written += tot;
+    __syncthreads();                             // sh.wsum is reused by the next scan
+  }
+  return min(written, a.k);
+}
+
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char row_smem[];
   RowShared& sh = *reinterpret_cast<RowShared*>(row_smem);
@@ -947,9 +1042,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
     const RowThreshold th = hist_threshold<kRowThreads>(hv, a.k, sh.wsum, sh.pair);
     if (th.n_cand <= kRowCap)
       nsel = row_select(a, r, nv, n_row, th, A, sh.cbuf, kRowCap, sh, oi, os, sort);
-    else
+    else if (a.cand)
       nsel = row_select(a, r, nv, n_row, th, A, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
                         a.n_chunks * kFiltChunk, sh, oi, os, sort);
+    else
+      nsel = row_select_stream(a, r, nv, n_row, th, sh, oi, os, sort);
   }
   if (sort) {                                                  // candidate lists come in any order
     __syncthreads();
