@@ -92,6 +92,25 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
   return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// max(0, x) on the bits (a negative float is a negative integer): one
+// integer max, where a float max first quiets a NaN operand in an extra
+// instruction.  -0 becomes +0.
+__device__ __forceinline__ float relu0(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sums across 16-lane rows without LDS: rows 0..3 of the result hold
+// x.r0 + x.r1, y.r0 + y.r1, x.r2 + x.r3, y.r2 + y.r3 (one row swap between
+// the operands, then one add).
+__device__ __forceinline__ float row_pair_sum(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// ... and across the wave's halves: the lower half holds x.lo + x.hi, the
+// upper half y.lo + y.hi.
+__device__ __forceinline__ float half_pair_sum(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // The append of one row inside the coarse scan's launch (its last column),
 // for the (m, gate) forms a decode step uses.
 __device__ __forceinline__ void fused_append_row(const AppendArgs& ap, int r, int t) {
@@ -243,21 +262,17 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
         float sp = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sp = fmaf(w0[i], fmaxf(d0[i], 0.0f), sp);
-          sp = fmaf(w1[i], fmaxf(d1[i], 0.0f), sp);
+          sp = fmaf(w0[i], relu0(d0[i]), sp);
+          sp = fmaf(w1[i], relu0(d1[i]), sp);
         }
         p[u] = sp;
       }
       // transpose-reduce: lane (n, g) ends with the full score of tile
-      // u4 + g, entry n (sum over the four head groups) after three lane
-      // exchanges
-      const bool b0 = g & 1, b1 = (g >> 1) & 1;
-      float keep0 = b0 ? p[1] : p[0], send0 = b0 ? p[0] : p[1];
-      float keep1 = b0 ? p[3] : p[2], send1 = b0 ? p[2] : p[3];
-      keep0 += __shfl_xor(send0, 16);
-      keep1 += __shfl_xor(send1, 16);
-      float sc = b1 ? keep1 : keep0;
-      sc += __shfl_xor(b1 ? keep0 : keep1, 32);
+      // u4 + g, entry n (sum over the four head groups): row g of k0 holds
+      // head groups (g & 2, +1) of tile (g & 1), of k1 those of tile 2 +
+      // (g & 1); the halves then pair them
+      const float k0 = row_pair_sum(p[0], p[1]), k1 = row_pair_sum(p[2], p[3]);
+      const float sc = half_pair_sum(k0, k1);
       const int64_t item = c0 + (t0 + u4 + g) * 16 + n;
       if (item < c1) {
         const bool vis = item_pos(a.im, r, item, nv) >= 0;
@@ -421,8 +436,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
         float sp = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sp = fmaf(w0[i][j], fmaxf(d0[j], 0.0f), sp);
-          sp = fmaf(w1[i][j], fmaxf(d1[j], 0.0f), sp);
+          sp = fmaf(w0[i][j], relu0(d0[j]), sp);
+          sp = fmaf(w1[i][j], relu0(d1[j]), sp);
         }
         p[i][u] = sp;
       }
@@ -431,24 +446,16 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
     // with the score of tile g (U = 4) or g & 1 (U = 2, lanes g >= 2 hold a
     // copy and store nothing), entry n; the adds pair the head groups as
     // index_score_kernel does, so the scores are bit-identical
-    const bool b0 = g & 1, b1 = (g >> 1) & 1;
     const int32_t item = c0 + (tg + (U == 4 ? g : (g & 1))) * 16 + n;
     const bool owner = U == 4 || g < 2;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       float sc;
       if (U == 4) {
-        float keep0 = b0 ? p[i][1] : p[i][0], send0 = b0 ? p[i][0] : p[i][1];
-        float keep1 = b0 ? p[i][3] : p[i][2], send1 = b0 ? p[i][2] : p[i][3];
-        keep0 += __shfl_xor(send0, 16);
-        keep1 += __shfl_xor(send1, 16);
-        sc = b1 ? keep1 : keep0;
-        sc += __shfl_xor(b1 ? keep0 : keep1, 32);
+        sc = half_pair_sum(row_pair_sum(p[i][0], p[i][1]), row_pair_sum(p[i][2], p[i][3]));
       } else {
-        float keep = b0 ? p[i][1] : p[i][0];
-        const float send = b0 ? p[i][0] : p[i][1];
-        keep += __shfl_xor(send, 16);
-        sc = keep + __shfl_xor(keep, 32);
+        const float k0 = row_pair_sum(p[i][0], p[i][1]);
+        sc = half_pair_sum(k0, k0);
       }
       if (owner && item < c1 && item < nv[i]) {
         a.scores[(int64_t)(rbase + i) * a.row_stride + item] = sc;
