@@ -358,7 +358,9 @@ constexpr int kRowTiles = kRowGroup >= 4 ? 2 : 4;   // 16-item tiles per group (
 template <int RG, int U>
 __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(ScoreArgs a) {
   static_assert(U == 2 || U == 4, "16-item tiles per group: 2 or 4");
-  __shared__ uint32_t hist[RG][kHistBins];
+  // the rows' histograms, then one word per thread for the counts of lanes
+  // that count nothing (the epilogue has no branch)
+  __shared__ uint32_t hist[RG * kHistBins + kScoreThreads];
   const int rbase = blockIdx.y * RG;
   // item counts stay below kMaxItems (2^24): 32-bit indices
   int32_t nv[RG];
@@ -415,8 +417,12 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
       qa1[i][v] = fp8x8_to_f16(qr1[i][2 * v], qr1[i][2 * v + 1]);
     }
   }
-  for (int b = threadIdx.x; b < RG * kHistBins; b += kScoreThreads) (&hist[0][0])[b] = 0u;
+  for (int b = threadIdx.x; b < RG * kHistBins; b += kScoreThreads) hist[b] = 0u;
   lds_barrier();                                 // the key loads stay in flight
+  // the workgroup's score rows: a store at an offset past the buffer's size
+  // is dropped by the hardware, which masks the stores without a branch
+  const auto srows = __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)rbase * a.row_stride, 0,
+                                                       (int)((int64_t)RG * a.row_stride * 4), 0x00020000);
 
   auto compute_group = [&](int32_t tg, const v8i* kb) {
     float p[RG][U];
@@ -447,7 +453,8 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
     // copy and store nothing), entry n; the adds pair the head groups as
     // index_score_kernel does, so the scores are bit-identical
     const int32_t item = c0 + (tg + (U == 4 ? g : (g & 1))) * 16 + n;
-    const bool owner = U == 4 || g < 2;
+    // lanes holding a copy get an item no bound admits
+    const int32_t item_o = (U == 4 || g < 2) ? item : INT32_MAX;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       float sc;
@@ -457,10 +464,17 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
         const float k0 = row_pair_sum(p[i][0], p[i][1]);
         sc = half_pair_sum(k0, k0);
       }
-      if (owner && item < c1 && item < nv[i]) {
-        a.scores[(int64_t)(rbase + i) * a.row_stride + item] = sc;
-        atomicAdd(&hist[i][order_key(sc) >> (32 - kHistBits)], 1u);
-      }
+      const bool own = item_o < min(c1, nv[i]);
+      // the order key without order_key's -0 case: a score here is never
+      // -0 (the sums start at +0, relu0 gives no -0, and a zero sum of
+      // terms that are not -0 is +0 when rounding to nearest)
+      const uint32_t u = __float_as_uint(sc);
+      const uint32_t ok = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+      int off = own ? 4 * item + i * 4 * a.row_stride : INT32_MAX;
+      uint32_t bin = own ? (uint32_t)(i * kHistBins) + (ok >> (32 - kHistBits)) : (uint32_t)(RG * kHistBins) + threadIdx.x;
+      asm volatile("" : "+v"(off), "+v"(bin));  // selects, not branches
+      __builtin_amdgcn_raw_buffer_store_b32(u, srows, off, 0, 0);
+      atomicAdd(&hist[bin], 1u);
     }
   };
   // two groups per trip, no exit between them (a group past the chunk is
@@ -480,7 +494,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
     if (rbase + i >= a.n_rows) break;            // uniform
     uint32_t* ghist = a.hist + (int64_t)(rbase + i) * kHistBins;
     for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
-      const uint32_t c = hist[i][b];
+      const uint32_t c = hist[i * kHistBins + b];
       if (c) atomicAdd(&ghist[b], c);
     }
   }
