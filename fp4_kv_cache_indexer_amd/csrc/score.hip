@@ -154,28 +154,33 @@ __device__ __forceinline__ void fused_block_summary(const AppendArgs& ap, int r,
 template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0, bool APP = false>
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ float sscore[kScoreStage];
+  // the histogram and the staged scores, each followed by one word per
+  // thread for the lanes that count or stage nothing (no branch)
+  __shared__ uint32_t hist[kHistBins + kScoreThreads];
+  __shared__ float sscore[kScoreStage + kScoreThreads];
   __shared__ __align__(16) uint8_t sp_key[APP ? kIdxDim : 16];
+  // E4M3 keys pass through a wave-private buffer of two 16-key tiles
+  __shared__ __align__(16) uint8_t kstage[KF ? 16 : kScoreWaves * 2 * 16 * kIdxDim];
   const int r = blockIdx.y;
   if (APP && blockIdx.x == gridDim.x - 1) {      // uniform: the row's append
     fused_append_row(a.app, r, threadIdx.x);
     return;
   }
   const int64_t nv = row_valid(a.im, r);
-  const int64_t n_row = row_items(a.im, nv);
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  // items stay below kMaxItems (2^24) per row: 32-bit item arithmetic
+  const int32_t n_row = (int32_t)row_items(a.im, nv);
+  const int32_t c0 = (int32_t)blockIdx.x * a.chunk;
   if (c0 >= n_row) return;                       // uniform for the workgroup
-  const int64_t c1 = min(c0 + (int64_t)a.chunk, n_row);
+  const int32_t c1 = min(c0 + a.chunk, n_row);
   const bool stage = c1 - c0 <= kScoreStage;     // uniform
   // the block whose summary the row's append refreshes, when this chunk
   // holds it: scored from its new summary, recomputed here
-  int64_t sp = -1;
+  int32_t sp = -1;
   if (APP && a.app.block_keys) {
     int64_t aseq;
     const int64_t e = append_entry(a.app, r, aseq);
     if (e >= 0 && e / kBlockPos >= c0 && e / kBlockPos < c1) {
-      sp = e / kBlockPos;
+      sp = (int32_t)(e / kBlockPos);
       fused_block_summary(a.app, r, aseq, e, sp_key);   // ordered before the scoring by the barrier below
     }
   }
@@ -187,6 +192,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // FP4 code bytes and the scale word (byte g)
   constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
   const uint8_t* kbase = a.keys + seq * a.seq_rows * kKeyBytes + g * (KF ? 16 : 32);
+  const uint8_t* krow = a.keys + seq * a.seq_rows * kKeyBytes;
   const uint8_t* sbase = KF ? a.key_scales + seq * a.seq_rows * 4 : nullptr;
 
   // MFMA A operands: indexer query rows n and 16+n, bytes [32g, 32g+32), as
@@ -211,16 +217,16 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // A wave works on groups of U tiles of 16 items (U a multiple of 4).
   // Loads are unconditional (an invisible item reads a visible row and its
   // score is masked when written).
-  const int64_t ntiles = (c1 - c0 + 15) / 16;
-  const int64_t gstride = (int64_t)kScoreWaves * U;
+  const int32_t ntiles = (c1 - c0 + 15) / 16;
+  const int32_t gstride = kScoreWaves * U;
   const int32_t p0 = (int32_t)item_pos(a.im, r, c0, nv);
   const int32_t safe_pos = p0 >= 0 ? p0 : 0;
-  auto load_group = [&](int64_t t0, v8i* kb, int32_t* pos) {
+  auto load_group = [&](int32_t t0, v8i* kb, int32_t* pos) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t item = c0 + (t0 + u) * 16 + n;
+      const int32_t item = c0 + (t0 + u) * 16 + n;
       pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
-      const int64_t p = pos[u] >= 0 ? pos[u] : safe_pos;
+      const uint64_t p = (uint32_t)(pos[u] >= 0 ? pos[u] : safe_pos);
       if (KF) {
         constexpr bool NT = MODE != 0;
         const uint4 c = NT ? load16_nt(kbase + p * kKeyBytes) : *reinterpret_cast<const uint4*>(kbase + p * kKeyBytes);
@@ -228,11 +234,51 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
         kb[u][4] = NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + p * 4))
                       : *reinterpret_cast<const uint32_t*>(sbase + p * 4);
       } else {
-        kb[u] = load32k<MODE != 0>(kbase + p * kKeyBytes);
+        // E4M3: each load instruction reads 8 whole keys (lane L: key 8j +
+        // L / 8 of the tile, bytes 16 (L % 8)), one request per cache line
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int32_t it = c0 + (t0 + u) * 16 + 8 * j + (lane >> 3);
+          const int32_t ps = it < c1 ? (int32_t)item_pos(a.im, r, it, nv) : -1;
+          const uint64_t pj = (uint32_t)(ps >= 0 ? ps : safe_pos);
+          const uint8_t* src = krow + pj * kIdxDim + 16 * (lane & 7);
+          const uint4 c = MODE != 0 ? load16_nt(src) : *reinterpret_cast<const uint4*>(src);
+          kb[u][4 * j] = c.x; kb[u][4 * j + 1] = c.y; kb[u][4 * j + 2] = c.z; kb[u][4 * j + 3] = c.w;
+        }
       }
     }
   };
-  auto compute_group = [&](int64_t t0, v8i* kb) {
+  // the loaded tiles into the operand layout (lane (n, g): bytes 32g .. +31
+  // of key n), two at a time through the wave's buffer; key k's 16-byte
+  // segment s sits at s ^ (k & 7) ^ ((k >> 3) & 1), so the writes (two keys
+  // per 16 lanes) and the reads (16 keys, one segment) touch distinct banks.
+  // The wave's own LDS accesses complete in order: no barrier.
+  uint8_t* kst = kstage + (KF ? 0 : wave * 2 * 16 * kIdxDim);
+  auto stage_group = [&](v8i* kb) {
+#pragma unroll
+    for (int h = 0; h < U; h += 2) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int kk = 8 * j + (lane >> 3);
+          const int seg = (lane & 7) ^ (kk & 7) ^ ((kk >> 3) & 1);
+          *reinterpret_cast<uint4*>(kst + s2 * 16 * kIdxDim + kk * kIdxDim + 16 * seg) =
+              make_uint4(kb[h + s2][4 * j], kb[h + s2][4 * j + 1], kb[h + s2][4 * j + 2], kb[h + s2][4 * j + 3]);
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int sl = (2 * g) ^ (n & 7) ^ ((n >> 3) & 1), sh = (2 * g + 1) ^ (n & 7) ^ ((n >> 3) & 1);
+        const uint4 lo = *reinterpret_cast<const uint4*>(kst + s2 * 16 * kIdxDim + n * kIdxDim + 16 * sl);
+        const uint4 hi = *reinterpret_cast<const uint4*>(kst + s2 * 16 * kIdxDim + n * kIdxDim + 16 * sh);
+        kb[h + s2] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+  };
+  // a store at an offset past the row's buffer is dropped by the hardware
+  const auto srows = __builtin_amdgcn_make_buffer_rsrc(srow, 0, (int)((int64_t)n_row * 4), 0x00020000);
+  auto compute_group = [&](int32_t t0, v8i* kb) {
+    if (!KF) stage_group(kb);
     if (APP && sp >= 0) {                        // uniform: the refreshed block's key from LDS
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -273,19 +319,27 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       // (g & 1); the halves then pair them
       const float k0 = row_pair_sum(p[0], p[1]), k1 = row_pair_sum(p[2], p[3]);
       const float sc = half_pair_sum(k0, k1);
-      const int64_t item = c0 + (t0 + u4 + g) * 16 + n;
-      if (item < c1) {
-        const bool vis = item_pos(a.im, r, item, nv) >= 0;
-        const float out = vis ? sc : __uint_as_float(0x7FC00000u);   // NaN: not visible
-        if (stage) sscore[item - c0] = out;
-        else srow[item] = out;
-        if (vis) atomicAdd(&hist[order_key(sc) >> (32 - kHistBits)], 1u);
+      const int32_t item = c0 + (t0 + u4 + g) * 16 + n;
+      const bool in = item < c1;
+      const bool vis = in && item_pos(a.im, r, item, nv) >= 0;
+      const float out = vis ? sc : __uint_as_float(0x7FC00000u);   // NaN: not visible
+      if (stage) {                               // uniform
+        int si = in ? item - c0 : kScoreStage + (int)threadIdx.x;
+        asm volatile("" : "+v"(si));             // a select, not a branch
+        sscore[si] = out;
+      } else {
+        int off = in ? 4 * item : INT32_MAX;
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), srows, off, 0, 0);
       }
+      uint32_t bin = vis ? order_key(sc) >> (32 - kHistBits) : kHistBins + threadIdx.x;
+      asm volatile("" : "+v"(bin));
+      atomicAdd(&hist[bin], 1u);
     }
   };
   v8i kA[U], kB[U];
   int32_t pA[U], pB[U];
-  int64_t t0 = (int64_t)wave * U;
+  int32_t t0 = wave * U;
   // Group loads are unconditional (tiles past the chunk read a visible key
   // and are discarded): a load on one side of a branch makes the compiler's
   // later waits cover it, which would serialise the double buffer.
@@ -302,7 +356,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     // straight-line: load group i+1 before computing group i
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const int64_t ti = t0 + i * gstride;
+      const int32_t ti = t0 + i * gstride;
       if (i + 1 < G) {
         if (i & 1) load_group(ti + gstride, kA, pA); else load_group(ti + gstride, kB, pB);
       }
@@ -314,7 +368,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     // two groups per trip and no exit between them (a group past the chunk
     // is computed and discarded): one loop shape keeps the waits exact
     for (; t0 < ntiles; t0 += 2 * gstride) {
-      const int64_t t1 = t0 + gstride;
+      const int32_t t1 = t0 + gstride;
       load_group(t1, kB, pB);
       __builtin_amdgcn_sched_barrier(0);
       compute_group(t0, kA);
@@ -330,7 +384,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   }
   lds_barrier();
   if (stage)
-    for (int64_t i = threadIdx.x; i < c1 - c0; i += kScoreThreads) srow[c0 + i] = sscore[i];
+    for (int32_t i = threadIdx.x; i < c1 - c0; i += kScoreThreads) srow[c0 + i] = sscore[i];
   uint32_t* ghist = a.hist + (int64_t)r * kHistBins;
   for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
     const uint32_t c = hist[b];
