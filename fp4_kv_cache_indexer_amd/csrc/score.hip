@@ -154,13 +154,18 @@ __device__ __forceinline__ void fused_block_summary(const AppendArgs& ap, int r,
 template <int MODE, int KF = 0, bool DB = false, int MINW = 4, int U = kTilesPerIter, int G = 0, bool APP = false>
 __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreArgs a) {
   a.im.mode = MODE;                              // lets the item mapping fold away
+  // Block summaries (the long, HBM-bound coarse scan) are read in whole
+  // cache lines and staged through LDS; the short gathers of the other
+  // modes read straight into the operand layout (the staging's LDS round
+  // trip costs them more than the halved line requests save).
+  constexpr bool FULL = !KF && MODE == kItemsBlocks;
   // the histogram and the staged scores, each followed by one word per
   // thread for the lanes that count or stage nothing (no branch)
   __shared__ uint32_t hist[kHistBins + kScoreThreads];
   __shared__ float sscore[kScoreStage + kScoreThreads];
   __shared__ __align__(16) uint8_t sp_key[APP ? kIdxDim : 16];
-  // E4M3 keys pass through a wave-private buffer of two 16-key tiles
-  __shared__ __align__(16) uint8_t kstage[KF ? 16 : kScoreWaves * 2 * 16 * kIdxDim];
+  // staged keys pass through a wave-private buffer of two 16-key tiles
+  __shared__ __align__(16) uint8_t kstage[FULL ? kScoreWaves * 2 * 16 * kIdxDim : 16];
   const int r = blockIdx.y;
   if (APP && blockIdx.x == gridDim.x - 1) {      // uniform: the row's append
     fused_append_row(a.app, r, threadIdx.x);
@@ -233,9 +238,11 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
         kb[u][0] = c.x; kb[u][1] = c.y; kb[u][2] = c.z; kb[u][3] = c.w;
         kb[u][4] = NT ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sbase + p * 4))
                       : *reinterpret_cast<const uint32_t*>(sbase + p * 4);
+      } else if (!FULL) {
+        kb[u] = load32k<MODE != 0>(kbase + p * kKeyBytes);
       } else {
-        // E4M3: each load instruction reads 8 whole keys (lane L: key 8j +
-        // L / 8 of the tile, bytes 16 (L % 8)), one request per cache line
+        // each load instruction reads 8 whole keys (lane L: key 8j + L / 8
+        // of the tile, bytes 16 (L % 8)), one request per cache line
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int32_t it = c0 + (t0 + u) * 16 + 8 * j + (lane >> 3);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // segment s sits at s ^ (k & 7) ^ ((k >> 3) & 1), so the writes (two keys
   // per 16 lanes) and the reads (16 keys, one segment) touch distinct banks.
   // The wave's own LDS accesses complete in order: no barrier.
-  uint8_t* kst = kstage + (KF ? 0 : wave * 2 * 16 * kIdxDim);
+  uint8_t* kst = kstage + (FULL ? wave * 2 * 16 * kIdxDim : 0);
   auto stage_group = [&](v8i* kb) {
 #pragma unroll
     for (int h = 0; h < U; h += 2) {
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // a store at an offset past the row's buffer is dropped by the hardware
   const auto srows = __builtin_amdgcn_make_buffer_rsrc(srow, 0, (int)((int64_t)n_row * 4), 0x00020000);
   auto compute_group = [&](int32_t t0, v8i* kb) {
-    if (!KF) stage_group(kb);
+    if (FULL) stage_group(kb);
     if (APP && sp >= 0) {                        // uniform: the refreshed block's key from LDS
 #pragma unroll
       for (int u = 0; u < U; ++u) {
