@@ -766,16 +766,16 @@ struct RowRound {
 
 // Raw loads of one round (addresses clamped into the row; masking happens in
 // row_compact), unconditional so that nothing waits on them before use.
-// Other modes than pool load a discarded word of the score row as block ids.
+// POOL: pool mode, whose block ids are loaded beside the scores (the other
+// modes neither load nor hold them).
+template <bool POOL>
 __device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float* srow, int64_t base,
                                          RowRound& R) {
-  const bool pool = a.im.mode == kItemsPool;
-  const int32_t* lrow = pool ? a.im.list + (int64_t)r * a.im.list_len : reinterpret_cast<const int32_t*>(srow);
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
     const int64_t iu = base + (int64_t)u * kRowSub + 4 * threadIdx.x;
     R.v[u] = *reinterpret_cast<const float4*>(srow + (iu < a.row_stride ? iu : 0));
-    R.blk[u] = lrow[pool && (iu >> 3) < a.im.list_len ? (iu >> 3) : 0];
+    if (POOL) R.blk[u] = a.im.list[(int64_t)r * a.im.list_len + ((iu >> 3) < a.im.list_len ? (iu >> 3) : 0)];
   }
 }
 
@@ -784,6 +784,7 @@ __device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float
 // Within a sub-round u an item's slot counts the kept items of lower lanes
 // (ballots of the bits of each lane's count) and of lower waves (per-wave
 // totals in LDS, one lane per (u, wave) summed by a row scan).
+template <bool POOL>
 __device__ __forceinline__ int row_compact(const SelectArgs& a, int r, int64_t nv, int64_t n_row, int64_t base,
                                            float thr, const RowRound& R, uint64_t* cbuf, int cap, int written,
                                            int parity, RowShared& sh) {
@@ -827,7 +828,7 @@ __device__ __forceinline__ int row_compact(const SelectArgs& a, int r, int64_t n
     const int tot = __builtin_amdgcn_readlane(sc, 16 * u + 15);
     int slot = start + incl - wt[u] + below[u];
     const int64_t iu = i0 + (int64_t)u * kRowSub;
-    if (a.im.mode == kItemsPool) {                             // uniform
+    if (POOL) {
       const int64_t pb = (int64_t)R.blk[u] * kBlockPos + (iu & 7);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -853,21 +854,29 @@ __device__ __forceinline__ int row_compact(const SelectArgs& a, int r, int64_t n
 
 // Collect, select and write one row with the candidates in cbuf (LDS or
 // global).  Returns the number of ids written to the output (<= k).
+template <bool POOL>
 __device__ __forceinline__ int row_select(const SelectArgs& a, int r, int64_t nv, int64_t n_row,
-                                          const RowThreshold& th, RowRound& A, uint64_t* cbuf, int cap,
-                                          RowShared& sh, int32_t* oi, float* os, bool sort) {
+                                          const RowThreshold& th, RowRound& A, RowRound& B, uint64_t* cbuf,
+                                          int cap, RowShared& sh, int32_t* oi, float* os, bool sort) {
   const int tid = threadIdx.x;
   const float* srow = a.scores + (int64_t)r * a.row_stride;
 
-  // 1. candidates in item order (A holds round 0, loaded before the threshold
-  // search; a row longer than one round waits for each further round)
+  // 1. candidates in item order.  A and B hold rounds 0 and 1, loaded before
+  // the threshold search; while one round is compacted the next is in
+  // flight, and its successor is loaded as soon as its registers are free.
+  // The loads are unconditional (clamped addresses; rounds past the row are
+  // read and ignored) so that each wait covers only its own round.
   const float thr = bin_floor(th.bstar);
   int written = 0, parity = 0;
-  for (int64_t base = 0;; base += kRowRound) {
-    written = row_compact(a, r, nv, n_row, base, thr, A, cbuf, cap, written, parity, sh);
+  for (int64_t base = 0;; base += 2 * kRowRound) {
+    written = row_compact<POOL>(a, r, nv, n_row, base, thr, A, cbuf, cap, written, parity, sh);
     parity ^= 1;
     if (base + kRowRound >= n_row) break;
-    row_load(a, r, srow, base + kRowRound, A);
+    row_load<POOL>(a, r, srow, base + 2 * kRowRound, A);
+    written = row_compact<POOL>(a, r, nv, n_row, base + kRowRound, thr, B, cbuf, cap, written, parity, sh);
+    parity ^= 1;
+    if (base + 2 * kRowRound >= n_row) break;
+    row_load<POOL>(a, r, srow, base + 3 * kRowRound, B);
   }
   __syncthreads();
   const int n_cand = min(written, cap);        // equal to th.n_cand: the histogram counted these items
@@ -1023,6 +1032,7 @@ __device__ __forceinline__ int row_select_stream(const SelectArgs& a, int r, int
   return min(written, a.k);
 }
 
+template <bool POOL>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char row_smem[];
   RowShared& sh = *reinterpret_cast<RowShared*>(row_smem);
@@ -1037,13 +1047,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(SelectArgs a) {
   if (n_row > 0) {                                             // uniform
     uint32_t hv[kHistBins / kRowThreads];
     hist_load<kRowThreads>(gh, hv);
-    RowRound A;                                                // the first round's scores fly
-    row_load(a, r, a.scores + (int64_t)r * a.row_stride, 0, A);   // during the threshold search
+    RowRound A, B;                                             // the first two rounds' scores fly
+    row_load<POOL>(a, r, a.scores + (int64_t)r * a.row_stride, 0, A);   // during the threshold search
+    row_load<POOL>(a, r, a.scores + (int64_t)r * a.row_stride, kRowRound, B);
     const RowThreshold th = hist_threshold<kRowThreads>(hv, a.k, sh.wsum, sh.pair);
     if (th.n_cand <= kRowCap)
-      nsel = row_select(a, r, nv, n_row, th, A, sh.cbuf, kRowCap, sh, oi, os, sort);
+      nsel = row_select<POOL>(a, r, nv, n_row, th, A, B, sh.cbuf, kRowCap, sh, oi, os, sort);
     else if (a.cand)
-      nsel = row_select(a, r, nv, n_row, th, A, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
+      nsel = row_select<POOL>(a, r, nv, n_row, th, A, B, a.cand + (int64_t)r * a.n_chunks * kFiltChunk,
                         a.n_chunks * kFiltChunk, sh, oi, os, sort);
     else
       nsel = row_select_stream(a, r, nv, n_row, th, sh, oi, os, sort);
@@ -1095,11 +1106,18 @@ hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)sizeof(RowShared));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.n_rows), dim3(kRowThreads), sizeof(RowShared), stream, a);
+  static const hipError_t attr_p = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel<true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)sizeof(RowShared));
+  static const hipError_t attr_o = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_row_kernel<false>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)sizeof(RowShared));
+  if (attr_p != hipSuccess) return attr_p;
+  if (attr_o != hipSuccess) return attr_o;
+  if (a.im.mode == kItemsPool)
+    hipLaunchKernelGGL(topk_row_kernel<true>, dim3((unsigned)a.n_rows), dim3(kRowThreads), sizeof(RowShared), stream, a);
+  else
+    hipLaunchKernelGGL(topk_row_kernel<false>, dim3((unsigned)a.n_rows), dim3(kRowThreads), sizeof(RowShared), stream, a);
   return hipGetLastError();
 }
 
