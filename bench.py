@@ -357,6 +357,60 @@ def measured_traffic(workload):
     return float(mb.group(1))
 
 
+def _time_us(fn, reps=8, skip=2):
+    """Mean of reps - skip event-timed calls of fn on the current stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev[skip:]]
+    return sum(t) / len(t)
+
+
+def run_probe(which):
+    """The diagnostic probes behind the kernels' designs: the block-summary
+    scan's read shape, the overlap of a wave's vector work with its MFMA
+    chain, and the attention gather's read shape."""
+    st = torch.cuda.current_stream()
+    if which == "scan":
+        rows, n = 8, 131072                     # the C3 coarse scan: 8 rows x 131,072 summaries
+        sets = [torch.randint(0, 256, (rows, n, 128), dtype=torch.uint8, device="cuda") for _ in range(4)]
+        nbytes = rows * n * 128
+        print("| workgroups per row | chunk | load shape | us | TB/s |\n|---:|---:|---|---:|---:|")
+        for per_row in (64, 96, 128, 192):
+            chunk = ((n + per_row - 1) // per_row + 15) // 16 * 16
+            for full, nt in ((False, False), (False, True), (True, False), (True, True)):
+                k = [0]
+                def fn():
+                    C.probe_scan_read(sets[k[0] % 4], chunk, full, nt, stream=st)
+                    k[0] += 1
+                us = _time_us(fn, reps=12, skip=4)
+                shape = ("whole lines" if full else "half lines") + (", non-temporal" if nt else "")
+                print(f"| {per_row} | {chunk} | {shape} | {us:.2f} | {nbytes / us / 1e6:.2f} |")
+    elif which == "mfma-valu":
+        iters, n_wg = 2048, 256
+        print("| waves per SIMD | FMAs per MFMA | us | ns per MFMA per SIMD |\n|---:|---:|---:|---:|")
+        for threads in (256, 512):
+            for nv in (0, 4, 8, 12, 16):
+                us = _time_us(lambda: C.probe_mfma_valu(nv, threads, iters, n_wg, stream=st))
+                per_simd = iters * 8 * (threads // 64) / 4
+                print(f"| {threads // 256} | {nv} | {us:.1f} | {us * 1e3 / per_simd:.2f} |")
+    else:
+        n_ent, rows = 524288, 4096              # the C5 attention: 4096 rows x 512 entries
+        codes = torch.randint(0, 256, (n_ent, 256), dtype=torch.uint8, device="cuda")
+        scales = torch.randint(0, 256, (n_ent, 32), dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(1)
+        ids = torch.randint(0, n_ent, (rows, 512), dtype=torch.int32, device="cuda", generator=g)
+        nbytes = rows * 512 * (256 + 32)
+        print("| lane mapping | us | TB/s |\n|---|---:|---:|")
+        for whole in (False, True):
+            us = _time_us(lambda: C.probe_gather(codes, scales, ids, 256, whole, stream=st))
+            name = "whole lines (16 lanes per entry)" if whole else "attention kernels' (4 x 16 B per quarter entry)"
+            print(f"| {name} | {us:.1f} | {nbytes / us / 1e6:.2f} |")
+
+
 def prof_summary(d):
     """Markdown tables from the rocprofv3 CSV output under directory d:
     kernel durations (*_kernel_stats.csv) and mean counter values per
@@ -796,6 +850,8 @@ def main():
                     help="also run a copy kernel of this size (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--sweep", action="store_true",
                     help="40-layer step across contexts 4K..1M (workload sched40 or sched40fp4); prints a table")
+    ap.add_argument("--probe", choices=["scan", "mfma-valu", "gather"], default=None,
+                    help="time one of the library's diagnostic probes and print its table")
     ap.add_argument("--prof-summary", metavar="DIR",
                     help="print markdown summaries of the rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
@@ -808,6 +864,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     C.lib()
+    if args.probe:
+        run_probe(args.probe)
+        return
     if args.attn_plan:
         hpw, ns = (int(v) for v in args.attn_plan.split(","))
         C.attn_plan_override(hpw, ns)

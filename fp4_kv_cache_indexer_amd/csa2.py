@@ -108,6 +108,7 @@ EXPORTS = (
     "csa2_indexer_topk_workspace", "csa2_indexer_topk", "csa2_indexer_topk_static", "csa2_append_indexer_topk",
     "csa2_sparse_attn_workspace", "csa2_sparse_attn_decode", "csa2_attn_plan_override",
     "csa2_kernel_timer_start", "csa2_kernel_timer_stop", "csa2_mfma_dot_probe",
+    "csa2_probe_scan_read", "csa2_probe_mfma_valu", "csa2_probe_gather",
 )
 
 KEY_E4M3, KEY_FP4 = 0, 1          # index-key formats (CSA2_KEY_*)
@@ -155,6 +156,12 @@ def lib():
     L.csa2_attn_plan_override.argtypes = [i32, i32]
     L.csa2_mfma_dot_probe.restype = i32
     L.csa2_mfma_dot_probe.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    L.csa2_probe_scan_read.restype = i32
+    L.csa2_probe_scan_read.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+    L.csa2_probe_mfma_valu.restype = i32
+    L.csa2_probe_mfma_valu.argtypes = [i32, i32, i32, i32, vp, vp]
+    L.csa2_probe_gather.restype = i32
+    L.csa2_probe_gather.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp, vp]
     L.csa2_sparse_attn_decode.restype = i32
     L.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
     L.csa2_kernel_timer_start.restype = i32
@@ -477,6 +484,41 @@ def mfma_dot_probe(q, k, stream=None):
     o8 = torch.empty((nq, nk), dtype=torch.float32, device=q.device)
     _check(lib().csa2_mfma_dot_probe(_ptr(q), _ptr(k), nq, nk, _ptr(o16), _ptr(o8), _stream(stream)))
     return o16, o8
+
+
+def probe_scan_read(keys, chunk, full_lines, nontemporal, stream=None):
+    """Timing probe: read keys uint8 [n_rows, n_keys, 128] in the block-summary
+    scan's shape (chunks of `chunk` keys per workgroup); returns the
+    per-thread XOR words."""
+    _dev(keys, "keys")
+    if keys.dim() != 3 or keys.shape[2] != 128 or keys.dtype != torch.uint8:
+        raise ValueError("probe_scan_read: keys must be uint8 [n_rows, n_keys, 128]")
+    n_rows, n_keys = keys.shape[0], keys.shape[1]
+    wgs = n_rows * ((n_keys + chunk - 1) // chunk)
+    out = torch.empty(wgs * 256, dtype=torch.int32, device=keys.device)
+    _check(lib().csa2_probe_scan_read(_ptr(keys), n_rows, n_keys, int(chunk), int(bool(full_lines)),
+                                      int(bool(nontemporal)), _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_mfma_valu(n_valu, threads, iters, n_wg, stream=None):
+    """Timing probe: MFMA chains with n_valu independent FMAs per MFMA."""
+    out = torch.empty(n_wg * threads, dtype=torch.float32, device="cuda")
+    _check(lib().csa2_probe_mfma_valu(int(n_valu), int(threads), int(iters), int(n_wg), _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_gather(codes, scales, ids, n_wg, whole_lines, stream=None):
+    """Timing probe: the attention gather's reads of FP4 entries (codes uint8
+    [n_ent, 256], scales uint8 [n_ent, 32]) for ids int32 [n_rows, 512]."""
+    _dev(codes, "codes"), _dev(scales, "scales"), _dev(ids, "ids")
+    if (codes.dim() != 2 or codes.shape[1] != 256 or scales.shape != (codes.shape[0], 32)
+            or ids.dim() != 2 or ids.shape[1] != 512 or ids.dtype != torch.int32):
+        raise ValueError("probe_gather: codes [n_ent, 256], scales [n_ent, 32], ids int32 [n_rows, 512]")
+    out = torch.empty(n_wg * 128, dtype=torch.int32, device=codes.device)
+    _check(lib().csa2_probe_gather(_ptr(codes), _ptr(scales), codes.shape[0], _ptr(ids), ids.shape[0], int(n_wg),
+                                   int(bool(whole_lines)), _ptr(out), _stream(stream)))
+    return out
 
 
 def attn_plan_override(heads_per_wg=0, n_split=0):

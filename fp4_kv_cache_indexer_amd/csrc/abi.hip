@@ -759,6 +759,47 @@ int32_t csa2_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int
   return CSA2_OK;
 }
 
+int32_t csa2_probe_scan_read(const uint8_t* keys, int32_t n_rows, int32_t n_keys, int32_t chunk, int32_t full_lines,
+                             int32_t nontemporal, uint32_t* out, void* stream) {
+  g_err.clear();
+  if (n_rows < 1 || n_keys < 1 || chunk < 16 || n_keys > (1 << 24))
+    return fail(CSA2_EINVAL, "scan probe: n_rows %d, n_keys %d, chunk %d out of range", n_rows, n_keys, chunk);
+  const int64_t wgs = (int64_t)n_rows * ((n_keys + chunk - 1) / chunk);
+  if (wgs > (1 << 20)) return fail(CSA2_EINVAL, "scan probe: %lld workgroups exceed 2^20", (long long)wgs);
+  if (!keys || !out || !aligned(keys, 16) || !aligned(out, 4))
+    return fail(CSA2_EINVAL, "scan probe: null or misaligned pointer");
+  const hipError_t e = csa2::launch_scan_read_probe(keys, n_rows, n_keys, chunk, full_lines != 0, nontemporal != 0,
+                                                    out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "scan probe");
+}
+
+int32_t csa2_probe_mfma_valu(int32_t n_valu, int32_t threads, int32_t iters, int32_t n_wg, float* out,
+                             void* stream) {
+  g_err.clear();
+  if (n_valu != 0 && n_valu != 4 && n_valu != 8 && n_valu != 12 && n_valu != 16)
+    return fail(CSA2_EINVAL, "mfma/valu probe: n_valu %d not one of 0, 4, 8, 12, 16", n_valu);
+  if (threads != 256 && threads != 512) return fail(CSA2_EINVAL, "mfma/valu probe: threads %d not 256 or 512", threads);
+  if (iters < 1 || iters > (1 << 20) || n_wg < 1 || n_wg > 65536)
+    return fail(CSA2_EINVAL, "mfma/valu probe: iters %d or n_wg %d out of range", iters, n_wg);
+  if (!out || !aligned(out, 4)) return fail(CSA2_EINVAL, "mfma/valu probe: null or misaligned out");
+  const hipError_t e = csa2::launch_mfma_valu_probe(n_valu, threads, iters, n_wg, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "mfma/valu probe");
+}
+
+int32_t csa2_probe_gather(const uint8_t* codes, const uint8_t* scales, int64_t n_ent, const int32_t* ids,
+                          int32_t n_rows, int32_t n_wg, int32_t whole_lines, uint32_t* out, void* stream) {
+  g_err.clear();
+  if (n_ent < 1 || n_ent > (1LL << 31) || n_rows < 1 || n_wg < 1 || n_wg > 65536)
+    return fail(CSA2_EINVAL, "gather probe: n_ent %lld, n_rows %d or n_wg %d out of range", (long long)n_ent, n_rows,
+                n_wg);
+  if (!codes || !scales || !ids || !out || !aligned(codes, 16) || !aligned(scales, 16) || !aligned(ids, 4) ||
+      !aligned(out, 4))
+    return fail(CSA2_EINVAL, "gather probe: null or misaligned pointer");
+  const hipError_t e = csa2::launch_gather_probe(codes, scales, n_ent, ids, n_rows, n_wg, whole_lines != 0, out,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : hip_fail(e, "gather probe");
+}
+
 int32_t csa2_kernel_timer_start(int32_t site, int32_t max_launches) {
   g_err.clear();
   if (site < CSA2_SITE_KV_QUANT || site > CSA2_SITE_APPEND)

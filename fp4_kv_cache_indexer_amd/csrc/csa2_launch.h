@@ -159,5 +159,11 @@ hipError_t launch_sparse_attn_tile(const AttnArgs& a, hipStream_t stream);     /
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int32_t n_k, float* out16,
                                  float* out8, hipStream_t stream);
+hipError_t launch_scan_read_probe(const uint8_t* keys, int32_t n_rows, int32_t n_keys, int32_t chunk, bool full,
+                                  bool nt, uint32_t* out, hipStream_t stream);
+hipError_t launch_mfma_valu_probe(int32_t n_valu, int32_t threads, int32_t iters, int32_t n_wg, float* out,
+                                  hipStream_t stream);
+hipError_t launch_gather_probe(const uint8_t* codes, const uint8_t* scales, int64_t n_ent, const int32_t* ids,
+                               int32_t n_rows, int32_t n_wg, bool whole, uint32_t* out, hipStream_t stream);
 
 }  // namespace csa2

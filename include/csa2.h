@@ -454,6 +454,44 @@ int32_t csa2_kernel_timer_stop(int32_t* n_launches, float* total_ms);
 int32_t csa2_mfma_dot_probe(const uint8_t* q, const uint8_t* k, int32_t n_q, int32_t n_k, float* out_f16,
                             float* out_f8, void* stream);
 
+/*
+ * Timing probes (diagnostics).  Each launches one read-only or arithmetic
+ * kernel on `stream` whose only output is one word per thread (XOR of the
+ * data read, or the accumulators), so that a caller can time the shape of
+ * work a hot kernel is built from; `bench.py --probe` prints their tables.
+ * Null or misaligned pointers and sizes outside the stated ranges return
+ * CSA2_EINVAL before any launch; a failed launch returns CSA2_EHIP.
+ *
+ * csa2_probe_scan_read [0539edu §3: the coarse stage streams the 128-byte
+ * E4M3 block summaries of each row]: reads keys [n_rows][n_keys][128] in
+ * chunks of `chunk` keys per 256-thread workgroup (n_rows * ceil(n_keys /
+ * chunk) <= 2^20 workgroups, 16 <= chunk, n_keys <= 2^24), four 16-key tiles
+ * per wave and two groups in flight; full_lines = 0: each lane reads 32
+ * bytes of one key (two loads, each touching half of 16 lines), else each
+ * load reads 8 whole keys; nontemporal != 0: non-temporal loads.  keys
+ * 16-byte aligned; out uint32 [workgroups * 256].
+ *
+ * csa2_probe_mfma_valu: n_wg workgroups of `threads` (256 or 512) threads,
+ * each wave running `iters` x 8 dependent v_mfma_f32_32x32x16_f16 with n_valu
+ * (0, 4, 8, 12 or 16) independent float FMAs after each; iters in [1, 2^20],
+ * n_wg in [1, 65536]; out float [n_wg * threads].
+ *
+ * csa2_probe_gather [0539edu §3: the attention gathers the selected entries,
+ * 256 FP4 code bytes and 32 E4M3 scale bytes each]: n_wg 128-thread
+ * workgroups (at most 65536) walk rows blockIdx, blockIdx + n_wg, ... of ids
+ * [n_rows][512] (clamped into [0, n_ent), n_ent <= 2^31), 32 ids per chunk,
+ * four chunks of loads in flight; whole_lines = 0: the attention kernels'
+ * lane mapping (4 x 16 code bytes and 8 scale bytes of a quarter entry per
+ * lane), else 16 lanes read one entry's 256 code bytes (whole lines) and 4
+ * scale bytes each.  codes [n_ent][256] and scales [n_ent][32] 16-byte
+ * aligned, ids 4-byte aligned; out uint32 [n_wg * 128].
+ */
+int32_t csa2_probe_scan_read(const uint8_t* keys, int32_t n_rows, int32_t n_keys, int32_t chunk, int32_t full_lines,
+                             int32_t nontemporal, uint32_t* out, void* stream);
+int32_t csa2_probe_mfma_valu(int32_t n_valu, int32_t threads, int32_t iters, int32_t n_wg, float* out, void* stream);
+int32_t csa2_probe_gather(const uint8_t* codes, const uint8_t* scales, int64_t n_ent, const int32_t* ids,
+                          int32_t n_rows, int32_t n_wg, int32_t whole_lines, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

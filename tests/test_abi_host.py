@@ -237,3 +237,21 @@ def test_indexer_workspace_passes_without_gpu():
     few = ws(8, 1 << 20)                                      # filter path: candidate area
     assert few >= 8 * (1 << 20) * (4 + 8), few
     assert ws(256, 1 << 20) < 256 * (1 << 20) * 8            # long-row select: no candidate area
+
+
+@needs_lib
+def test_probe_validation_without_gpu():
+    """The timing probes refuse bad sizes and pointers before any launch."""
+    L = C.lib()
+    p = ctypes.c_void_p(4096)                    # aligned, never dereferenced: validation fails first
+    assert L.csa2_probe_scan_read(p, 8, 1024, 8, 1, 1, p, None) == 1          # chunk < 16
+    assert L.csa2_probe_scan_read(None, 8, 1024, 256, 1, 1, p, None) == 1     # keys missing
+    assert L.csa2_probe_scan_read(ctypes.c_void_p(4097), 8, 1024, 256, 1, 1, p, None) == 1   # misaligned
+    assert L.csa2_probe_scan_read(p, 1 << 12, 1 << 24, 16, 1, 1, p, None) == 1   # > 2^20 workgroups
+    assert L.csa2_probe_mfma_valu(5, 256, 16, 1, p, None) == 1                 # FMAs per MFMA not offered
+    assert L.csa2_probe_mfma_valu(4, 128, 16, 1, p, None) == 1                 # 128 threads
+    assert L.csa2_probe_mfma_valu(4, 256, 0, 1, p, None) == 1                  # no iterations
+    assert L.csa2_probe_gather(p, p, 0, p, 4, 1, 1, p, None) == 1              # no entries
+    assert L.csa2_probe_gather(p, None, 16, p, 4, 1, 1, p, None) == 1          # scales missing
+    assert L.csa2_probe_gather(p, p, 16, p, 4, 70000, 1, p, None) == 1         # too many workgroups
+    assert b"probe" in L.csa2_last_error()
