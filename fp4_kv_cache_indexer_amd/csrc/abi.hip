@@ -581,6 +581,7 @@ int32_t run_indexer(const csa2_indexer_args* a, const IndexerPlan& p, char* w, h
   im0.n_seq = a->n_seq;
   im0.row_seq = a->row_seq;
   im0.n_valid = a->n_valid;
+  im0.any = a->q;
   im0.n_ent = a->n_ent;
   im0.n_items = p.items0;
 

@@ -104,12 +104,14 @@ __global__ __launch_bounds__(kTThreads, 2) void sparse_attn_tile_kernel(AttnArgs
   const int h32 = lane >> 5;                   // lane half
   const int l32 = lane & 31;
 
-  const int64_t seq = a.row_seq ? a.row_seq[r] : r;
+  const int32_t w_seq = row_word(a.row_seq, r, a.q), w_len = row_word(a.swa_len, r, a.q),
+                w_st = row_word(a.swa_start, r, a.q);     // loaded together
+  const int64_t seq = a.row_seq ? (int64_t)w_seq : (int64_t)r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;
-  int swl = (a.swa_len && seq_ok) ? a.swa_len[r] : 0;
+  int swl = (a.swa_len && seq_ok) ? w_len : 0;
   swl = max(0, min(swl, a.swa_max));
-  int swst = a.swa_start ? a.swa_start[r] : 0;
+  int swst = a.swa_start ? w_st : 0;
   if (a.swa_cap > 0) { swst %= a.swa_cap; if (swst < 0) swst += a.swa_cap; }
   const int nk = nsel + swl;
   const int k0 = split * a.keys_per_split;

@@ -110,4 +110,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Row r's word of a per-row array, or the discarded stand-in word when the
+// array is absent: the load is unconditional, so a row's words go out
+// together instead of one after another behind branches.
+__device__ __forceinline__ int32_t row_word(const int32_t* arr, int r, const void* any) {
+  return *(arr ? arr + r : static_cast<const int32_t*>(any));
+}
+
 }  // namespace csa2

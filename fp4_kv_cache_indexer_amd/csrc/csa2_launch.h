@@ -32,12 +32,17 @@ enum ItemMode : int32_t {
 };
 
 struct ItemMap {
-  int32_t mode;
-  int64_t n_seq;            // rows whose sequence is outside [0, n_seq) see nothing
+  // A row's two words come from these arrays; the kernels load both at once
+  // and unconditionally, an absent array reading the word at `any` (a
+  // readable address; the value is discarded).  Kept together at the front
+  // so that one scalar load fetches the three pointers.
   const int32_t* row_seq;   // [R] or null (row r reads sequence row_base + r)
-  int64_t row_base;         // first row of this launch among the call's rows
-  int32_t n_items;          // item stride per row (scores row length)
   const int32_t* n_valid;   // [R] or null
+  const void* any;          // readable stand-in address (non-null)
+  int32_t mode;
+  int32_t n_items;          // item stride per row (scores row length)
+  int64_t n_seq;            // rows whose sequence is outside [0, n_seq) see nothing
+  int64_t row_base;         // first row of this launch among the call's rows
   int64_t n_ent;            // default n_valid
   const int32_t* list;      // kept blocks [R][list_len] or cand [R][list_len]
   int32_t list_len;
@@ -126,10 +131,14 @@ hipError_t launch_topk_row(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);
 
 struct AttnArgs {
+  // the per-row arrays (each [R] or null) and Q, whose first word stands in
+  // for an absent row word (a row's words are loaded at once, unconditionally)
+  const int32_t* row_seq;
+  const int32_t* swa_start;
+  const int32_t* swa_len;
+  const uint16_t* q;
   int32_t n_rows, n_heads;
   int64_t n_seq;
-  const int32_t* row_seq;
-  const uint16_t* q;
   const uint8_t* codes;
   const uint8_t* scales;
   int64_t n_ent;
@@ -138,8 +147,6 @@ struct AttnArgs {
   const uint8_t* swa;
   int32_t swa_cap;
   int32_t swa_max;          // window lengths are clamped to this (<= swa_cap)
-  const int32_t* swa_start;
-  const int32_t* swa_len;
   float sm_scale_log2;      // sm_scale * log2(e)
   float* out;
   float* lse;

@@ -14,16 +14,18 @@ namespace csa2 {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
-  return im.row_seq ? (int64_t)im.row_seq[r] : im.row_base + r;
+  const int32_t v = row_word(im.row_seq, r, im.any);
+  return im.row_seq ? (int64_t)v : im.row_base + r;
 }
 
 // Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's
 // sequence is not in the cache.
 __device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r) {
   const int64_t seq = row_seq_of(im, r);
-  if (seq < 0 || seq >= im.n_seq) return 0;
-  const int64_t nv = im.n_valid ? (int64_t)im.n_valid[r] : im.n_ent;
-  return nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
+  const int32_t vn = row_word(im.n_valid, r, im.any);
+  const int64_t nv = im.n_valid ? (int64_t)vn : im.n_ent;
+  const int64_t c = nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
+  return (seq < 0 || seq >= im.n_seq) ? 0 : c;
 }
 
 // Items row walks.  A row that sees no entry (n_valid 0, or a sequence

@@ -171,11 +171,35 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     fused_append_row(a.app, r, threadIdx.x);
     return;
   }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int32_t c0 = (int32_t)blockIdx.x * a.chunk;
+  // Pool and candidate items are looked up in the row's list.  The first
+  // group's lookups go out before the row's sequence and count are known
+  // (clamped to the row's items, unconditional), so the two round trips
+  // overlap.
+  constexpr bool LIST = MODE == kItemsPool || MODE == kItemsCand;
+  const int32_t* lrow = LIST ? a.im.list + (int64_t)r * a.im.list_len : nullptr;
+  int32_t le0[U];
+  if (LIST) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t ic = min(c0 + (wave * U + u) * 16 + n, a.im.n_items - 1);
+      le0[u] = lrow[MODE == kItemsPool ? ic >> 3 : ic];
+    }
+  }
+  // the row's sequence, read (once) before the early exit below
+  const int64_t seq = row_seq_of(a.im, r);
   const int64_t nv = row_valid(a.im, r);
   // items stay below kMaxItems (2^24) per row: 32-bit item arithmetic
   const int32_t n_row = (int32_t)row_items(a.im, nv);
-  const int32_t c0 = (int32_t)blockIdx.x * a.chunk;
-  if (c0 >= n_row) return;                       // uniform for the workgroup
+  if (c0 >= n_row) {                             // uniform for the workgroup
+    if (LIST) {                                  // the lookups stay above the branch
+#pragma unroll
+      for (int u = 0; u < U; ++u) asm volatile("" ::"v"(le0[u]));
+    }
+    return;
+  }
   const int32_t c1 = min(c0 + a.chunk, n_row);
   const bool stage = c1 - c0 <= kScoreStage;     // uniform
   // the block whose summary the row's append refreshes, when this chunk
@@ -190,9 +214,6 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     }
   }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t seq = row_seq_of(a.im, r);
   // lane (n, g) owns channels 32g .. 32g+31 of key n: 32 E4M3 bytes, or 16
   // FP4 code bytes and the scale word (byte g)
   constexpr int kKeyBytes = KF ? kIdxDim / 2 : kIdxDim;
@@ -224,13 +245,34 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // score is masked when written).
   const int32_t ntiles = (c1 - c0 + 15) / 16;
   const int32_t gstride = kScoreWaves * U;
-  const int32_t p0 = (int32_t)item_pos(a.im, r, c0, nv);
-  const int32_t safe_pos = p0 >= 0 ? p0 : 0;
-  auto load_group = [&](int32_t t0, v8i* kb, int32_t* pos) {
+  // Later groups' lookups are likewise issued together before any of their
+  // key loads, so a group costs one lookup round trip -- a lookup behind a
+  // branch, or after the previous tile's key loads, would wait for every
+  // load issued before it.  Invisible list items read position 0.
+  const int32_t safe_pos = LIST ? 0 : c0;
+  auto load_group = [&](int32_t t0, v8i* kb, int32_t* pos, const int32_t* pre) {
+    if (LIST) {
+      int32_t le[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t ic = min(c0 + (t0 + u) * 16 + n, c1 - 1);
+        le[u] = pre ? pre[u] : lrow[MODE == kItemsPool ? ic >> 3 : ic];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t item = c0 + (t0 + u) * 16 + n;
+        const int64_t pp = MODE == kItemsPool ? (int64_t)le[u] * kBlockPos + (item & 7) : (int64_t)le[u];
+        pos[u] = (item < c1 && le[u] >= 0 && pp < nv) ? (int32_t)pp : -1;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t item = c0 + (t0 + u) * 16 + n;
+        pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int32_t item = c0 + (t0 + u) * 16 + n;
-      pos[u] = (item < c1) ? (int32_t)item_pos(a.im, r, item, nv) : -1;
       const uint64_t p = (uint32_t)(pos[u] >= 0 ? pos[u] : safe_pos);
       if (KF) {
         constexpr bool NT = MODE != 0;
@@ -284,7 +326,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   };
   // a store at an offset past the row's buffer is dropped by the hardware
   const auto srows = __builtin_amdgcn_make_buffer_rsrc(srow, 0, (int)((int64_t)n_row * 4), 0x00020000);
-  auto compute_group = [&](int32_t t0, v8i* kb) {
+  auto compute_group = [&](int32_t t0, v8i* kb, const int32_t* pos) {
     if (FULL) stage_group(kb);
     if (APP && sp >= 0) {                        // uniform: the refreshed block's key from LDS
 #pragma unroll
@@ -328,7 +370,13 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       const float sc = half_pair_sum(k0, k1);
       const int32_t item = c0 + (t0 + u4 + g) * 16 + n;
       const bool in = item < c1;
-      const bool vis = in && item_pos(a.im, r, item, nv) >= 0;
+      bool vis;
+      if (LIST) {                                // this lane's looked-up position (-1 past the chunk)
+        const int32_t pg = g == 0 ? pos[u4] : g == 1 ? pos[u4 + 1] : g == 2 ? pos[u4 + 2] : pos[u4 + 3];
+        vis = pg >= 0;
+      } else {
+        vis = in && item_pos(a.im, r, item, nv) >= 0;
+      }
       const float out = vis ? sc : __uint_as_float(0x7FC00000u);   // NaN: not visible
       if (stage) {                               // uniform
         int si = in ? item - c0 : kScoreStage + (int)threadIdx.x;
@@ -350,7 +398,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   // Group loads are unconditional (tiles past the chunk read a visible key
   // and are discarded): a load on one side of a branch makes the compiler's
   // later waits cover it, which would serialise the double buffer.
-  if (G > 0 || DB) load_group(t0, kA, pA);
+  if (G > 0 || DB) load_group(t0, kA, pA, le0);
   __builtin_amdgcn_sched_barrier(0);             // the key loads go out first
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -365,28 +413,28 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
     for (int i = 0; i < G; ++i) {
       const int32_t ti = t0 + i * gstride;
       if (i + 1 < G) {
-        if (i & 1) load_group(ti + gstride, kA, pA); else load_group(ti + gstride, kB, pB);
+        if (i & 1) load_group(ti + gstride, kA, pA, nullptr); else load_group(ti + gstride, kB, pB, nullptr);
       }
       // keep the next group's loads above this group's arithmetic
       __builtin_amdgcn_sched_barrier(0);
-      if (i & 1) compute_group(ti, kB); else compute_group(ti, kA);
+      if (i & 1) compute_group(ti, kB, pB); else compute_group(ti, kA, pA);
     }
   } else if (DB) {
     // two groups per trip and no exit between them (a group past the chunk
     // is computed and discarded): one loop shape keeps the waits exact
     for (; t0 < ntiles; t0 += 2 * gstride) {
       const int32_t t1 = t0 + gstride;
-      load_group(t1, kB, pB);
+      load_group(t1, kB, pB, nullptr);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group(t0, kA);
-      load_group(t1 + gstride, kA, pA);
+      compute_group(t0, kA, pA);
+      load_group(t1 + gstride, kA, pA, nullptr);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group(t1, kB);
+      compute_group(t1, kB, pB);
     }
   } else {
     for (; t0 < ntiles; t0 += gstride) {
-      load_group(t0, kA, pA);
-      compute_group(t0, kA);
+      load_group(t0, kA, pA, nullptr);
+      compute_group(t0, kA, pA);
     }
   }
   lds_barrier();

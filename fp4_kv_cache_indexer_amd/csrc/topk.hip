@@ -40,11 +40,25 @@ __device__ __forceinline__ float comp_score(uint64_t K) { return order_key_inv((
 // Branch-free: an in-bounds float4 load (the row's stride is a multiple of 4
 // and i0 is too) with lanes past the row's items set to NaN.  A branch around
 // a tail path would make the compiler wait for each load before the next.
-__device__ __forceinline__ float4 load_items4(const float* srow, int64_t i0, int64_t n_row, int64_t stride) {
-  const float4 t = *reinterpret_cast<const float4*>(srow + (i0 < stride ? i0 : 0));
+__device__ __forceinline__ float4 load_items4_raw(const float* srow, int64_t i0, int64_t stride) {
+  return *reinterpret_cast<const float4*>(srow + (i0 < stride ? i0 : 0));
+}
+__device__ __forceinline__ float4 mask_items4(float4 t, int64_t i0, int64_t n_row) {
   const float nan = __uint_as_float(0x7FC00000u);
   return make_float4(i0 + 0 < n_row ? t.x : nan, i0 + 1 < n_row ? t.y : nan,
                      i0 + 2 < n_row ? t.z : nan, i0 + 3 < n_row ? t.w : nan);
+}
+
+// On a path that discards loads issued above it (an early exit), mark them
+// used there, so that the compiler cannot sink them below the branch into
+// the path that uses them (where they would wait for the row's other loads
+// before going out).
+template <int N, int M>
+__device__ __forceinline__ void keep_loads_above(const float4 (&v)[N], const uint32_t (&h)[M]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(v[i].x));
+#pragma unroll
+  for (int i = 0; i < M; ++i) asm volatile("" ::"v"(h[i]));
 }
 
 template <int NT>
@@ -244,23 +258,31 @@ __global__ __launch_bounds__(kFiltThreads) void topk_filter_kernel(SelectArgs a)
   __shared__ int wsum[2][kFiltThreads / 64];
   __shared__ int thr[4];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = row_valid(a.im, r);
-  const int64_t n_row = row_items(a.im, nv);
   const int64_t c0 = (int64_t)c * kFiltChunk;
-  if (c0 >= n_row) return;                                     // uniform
-  const int64_t c1 = min(c0 + (int64_t)kFiltChunk, n_row);
 
-  // this thread's items and its bins, loaded before the threshold search
+  // this thread's items and its bins, loaded first: their addresses do not
+  // depend on the row's sequence and count, whose loads then overlap them
   const float* srow = a.scores + (int64_t)r * a.row_stride;
   const int64_t i0 = c0 + (int64_t)kFiltPer * tid;
+  float4 raw[kFiltPer / 4];
+#pragma unroll
+  for (int u = 0; u < kFiltPer / 4; ++u) raw[u] = load_items4_raw(srow, i0 + 4 * u, a.row_stride);
+  uint32_t hv[kHistBins / kFiltThreads];
+  hist_load_desc<kFiltThreads>(a.hist + (int64_t)r * kHistBins, hv);
+
+  const int64_t nv = row_valid(a.im, r);
+  const int64_t n_row = row_items(a.im, nv);
+  if (c0 >= n_row) {                                           // uniform
+    keep_loads_above(raw, hv);
+    return;
+  }
+  const int64_t c1 = min(c0 + (int64_t)kFiltChunk, n_row);
   float v[kFiltPer];
 #pragma unroll
   for (int u = 0; u < kFiltPer / 4; ++u) {
-    const float4 q = load_items4(srow, i0 + 4 * u, c1, a.row_stride);
+    const float4 q = mask_items4(raw[u], i0 + 4 * u, c1);
     v[4 * u] = q.x; v[4 * u + 1] = q.y; v[4 * u + 2] = q.z; v[4 * u + 3] = q.w;
   }
-  uint32_t hv[kHistBins / kFiltThreads];
-  hist_load_desc<kFiltThreads>(a.hist + (int64_t)r * kHistBins, hv);
   const RowThreshold th = dpp_threshold<kFiltThreads>(hv, a.k, wsum[0], thr);
 
   // compaction in item order
@@ -450,17 +472,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
   RegRowShared& shr = *reinterpret_cast<RegRowShared*>(reg_row_smem);
   RegShared& sh = shr.reg;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = row_valid(a.im, r);
-  const int n_row = (int)row_items(a.im, nv);
-  int32_t* oi = a.out_idx + (int64_t)r * a.k;
-  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
-  if (n_row == 0) {                                            // uniform: nothing visible
-    for (int j = tid; j < a.k; j += kRegThreads) {
-      oi[j] = -1;
-      if (os) os[j] = 0.0f;
-    }
-    return;
-  }
+  // the row's bins, scores and (pool) block ids first: their addresses do
+  // not depend on the row's sequence and count, whose loads then overlap them
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
   uint32_t hv[kHistBins / kRegThreads];
   hist_load_desc<kRegThreads>(gh, hv);
@@ -477,6 +490,19 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
     const int32_t* lrow = a.im.list + (int64_t)r * a.im.list_len;
     blk[0] = lrow[min(2 * tid, a.im.list_len - 1)];
     blk[1] = lrow[min(2 * tid + 1, a.im.list_len - 1)];
+  }
+  const int64_t nv = row_valid(a.im, r);
+  const int n_row = (int)row_items(a.im, nv);
+  int32_t* oi = a.out_idx + (int64_t)r * a.k;
+  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
+  if (n_row == 0) {                                            // uniform: nothing visible
+    keep_loads_above(v, hv);
+    asm volatile("" ::"v"(blk[0]), "v"(blk[1]));
+    for (int j = tid; j < a.k; j += kRegThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.0f;
+    }
+    return;
   }
   if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
   const RowThreshold th = dpp_threshold<kRegThreads>(hv, a.k, sh.wsum[0], sh.thr);   // its barriers order the zeroing too
