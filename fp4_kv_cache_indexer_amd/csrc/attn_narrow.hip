@@ -49,7 +49,7 @@ struct NarrowShared {
   float mx[2][kHeads];                         // the two key halves' chunk maxima
   float lsum[2][kHeads];                       // the two key halves' weight sums
   int32_t kvalid[kChunk];
-  int32_t sidx[kMaxSplitKeys];
+  int32_t sidx[kMaxSplitKeys + 1];             // + a slot for threads that stage no id
 };
 
 // The raw bytes one thread gathers for its key and 32 channels of a chunk:
@@ -80,8 +80,9 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
   const int n = lane & 15, g = lane >> 4;
   const int hbase = hg * kHeads;
 
-  const int32_t w_seq = row_word(a.row_seq, r, a.q), w_len = row_word(a.swa_len, r, a.q),
-                w_st = row_word(a.swa_start, r, a.q);     // loaded together
+  int32_t w_seq, w_len, w_st;                    // loaded together
+  scalar_words3(row_word_ptr(a.row_seq, r, a.q), row_word_ptr(a.swa_len, r, a.q), row_word_ptr(a.swa_start, r, a.q),
+                w_seq, w_len, w_st);
   const int64_t seq = a.row_seq ? (int64_t)w_seq : (int64_t)r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;
@@ -99,15 +100,25 @@ __global__ __launch_bounds__(kThreads, 4) void sparse_attn_narrow_kernel(AttnArg
   const uint8_t* swa_s = a.swa ? a.swa + (seq_ok ? seq : 0) * (int64_t)a.swa_cap * kD : nullptr;
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q + (int64_t)r * H * kD);   // readable, discarded
 
-  // stage the split's selected ids and the group's Q; all loads fly together
+  // stage the split's selected ids (one per thread; a split without any
+  // reads Q's first word) and the group's Q: all loads go out before the
+  // first LDS write waits for them
+  static_assert(kMaxSplitKeys <= kThreads, "one staged id per thread");
+  constexpr int kQPer = kHeads * kRow / 16 / kThreads;  // 16-byte Q units per thread
   const int nst = max(0, min(k0 + a.keys_per_split, a.top_k) - k0);
-  for (int i = tid; i < nst; i += kThreads) sh.sidx[i] = idxr[k0 + i];
+  const int32_t id_v = *(nst > 0 ? idxr + k0 + min(tid, nst - 1) : reinterpret_cast<const int32_t*>(a.q));
+  uint4 qv[kQPer];
 #pragma unroll
-  for (int i = 0; i < kHeads * kRow / 16 / kThreads; ++i) {
+  for (int i = 0; i < kQPer; ++i) {
     const int u = i * kThreads + tid;              // 16-byte unit: head u/64, segment u%64
+    qv[i] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)r * H + hbase + (u >> 6)) * kD + (u & 63) * 8);
+  }
+  sh.sidx[tid < nst ? tid : kMaxSplitKeys] = id_v;   // no branch for the Q loads to sink below
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int u = i * kThreads + tid;
     const int h = u >> 6, seg = u & 63;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)r * H + hbase + h) * kD + seg * 8);
-    *reinterpret_cast<uint4*>(sh.q + h * kRow + ((seg ^ tile_sw(h)) << 4)) = v;
+    *reinterpret_cast<uint4*>(sh.q + h * kRow + ((seg ^ tile_sw(h)) << 4)) = qv[i];
   }
   float m_run = -INFINITY, l_run = 0.0f;            // waves 0, 1: head n, own key half
   v4f acc[kTilesPerWave];

@@ -104,8 +104,9 @@ __global__ __launch_bounds__(kTThreads, 2) void sparse_attn_tile_kernel(AttnArgs
   const int h32 = lane >> 5;                   // lane half
   const int l32 = lane & 31;
 
-  const int32_t w_seq = row_word(a.row_seq, r, a.q), w_len = row_word(a.swa_len, r, a.q),
-                w_st = row_word(a.swa_start, r, a.q);     // loaded together
+  int32_t w_seq, w_len, w_st;
+  scalar_words3(row_word_ptr(a.row_seq, r, a.q), row_word_ptr(a.swa_len, r, a.q), row_word_ptr(a.swa_start, r, a.q),
+                w_seq, w_len, w_st);
   const int64_t seq = a.row_seq ? (int64_t)w_seq : (int64_t)r;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   const int nsel = seq_ok ? a.top_k : 0;

@@ -113,8 +113,31 @@ __device__ __forceinline__ void lds_barrier() {
 // Row r's word of a per-row array, or the discarded stand-in word when the
 // array is absent: the load is unconditional, so a row's words go out
 // together instead of one after another behind branches.
-__device__ __forceinline__ int32_t row_word(const int32_t* arr, int r, const void* any) {
-  return *(arr ? arr + r : static_cast<const int32_t*>(any));
+__device__ __forceinline__ const int32_t* row_word_ptr(const int32_t* arr, int r, const void* any) {
+  return arr ? arr + r : static_cast<const int32_t*>(any);
+}
+
+// Two (three) uniform words through the scalar cache, issued back to back
+// and waited for once, in one asm block (the compiler would otherwise wait
+// for the first before issuing the second).  The addresses must be uniform
+// and readable.
+__device__ __forceinline__ void scalar_words2(const int32_t* p0, const int32_t* p1, int32_t& v0, int32_t& v1) {
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1)
+      : "s"(p0), "s"(p1));
+}
+__device__ __forceinline__ void scalar_words3(const int32_t* p0, const int32_t* p1, const int32_t* p2, int32_t& v0,
+                                              int32_t& v1, int32_t& v2) {
+  asm volatile(
+      "s_load_dword %0, %3, 0x0\n\t"
+      "s_load_dword %1, %4, 0x0\n\t"
+      "s_load_dword %2, %5, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2)
+      : "s"(p0), "s"(p1), "s"(p2));
 }
 
 }  // namespace csa2

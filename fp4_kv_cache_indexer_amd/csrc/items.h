@@ -14,15 +14,16 @@ namespace csa2 {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
-  const int32_t v = row_word(im.row_seq, r, im.any);
-  return im.row_seq ? (int64_t)v : im.row_base + r;
+  return im.row_seq ? (int64_t)im.row_seq[r] : im.row_base + r;
 }
 
 // Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's
 // sequence is not in the cache.
-__device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r) {
-  const int64_t seq = row_seq_of(im, r);
-  const int32_t vn = row_word(im.n_valid, r, im.any);
+__device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r, int64_t* seq_out = nullptr) {
+  int32_t vs, vn;
+  scalar_words2(row_word_ptr(im.row_seq, r, im.any), row_word_ptr(im.n_valid, r, im.any), vs, vn);
+  const int64_t seq = im.row_seq ? (int64_t)vs : im.row_base + r;
+  if (seq_out) *seq_out = seq;
   const int64_t nv = im.n_valid ? (int64_t)vn : im.n_ent;
   const int64_t c = nv < 0 ? 0 : (nv > im.n_ent ? im.n_ent : nv);
   return (seq < 0 || seq >= im.n_seq) ? 0 : c;

@@ -188,9 +188,8 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
       le0[u] = lrow[MODE == kItemsPool ? ic >> 3 : ic];
     }
   }
-  // the row's sequence, read (once) before the early exit below
-  const int64_t seq = row_seq_of(a.im, r);
-  const int64_t nv = row_valid(a.im, r);
+  int64_t seq;
+  const int64_t nv = row_valid(a.im, r, &seq);
   // items stay below kMaxItems (2^24) per row: 32-bit item arithmetic
   const int32_t n_row = (int32_t)row_items(a.im, nv);
   if (c0 >= n_row) {                             // uniform for the workgroup

@@ -592,7 +592,8 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_row_kernel(SelectArgs a)
 // candidate order is ascending position) and writes the kept ones in that
 // order; candidate mode (caller lists in any order) sorts them by position
 // in LDS first.  Thread t speculatively loads 8 candidate slots of chunk
-// t / TPC (TPC threads per chunk) before the chunks' counts are known; when
+// t / TPC (TPC threads per chunk, from the launch's chunk count) before the
+// chunks' counts are known; when
 // no chunk holds more candidates than its threads' slots, the keys are then
 // in registers (slots past a chunk's count are masked).  Otherwise (wide
 // ties) the same steps walk every chunk's candidates in global memory,
@@ -626,24 +627,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
   __shared__ SelShared shs;
   RegShared& sh = shs.reg;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = row_valid(a.im, r);
-  const int64_t n_row = row_items(a.im, nv);
-  int32_t* oi = a.out_idx + (int64_t)r * a.k;
-  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
-  if (n_row == 0) {                                            // uniform: nothing visible
-    for (int j = tid; j < a.k; j += kSelThreads) {
-      oi[j] = -1;
-      if (os) os[j] = 0.0f;
-    }
-    return;
-  }
-  const bool sort = a.im.mode == kItemsCand;
-  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);
-  const int tpc = min(kFiltChunk / kSelNK, kSelThreads / nch);  // 0 when there are more chunks than threads
+  // The row's bins, chunk counts and candidate slots go out first: their
+  // addresses do not depend on the row's words, whose loads then overlap
+  // them.  The slots are mapped for the launch's chunk count, TPC threads of
+  // kSelNK slots per chunk (a row with fewer chunks leaves the threads past
+  // its chunks idle; a chunk with more candidates than its slots takes the
+  // walk over global memory below).
   uint32_t* gh = a.hist + (int64_t)r * kHistBins;
   uint32_t hv[kHistBins / kSelThreads];
   hist_load_desc<kSelThreads>(gh, hv);
-  const int c = tpc > 0 ? min(tid / tpc, nch - 1) : 0;           // threads past the chunks repeat the last
+  const int tpc = min(kFiltChunk / kSelNK, kSelThreads / a.n_chunks);  // 0 when there are more chunks than threads
+  const int c = tpc > 0 ? min(tid / tpc, a.n_chunks - 1) : 0;
   const int s0 = tpc > 0 ? kSelNK * (tid % tpc) : 0;
   const int cnt = (int)a.cand_count[(int64_t)r * a.n_chunks + c];
   const uint64_t* crow = a.cand + ((int64_t)r * a.n_chunks + c) * kFiltChunk + s0;
@@ -654,6 +648,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectArgs a) 
     K[i] = ((uint64_t)q.y << 32) | q.x;
     K[i + 1] = ((uint64_t)q.w << 32) | q.z;
   }
+  const int64_t nv = row_valid(a.im, r);
+  const int64_t n_row = row_items(a.im, nv);
+  int32_t* oi = a.out_idx + (int64_t)r * a.k;
+  float* os = a.out_score ? a.out_score + (int64_t)r * a.k : nullptr;
+  if (n_row == 0) {                                            // uniform: nothing visible
+#pragma unroll
+    for (int i = 0; i < kSelNK; ++i) asm volatile("" ::"v"(K[i]));   // the loads stay above the branch
+#pragma unroll
+    for (int i = 0; i < kHistBins / kSelThreads; ++i) asm volatile("" ::"v"(hv[i]));
+    asm volatile("" ::"v"(cnt));
+    for (int j = tid; j < a.k; j += kSelThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.0f;
+    }
+    return;
+  }
+  const bool sort = a.im.mode == kItemsCand;
+  const int nch = (int)((n_row + kFiltChunk - 1) / kFiltChunk);   // the row's chunks (<= a.n_chunks)
   if (tid < 256) { sh.h[0][tid] = 0u; sh.h[1][tid] = 0u; }
   if (tid == 0) sh.flag = tpc > 0 ? 0 : 1;
   lds_barrier();
