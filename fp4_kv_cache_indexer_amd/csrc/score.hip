@@ -111,6 +111,19 @@ __device__ __forceinline__ float half_pair_sum(float x, float y) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Adds a workgroup's LDS histogram (kHistBins counts, 8-byte aligned) into
+// the row's histogram in memory: two adjacent bins per 64-bit atomic add
+// (the low word is the even bin; no count reaches 2^32, so no carry crosses
+// into the odd one), half the atomics of one per bin, for the pairs that
+// counted anything.  Every workgroup of a row adds into the same words.
+__device__ __forceinline__ void flush_hist(const uint32_t* lh, uint32_t* gh) {
+  unsigned long long* g2 = reinterpret_cast<unsigned long long*>(gh);
+  for (int b = threadIdx.x; b < kHistBins / 2; b += blockDim.x) {
+    const uint2 c = *reinterpret_cast<const uint2*>(lh + 2 * b);
+    if (c.x | c.y) atomicAdd(g2 + b, ((unsigned long long)c.y << 32) | c.x);
+  }
+}
+
 // The append of one row inside the coarse scan's launch (its last column),
 // for the (m, gate) forms a decode step uses.
 __device__ __forceinline__ void fused_append_row(const AppendArgs& ap, int r, int t) {
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   constexpr bool FULL = !KF && MODE == kItemsBlocks;
   // the histogram and the staged scores, each followed by one word per
   // thread for the lanes that count or stage nothing (no branch)
-  __shared__ uint32_t hist[kHistBins + kScoreThreads];
+  __shared__ __align__(8) uint32_t hist[kHistBins + kScoreThreads];
   __shared__ float sscore[kScoreStage + kScoreThreads];
   __shared__ __align__(16) uint8_t sp_key[APP ? kIdxDim : 16];
   // staged keys pass through a wave-private buffer of two 16-key tiles
@@ -439,11 +452,7 @@ __global__ __launch_bounds__(kScoreThreads, MINW) void index_score_kernel(ScoreA
   lds_barrier();
   if (stage)
     for (int32_t i = threadIdx.x; i < c1 - c0; i += kScoreThreads) srow[c0 + i] = sscore[i];
-  uint32_t* ghist = a.hist + (int64_t)r * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
-    const uint32_t c = hist[b];
-    if (c) atomicAdd(&ghist[b], c);
-  }
+  flush_hist(hist, a.hist + (int64_t)r * kHistBins);
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +477,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
   static_assert(U == 2 || U == 4, "16-item tiles per group: 2 or 4");
   // the rows' histograms, then one word per thread for the counts of lanes
   // that count nothing (the epilogue has no branch)
-  __shared__ uint32_t hist[RG * kHistBins + kScoreThreads];
+  __shared__ __align__(8) uint32_t hist[RG * kHistBins + kScoreThreads];
   const int rbase = blockIdx.y * RG;
   // item counts stay below kMaxItems (2^24): 32-bit indices
   int32_t nv[RG];
@@ -600,11 +609,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
 #pragma unroll
   for (int i = 0; i < RG; ++i) {
     if (rbase + i >= a.n_rows) break;            // uniform
-    uint32_t* ghist = a.hist + (int64_t)(rbase + i) * kHistBins;
-    for (int b = threadIdx.x; b < kHistBins; b += kScoreThreads) {
-      const uint32_t c = hist[i * kHistBins + b];
-      if (c) atomicAdd(&ghist[b], c);
-    }
+    flush_hist(hist + i * kHistBins, a.hist + (int64_t)(rbase + i) * kHistBins);
   }
 }
 
