@@ -9,8 +9,10 @@ window attention (sparse_attn_decode).  Inputs are seeded synthetic data,
 resident in HBM before the timed region; several independent input sets are
 rotated so the working set exceeds the 256 MB Infinity Cache.
 
-The timed region replays one captured HIP graph per input set (the form a
-serving loop would run).  (Running the cache append on a second stream,
+The timed region replays captured HIP graphs that each hold four consecutive
+steps (one per input set), as the graph of a model step holds the hot path of
+many layers; the same steps replayed as one graph per step are timed as well
+and reported beside it (each graph launch adds a few microseconds).  (Running the cache append on a second stream,
 joined before the attention, was measured slower inside the graph: about
 13 us per step more for 3-5 us of overlapped work.)  An equal eager pass afterwards times the dominant
 kernel (the coarse indexer scan) with HIP events recorded by the library on
@@ -844,6 +846,9 @@ def main():
     ap.add_argument("--sites", action="store_true",
                     help="also print the event-timed average duration of every launch site")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--graph-steps", type=int, default=4,
+                    help="steps per replayed graph in the timed region (1: one graph launch per step; "
+                         "with more, the same steps with one launch each are timed too and reported)")
     ap.add_argument("--attn-plan", metavar="HPW,NS", default=None,
                     help="pin the attention geometry: heads per workgroup (16 or 64) and key splits")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -913,21 +918,51 @@ def main():
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
+    # --graph-steps G: the timed region replays graphs that each hold G
+    # consecutive steps (over the input sets in turn), as a model step's
+    # graph holds the hot path of many layers; G = 1 launches one graph per
+    # step.  K steps are floor(K / G) replays of the G-step graph and K mod G
+    # replays of single-step graphs.
+    gsteps = max(1, args.graph_steps) if graphs else 1
+    multi = None
+    if gsteps > 1:
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi):
+            for j in range(gsteps):
+                step_fn(w, sets[j % len(sets)])
+        for _ in range(2):
+            multi.replay()
+        torch.cuda.synchronize()
+        for s, (ri, ro) in zip(sets, ref):          # the last step of each set still matches its eager step
+            if not (torch.equal(s.idx, ri) and torch.equal(s.out, ro)):
+                raise RuntimeError("multi-step graph replay differs from the eager step")
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            step_fn(w, sets[i % len(sets)])
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
+    def timed_steps(g_steps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        if g_steps > 1:
+            for i in range(args.steps // g_steps):
+                multi.replay()
+        for i in range(args.steps % g_steps if g_steps > 1 else args.steps):
+            if graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                step_fn(w, sets[i % len(sets)])
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+    one_graph = None
+    if gsteps > 1:                     # the same K steps, one graph launch each, for reference
+        ms1 = timed_steps(1)
+        one_graph = {"ms_per_step": round(ms1 / args.steps, 5),
+                     "value": round(w["B"] * args.steps / (ms1 / 1e3), 1)}
+        print(f"[bench] one graph per step: {ms1 / args.steps * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    ms = timed_steps(gsteps)
     ms_step = ms / args.steps
     qps = w["B"] * args.steps / (ms / 1e3)
-    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {qps:.0f} queries/s",
+    print(f"[bench] timed {args.steps} steps ({gsteps} per graph): {ms_step * 1e3:.1f} us/step, {qps:.0f} queries/s",
           file=sys.stderr, flush=True)
 
     # the distribution of single steps (a separate pass: an event pair around
@@ -995,7 +1030,7 @@ def main():
                    "entries_per_seq": w["N"], "heads": w["H"], "top_k": w["k"],
                    "keep_blocks": w["keep"], "swa_window": 128, "input_sets_rotated": len(sets),
                    "layers": ("40-layer CSA2 schedule" if w.get("sched") else "/".join(layers_of(w))),
-                   "timed": "graph replays" if graphs else "eager launches"},
+                   "timed": (f"graph replays, {gsteps} steps per graph" if graphs else "eager launches")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": f"index_score_kernel ({site})", "avg_us": round(avg_s * 1e6, 3),
@@ -1006,6 +1041,8 @@ def main():
                           "flops_per_launch": attn_flops(w)},
         "cpu_baseline": None,
     }
+    if one_graph is not None:
+        res["one_graph_per_step"] = one_graph
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = (cpu_baseline_sched(w, args.cpu_seconds) if w.get("sched")
                                else cpu_baseline(w, sets[0], args.cpu_seconds))
