@@ -319,6 +319,17 @@ def test_indexer_flat_long_rows():
     check_flat_rows(case, gi, gsc, 2048)
 
 
+def test_indexer_flat_long_rows_mixed_lengths():
+    """The filter + select path with rows of very different lengths in one
+    call: the select maps its candidate slots by the launch's chunk count
+    (74 here), so a 10-chunk row leaves most threads idle, and a row that
+    sees nothing writes -1."""
+    say("indexer flat N=300000 R=3 k=2048, n_valid 300000 / 40000 / 0")
+    case = idx_case(13, 1, 300000, 3, row_seq=np.array([0, 0, 0]), n_valid=np.array([300000, 40000, 0]))
+    gi, gsc = run_indexer(case, 2048)
+    check_flat_rows(case, gi, gsc, 2048)
+
+
 def test_indexer_block_pool():
     """Block-pool mode: select among the positions of given blocks (ascending
     lists with -1 holes and blocks past n_valid), ragged rows."""
