@@ -12,9 +12,10 @@ rotated so the working set exceeds the 256 MB Infinity Cache.
 The timed region replays captured HIP graphs that each hold four consecutive
 steps (one per input set), as the graph of a model step holds the hot path of
 many layers; the same steps replayed as one graph per step are timed as well
-and reported beside it (each graph launch adds a few microseconds).  (Running the cache append on a second stream,
-joined before the attention, was measured slower inside the graph: about
-13 us per step more for 3-5 us of overlapped work.)  An equal eager pass afterwards times the dominant
+and reported beside it (each graph launch adds a few microseconds).
+(Running the cache append on a second stream, joined before the attention,
+was measured slower inside the graph: about 13 us per step more for 3-5 us
+of overlapped work.)  An equal eager pass afterwards times the dominant
 kernel (the coarse indexer scan) with HIP events recorded by the library on
 the kernel's own stream; that duration gives the roofline line.  The
 cpu_baseline leg times the oracle on a bounded sample of the same workload.
