@@ -13,12 +13,9 @@ namespace csa2 {
 // item <-> position mapping
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int64_t row_seq_of(const ItemMap& im, int r) {
-  return im.row_seq ? (int64_t)im.row_seq[r] : im.row_base + r;
-}
-
 // Entries visible to row r: n_valid clamped to [0, n_ent]; none if the row's
-// sequence is not in the cache.
+// sequence (row_seq[r], or row_base + r) is not in the cache.  The row's
+// sequence goes to *seq_out when asked for.
 __device__ __forceinline__ int64_t row_valid(const ItemMap& im, int r, int64_t* seq_out = nullptr) {
   int32_t vs, vn;
   scalar_words2(row_word_ptr(im.row_seq, r, im.any), row_word_ptr(im.n_valid, r, im.any), vs, vn);
