@@ -79,6 +79,11 @@ hipError_t timed(int32_t site, hipStream_t s, F f) {
 // against 1.029 ms; one 16-head row keeps its 10 splits (10 workgroups).
 #define CSA2_ATTN_CUS 256
 #define CSA2_NARROW_CU_SPLIT_KEYS 96
+// 64-head splits take at least this many keys (four chunks: the pipeline's
+// depth).  Measured on 32 rows x 64 heads x 640 keys: 5 splits of 128 keys
+// against 7 of 96, step 110.6 against 112.6 us (the combine reads fewer
+// partials); 64 rows keep 4 splits of 160.
+#define CSA2_WIDE_MIN_SPLIT_KEYS 128
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -261,6 +266,7 @@ int32_t check_attn(const csa2_attn_args* a, AttnPlan* p, bool check_ptrs) {
   const int64_t hg = (a->n_heads + p->heads_per_wg - 1) / p->heads_per_wg;
   const int64_t wgs = (int64_t)a->n_rows * hg;
   int64_t ns = wgs > 0 ? (256 + wgs - 1) / wgs : 1;
+  if (p->heads_per_wg == 64) ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / CSA2_WIDE_MIN_SPLIT_KEYS));
   if (p->heads_per_wg == 16) {
     // as many splits as run at once, but no more workgroups than compute
     // units where splits of up to three chunks already fill them
