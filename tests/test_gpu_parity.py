@@ -696,6 +696,34 @@ def test_attn_no_keys():
     assert np.all(out == 0) and np.all(lse == -np.inf)
 
 
+def test_empty_inputs():
+    """Zero rows through every entry point and zero tokens through the cache
+    write: each call succeeds, launches nothing and returns empty outputs
+    (the host returns before validating pointers, which empty tensors leave
+    NULL)."""
+    say("zero rows: indexer flat/hierarchical/static, attention, append; zero tokens: cache write")
+    N = 4096
+    keys = torch.zeros((1, N, 128), dtype=torch.uint8, device="cuda")
+    bkeys = torch.zeros((1, N // 8, 128), dtype=torch.uint8, device="cuda")
+    q0 = torch.zeros((0, 32, 128), dtype=torch.uint8, device="cuda")
+    assert tuple(C.indexer_topk(q0, keys, 512).shape) == (0, 512)
+    assert tuple(C.indexer_topk(q0, keys, 512, block_keys=bkeys, keep_blocks=64).shape) == (0, 512)
+    assert tuple(C.indexer_topk_static(q0, keys, 512).shape) == (0, 512)
+    codes = torch.zeros((1, N, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((1, N, 32), dtype=torch.uint8, device="cuda")
+    qa = torch.zeros((0, 64, 512), dtype=torch.bfloat16, device="cuda")
+    out, lse = C.sparse_attn_decode(qa, codes, scales, torch.zeros((0, 512), dtype=torch.int32, device="cuda"))
+    assert tuple(out.shape) == (0, 64, 512) and tuple(lse.shape) == (0, 64)
+    C.decode_append(torch.zeros((0, 512), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((0,), dtype=torch.int64, device="cuda"), codes, scales,
+                    torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda"), keys)
+    x0 = torch.zeros((1, 0, 512), dtype=torch.bfloat16, device="cuda")
+    c0, s0 = C.kv_compress_quantize(x0, 2)
+    assert tuple(c0.shape) == (1, 0, 256) and tuple(s0.shape) == (1, 0, 32)
+    torch.cuda.synchronize()
+    assert torch.all(codes == 0) and torch.all(keys == 0)   # nothing was written
+
+
 # ---------------------------------------------------------------------------
 # layer groups and prefill rows
 # ---------------------------------------------------------------------------
