@@ -413,6 +413,10 @@ __global__ __launch_bounds__(kTThreads, 2) void sparse_attn_tile_kernel(AttnArgs
   // others'.
   const int64_t rh0 = (int64_t)r * H + hbase;
   if (qk_wave) {
+    // the score wave shares its SIMD with a dequantising wave: issuing at a
+    // raised priority keeps its dependent MFMA chain from waiting behind
+    // the other wave's vector instructions
+    __builtin_amdgcn_s_setprio(3);
     // score waves: Q of head tile `wave` (head 32*wave + l32), channels
     // 16ks + 8*h32 .. +8 for ks < 32, scaled by a power of two into fp16.
     // The tile's 32 rows (32 KB, contiguous) come in with one 1 KB row per
