@@ -541,7 +541,11 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
   const auto srows = __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)rbase * a.row_stride, 0,
                                                        (int)((int64_t)RG * a.row_stride * 4), 0x00020000);
 
+  // The two waves of a SIMD alternate: the one in its MFMA phase issues at a
+  // raised priority, and the other's epilogue (transposes, stores, histogram
+  // atomics) fills the issue slots between its MFMAs.
   auto compute_group = [&](int32_t tg, const v8i* kb) {
+    __builtin_amdgcn_s_setprio(1);
     float p[RG][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -565,6 +569,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
         p[i][u] = sp;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // per row, the transpose-reduce of index_score_kernel: lane (n, g) ends
     // with the score of tile g (U = 4) or g & 1 (U = 2, lanes g >= 2 hold a
     // copy and store nothing), entry n; the adds pair the head groups as
