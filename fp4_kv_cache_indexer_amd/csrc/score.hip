@@ -595,7 +595,9 @@ __global__ __launch_bounds__(kScoreThreads, 2) void index_score_rows_kernel(Scor
       int off = own ? 4 * item + i * 4 * a.row_stride : INT32_MAX;
       uint32_t bin = own ? (uint32_t)(i * kHistBins) + (ok >> (32 - kHistBits)) : (uint32_t)(RG * kHistBins) + threadIdx.x;
       asm volatile("" : "+v"(off), "+v"(bin));  // selects, not branches
-      __builtin_amdgcn_raw_buffer_store_b32(u, srows, off, 0, 0);
+      // non-temporal: the block is read once, by the top-k after the scan,
+      // and streaming it past the caches keeps the shared keys there
+      __builtin_amdgcn_raw_buffer_store_b32(u, srows, off, 0, 2);
       atomicAdd(&hist[bin], 1u);
     }
   };

@@ -797,6 +797,8 @@ struct RowShared {
 // One round's raw loads for one thread: items base + u*kRowSub + 4 tid + j
 // (u, j < 4; the loads of a wave are contiguous) and, in pool mode, the id of
 // the block each float4 belongs to.
+typedef float f4nt __attribute__((ext_vector_type(4)));
+
 struct RowRound {
   float4 v[kRowU];
   int32_t blk[kRowU];
@@ -812,7 +814,9 @@ __device__ __forceinline__ void row_load(const SelectArgs& a, int r, const float
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
     const int64_t iu = base + (int64_t)u * kRowSub + 4 * threadIdx.x;
-    R.v[u] = *reinterpret_cast<const float4*>(srow + (iu < a.row_stride ? iu : 0));
+    // non-temporal: each score is read once here
+    const f4nt t = __builtin_nontemporal_load(reinterpret_cast<const f4nt*>(srow + (iu < a.row_stride ? iu : 0)));
+    R.v[u] = make_float4(t[0], t[1], t[2], t[3]);
     if (POOL) R.blk[u] = a.im.list[(int64_t)r * a.im.list_len + ((iu >> 3) < a.im.list_len ? (iu >> 3) : 0)];
   }
 }
