@@ -34,7 +34,10 @@ __global__ __launch_bounds__(256) void kv_compress_quantize_kernel(
   uint32_t lo, hi;
   const uint32_t sc = pool_quantize16<M, GATE>(xs, zs, lo, hi);
   const int64_t oe = s * out_seq_stride + e;
-  *reinterpret_cast<uint2*>(codes + oe * 256 + g * 8) = make_uint2(lo, hi);
+  // non-temporal: the codes of a whole cache are streamed out once (a wave
+  // writes two entries' 512 contiguous bytes) and read back much later
+  typedef unsigned u2x __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u2x{lo, hi}, reinterpret_cast<u2x*>(codes + oe * 256 + g * 8));
   scales[oe * 32 + g] = (uint8_t)sc;
 }
 
